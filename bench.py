@@ -1,0 +1,199 @@
+"""Benchmark of the latent-MoE layer forward on one MI355X.
+
+One step = one full layer forward (router GEMM, routing, permutation, down projection,
+grouped FC1 + SituGLU, grouped FC2 + combine, shared expert, RMSNorm + up projection
+with the shared add) over one batch of seeded synthetic tokens already resident in HBM.
+
+Prints one JSON line: layer tokens/s of the decode-shape layer (T=8, H=7168, L=2048,
+E=896, top-16, d=512, shared I=4096, bf16), routing us/call at T=1024, the HBM
+roofline fraction of the dominant kernel (grouped FC1 + SituGLU, timed with HIP events
+on its launch stream) and the CPU oracle timed on a bounded sample of the same work.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_bf16]
+                       [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "latent-MoE layer tokens/sec + route µs/call; % of HBM BW / MFMA peak"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def layer_bytes(cfg, n_touched):
+    """Algorithmic HBM bytes of one layer step: every weight byte of the dense projections,
+    the shared expert and the touched experts read once; activations read and written
+    once (bf16 = 2 bytes)."""
+    e = 2
+    dense = e * (cfg.E * cfg.H + cfg.L * cfg.H + 3 * cfg.H * cfg.I + cfg.H * cfg.L)
+    experts = n_touched * 3 * cfg.L * cfg.d * e
+    acts = e * cfg.T * cfg.H * 2
+    return dense + experts + acts
+
+
+def fc1_bytes(cfg, n_touched, rows):
+    """Algorithmic bytes of one grouped FC1 + SituGLU launch: W1 of each touched expert
+    (2d x L bf16) read once, the latent rows read once, the activation rows written once."""
+    return n_touched * 2 * cfg.d * cfg.L * 2 + cfg.T * cfg.L * 2 + rows * cfg.d * 2
+
+
+def route_microbench(torch, B, LI, reps=200):
+    cfg = LI.ROUTE_MASKED
+    logits = LI.make_route_logits(cfg, 3, device="cuda")
+    bias = LI.make_bias(cfg, 3, device="cuda")
+    ids = torch.empty(cfg.T, cfg.K, dtype=torch.int32, device="cuda")
+    w = torch.empty(cfg.T, cfg.K, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(20):
+        B.lmoe_route(cfg.T, cfg.E, cfg.K, logits, bias, cfg.rsf, 1, ids, w)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        B.lmoe_route(cfg.T, cfg.E, cfg.K, logits, bias, cfg.rsf, 1, ids, w)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1000.0 / reps
+    nbytes = cfg.T * cfg.E * 4 + cfg.E * 4 + cfg.T * cfg.K * 8
+    return us, nbytes
+
+
+def cpu_baseline(torch, LI, cfg, seed, X_cpu, n_tokens):
+    """The oracle timed on the host on `n_tokens` tokens of the same workload."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import numpy as np
+
+    import oracle
+    from gpu_helpers import oracle_weights, run_oracle_layer
+    w_cpu = LI.make_layer_weights(cfg, seed, device="cpu", experts=False)
+    o = oracle_weights(cfg, seed, w_cpu)
+    X64 = X_cpu[:n_tokens].to(torch.float64).numpy()
+    # expert weights are generated ahead of the timed region (the oracle reads arrays)
+    ids, _, _ = oracle.route(oracle.router_logits(X64, o["W_r"]), o["bias"], cfg.K, cfg.rsf)
+    for e in np.unique(ids):
+        o["W1"][e], o["W2"][e]
+    t0 = time.perf_counter()
+    run_oracle_layer(cfg, o, X64)
+    dt = time.perf_counter() - t0
+    return n_tokens / dt, dt
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_bf16")
+    ap.add_argument("--seed", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=2)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no multi-GPU path)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import lmoe_inputs as LI
+    from latent_moe_layer_sigmoid_amd import LatentMoELayer, LayerShape, StepTimer
+    from latent_moe_layer_sigmoid_amd import binding as B
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    cfg = LI.CONFIGS[args.workload]
+    log(f"workload {cfg.name}: generating weights on the GPU")
+    w = LI.make_layer_weights(cfg, args.seed, device="cuda")
+    shape = LayerShape(H=cfg.H, L=cfg.L, E=cfg.E, K=cfg.K, d=cfg.d, I=cfg.I, dtype=cfg.dtype, experts=cfg.experts,
+                       beta=cfg.beta, linear_beta=cfg.linear_beta, rsf=cfg.rsf, eps=cfg.eps, tile_m=cfg.tile_m)
+    layer = LatentMoELayer(shape, w)
+    X_cpu = LI.make_x(cfg, args.seed)
+    X = X_cpu.to("cuda")
+    stream = torch.cuda.current_stream()
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        layer.forward(X)
+    torch.cuda.synchronize()
+
+    # timed region: K whole-layer steps, back to back
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        layer.forward(X)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1000.0 / args.steps
+    tok_s = cfg.T * args.steps / elapsed
+
+    # per-step kernel durations (events on the launch stream), separate pass
+    timer = StepTimer(stream)
+    for _ in range(args.steps):
+        layer.forward(X, timer=timer)
+    torch.cuda.synchronize()
+    dur = timer.durations()
+
+    b = layer.buffers(cfg.T)
+    counts = b["counts"].cpu()
+    n_touched = int((counts > 0).sum())
+    rows = int(b["tile_offsets"][-1].item())
+    fb = fc1_bytes(cfg, n_touched, rows)
+    fc1_ms = dur["fc1"]
+    achieved = fb / (fc1_ms * 1e-3) / 1e9
+    lb = layer_bytes(cfg, n_touched)
+    log(f"n_touched={n_touched} rows={rows} fc1={fc1_ms * 1e3:.1f}us step={ms_per_step * 1e3:.1f}us "
+        f"layer bytes={lb / 1e6:.1f}MB")
+    log("per-step us: " + ", ".join(f"{k}={v * 1e3:.1f}" for k, v in dur.items()))
+
+    route_us, route_bytes = route_microbench(torch, B, LI)
+    log(f"route T=1024: {route_us:.2f} us/call")
+
+    res = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded counter-based generator; random-init weights)",
+        "config": {"workload": f"{cfg.name}: T={cfg.T} H={cfg.H} L={cfg.L} E={cfg.E} top-{cfg.K} d={cfg.d} "
+                               f"shared I={cfg.I} experts={cfg.experts} tile_m={cfg.tile_m}",
+                   "tokens_per_step": cfg.T, "seed": args.seed},
+        "roofline": {"kernel": "grouped FC1 + SituGLU (stream_gemm_kernel, SituGLU epilogue)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": fb, "avg_ms": round(fc1_ms, 5), "n_touched_experts": n_touched},
+        "layer_hbm": {"algorithmic_bytes": lb, "achieved_GBs": round(lb / (ms_per_step * 1e-3) / 1e9, 1),
+                      "frac": round(lb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "route_us_per_call": round(route_us, 3),
+        "route_hbm_frac": round(route_bytes / (route_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 5),
+        "step_us": {k: round(v * 1e3, 2) for k, v in dur.items()},
+    }
+    if not args.no_cpu_baseline:
+        n = min(args.cpu_tokens, cfg.T)
+        log(f"cpu baseline: oracle on {n} tokens")
+        v, dt = cpu_baseline(torch, LI, cfg, args.seed, X_cpu, n)
+        res["cpu_baseline"] = {"value": round(v, 4), "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
+                               "kind": "oracle",
+                               "sample": f"{n} of the {cfg.T} tokens of one step ({n * cfg.K} expert pairs), "
+                                         f"numpy float64, {dt:.2f} s"}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,193 @@
+/* lmoe.h -- C ABI of the latent-MoE layer forward for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (one GPU, full share of the work):
+ *   router GEMM -> single-group sigmoid top-k routing -> latent down projection
+ *   -> expert-sorted permutation -> grouped FC1 + SituGLU -> grouped FC2 + weighted
+ *   combine -> latent RMSNorm -> up projection with the shared-expert add.
+ *
+ * Sources cited below:
+ *   [P1] vLLM pull request 50088, "[MoE] Latent-MoE runner, fused MoE tail, SituGLU
+ *        activation and single-group top-k routing", section "What's in it", commits 1-7.
+ *   [P2] TensorRT-LLM pull request 20541 (Kimi K3 MoE decode, router stream),
+ *        sections "Description" and "Commit 1: routing as its own op".
+ *   [P3] vLLM API page vllm.models.kimi_k3.amd.latent_moe_runner, ROCmLatentMoERunner
+ *        (_fused_forward, _shard_up_proj_tail, enable_quantized_routed_input).
+ *   [OCP-MX] OCP Microscaling Formats (MX) v1.0 (E4M3, E2M1, E8M0, blocks of 32).
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers, row-major and densely packed. Weights are
+ *     stored [out, in] (the contraction dimension is contiguous), the nn.Linear layout
+ *     that [P3] _shard_up_proj_tail multiplies by weight.t().
+ *   - The caller owns every buffer and the stream. A call validates its arguments on
+ *     the host, enqueues kernels on `stream` and returns; results are valid once the
+ *     stream reaches the call ([P2] "Commit 1": routing is an op on the current stream
+ *     writing caller-allocated outputs). The library never allocates device memory,
+ *     never synchronizes and keeps no per-call state, so calls from several host
+ *     threads are safe on distinct buffers.
+ *   - Errors are returned, never thrown; an invalid call enqueues nothing. Contract
+ *     violations that only the device can see (an expert id >= E inside topk_ids,
+ *     counts that do not match the ids) are undefined behaviour.
+ *   - T == 0 (or rows == 0) is a successful no-op that touches no HIP API.
+ *   - dtype pairs supported: activations and weights both LMOE_F32 or both LMOE_BF16
+ *     (fp32 accumulate); for the expert GEMMs also activations LMOE_MXFP8_E4M3 with
+ *     weights LMOE_MXFP4_E2M1 (scaled MFMA, fp32 accumulate).
+ */
+#ifndef LMOE_H
+#define LMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LMOE_ABI_VERSION 1
+
+typedef enum {
+  LMOE_OK = 0,
+  LMOE_ERR_INVALID_ARG = 1, /* null pointer, bad size, beta <= 0, mismatched dtypes, ... */
+  LMOE_ERR_UNSUPPORTED = 2, /* no kernel for this shape / dtype combination */
+  LMOE_ERR_WORKSPACE = 3,   /* workspace or capacity too small ([P2] "Commit 1": the runner validates the workspace) */
+  LMOE_ERR_HIP = 4          /* a HIP launch error was reported */
+} lmoe_status;
+
+typedef enum {
+  LMOE_F32 = 0,
+  LMOE_BF16 = 1,
+  LMOE_MXFP8_E4M3 = 2, /* one byte per element + one E8M0 scale byte per 32 elements */
+  LMOE_MXFP4_E2M1 = 3  /* two elements per byte (element 2i low nibble) + one E8M0 byte per 32 */
+} lmoe_dtype;
+
+int lmoe_abi_version(void);
+const char* lmoe_status_string(lmoe_status s);
+
+/* a1 / a3 -- dense projection y[M,N] = x[M,Kd] @ w[N,Kd]^T with fp32 accumulation.
+ * Used for the router GEMM (y LMOE_F32: [P1] commit 4, DeepSeekV3 routing takes FP32
+ * logits; [P2] "Description": the router GEMM runs first) and the latent down projection
+ * ([P2] "Description"; [P3] _fused_forward: routed input transform on hidden).
+ * x_dtype == w_dtype in {F32, BF16}; y_dtype in {F32, BF16}. Kd % 128 == 0 (BF16) or
+ * Kd % 64 == 0 (F32), N % 16 == 0, else LMOE_ERR_UNSUPPORTED. */
+lmoe_status lmoe_linear(int M, int N, int Kd, lmoe_dtype x_dtype, const void* x,
+                        lmoe_dtype w_dtype, const void* w, lmoe_dtype y_dtype, void* y,
+                        hipStream_t stream);
+
+/* a2 -- single-group DeepSeekV3 top-k routing ([P1] commit 1: with one group the
+ * grouped top-k is a plain top-k over all experts, result k held in lane k; [P1]
+ * commit 4: sigmoid scores, selection bias, routed scaling factor, FP32 logits).
+ *   s = sigmoid(logits[t, :]);  selection key = s + bias (bias may be NULL = 0);
+ *   topk_ids[t, k]  = expert with the k-th largest key (ties -> lower expert index);
+ *   topk_weights[t, k] = rsf * s[id] / sum_j s[id_j]   (renormalize != 0)
+ *                      = rsf * s[id]                   (renormalize == 0).
+ * logits fp32 [T,E]; bias fp32 [E]; topk_ids int32 [T,K]; topk_weights fp32 [T,K].
+ * 1 <= K <= min(E, 64) (the sorting-network bound of [P1] commit 1); E <= 1024. */
+lmoe_status lmoe_route(int T, int E, int K, const float* logits, const float* bias,
+                       float routed_scaling_factor, int renormalize,
+                       int32_t* topk_ids, float* topk_weights, hipStream_t stream);
+
+/* a5 -- stable expert-sorted permutation of the T*K (token, slot) pairs, pair p = t*K + k
+ * ([P2] "Commit 1": the routing workspace that FC1 / FC2 / finalize read, computed for
+ * the tile the runner reports). Outputs (all int32, caller-allocated):
+ *   expert_counts[E]       pairs routed to each expert;
+ *   expert_offsets[E+1]    exclusive prefix sum of the counts;
+ *   tile_offsets[E+1]      exclusive prefix sum of counts rounded up to tile_m;
+ *   row_to_pair[rows_cap]  for rows r < tile_offsets[E]: the pair in row r, -1 on pad
+ *                          rows; pairs of one expert are in ascending pair order;
+ *   tile_expert[rows_cap / tile_m]  expert of each tile of tile_m rows, -1 past the end;
+ *   pair_to_row[T*K]       inverse of row_to_pair.
+ * tile_m in {16, 32, 64, 128, 256}. rows_cap >= lmoe_permute_rows_cap(T, E, K, tile_m) and
+ * a multiple of tile_m, else LMOE_ERR_WORKSPACE. workspace: device scratch of at least
+ * lmoe_permute_workspace_bytes(T, E, K) bytes (NULL allowed when that is 0). */
+size_t lmoe_permute_workspace_bytes(int T, int E, int K);
+int lmoe_permute_rows_cap(int T, int E, int K, int tile_m);
+lmoe_status lmoe_permute(int T, int E, int K, int tile_m, const int32_t* topk_ids,
+                         int32_t* expert_counts, int32_t* expert_offsets, int32_t* tile_offsets,
+                         int32_t* row_to_pair, int32_t* tile_expert, int32_t* pair_to_row,
+                         int rows_cap, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* a4 / a8 -- MXFP8 (E4M3) quantization along rows ([OCP-MX]; [P2] "Description": input
+ * quantization before the MXE4M3 x MXE2M1 experts; [P1] commit 3: the general gated
+ * activations apply the activation, then requantize). Per 32 consecutive elements:
+ * exponent X = floor(log2 max|v|) - 8 clamped to [-127,127] (0 for an all-zero block);
+ * code = E4M3(v / 2^X), nearest-even, saturating at 448, sign bit set for v < 0.
+ * in [rows, cols] (F32 or BF16), codes u8 [rows, cols], scales u8 [rows, cols/32] = X+127.
+ * cols % 32 == 0. */
+lmoe_status lmoe_quant_mxfp8(int rows, int cols, lmoe_dtype in_dtype, const void* in,
+                             uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+/* a6 + a7 (+ a8) -- grouped FC1 with the SituGLU epilogue ([P1] commit 2: SituGLU,
+ * fp32 accumulate, written straight to the output; [P1] commit 5: SituGLU acts on the
+ * dequantized gate/up; [P3] enable_quantized_routed_input: gate and up not interleaved).
+ *   For every row r of a tile with expert e = tile_expert[r / tile_m] >= 0 and pair
+ *   p = row_to_pair[r] >= 0, with token t = p / K:
+ *     h = a[t, :] @ w1[e]^T           (w1 [E, 2d, in_dim]; h[:d] gate, h[d:] up)
+ *     act[r, j] = SituGLU(h[j], h[d+j]) = beta*tanh(g/beta)*sigmoid(g)
+ *                 * (linear_beta > 0 ? linear_beta*tanh(u/linear_beta) : u)
+ *   Rows with p < 0 (padding) and rows of tiles with expert -1 are never written.
+ * Dense mode (the shared expert): row_to_pair == NULL and tile_expert == NULL, E == 1,
+ * K == 1: row r = token r for r < T.
+ * beta must be finite and > 0 ([P1] commit 3: beta is required); linear_beta <= 0 means
+ * unset (passes up through). tile_m must be the tile the permutation was built with.
+ * a_dtype/w_dtype: F32/F32, BF16/BF16, or MXFP8_E4M3/MXFP4_E2M1 (a_scale [T, in_dim/32],
+ * w1_scale [E, 2d, in_dim/32]). act_dtype: F32 or BF16 (same as a_dtype for the dense
+ * dtypes), or MXFP8_E4M3 with act_scale [rows_cap, d/32] (SituGLU in fp32, then
+ * requantized per 32 outputs). */
+lmoe_status lmoe_fc1_situ(int T, int E, int K, int in_dim, int d, int tile_m,
+                          lmoe_dtype a_dtype, const void* a, const uint8_t* a_scale,
+                          const int32_t* row_to_pair, const int32_t* tile_expert,
+                          lmoe_dtype w_dtype, const void* w1, const uint8_t* w1_scale,
+                          float beta, float linear_beta,
+                          lmoe_dtype act_dtype, void* act, uint8_t* act_scale,
+                          int rows_cap, hipStream_t stream);
+
+/* a9 -- grouped FC2 with the weighted combine ([P2] "Commit 1": finalize reads the
+ * routing workspace; [P3] enable_quantized_routed_input: router weights are applied
+ * after the experts, not on their input).
+ *   y_r = act[r, :] @ w2[e]^T (w2 [E, out_dim, d]) for every valid row r, then
+ *   out[t, :] = sum_{k=0..K-1} topk_weights[t, k] * y_{pair_to_row(t*K+k)}   (k ascending),
+ *   `out` [T, out_dim] is overwritten. topk_weights NULL means weight 1.
+ * With K > 1 the per-pair products go through `workspace` (>= lmoe_fc2_workspace_bytes
+ * bytes) and are summed in fixed k order, so the result is bitwise reproducible.
+ * Dense mode as in lmoe_fc1_situ (shared expert: E == 1, K == 1).
+ * act_dtype/w_dtype: F32/F32, BF16/BF16 or MXFP8_E4M3/MXFP4_E2M1 (act_scale [rows_cap,
+ * d/32], w2_scale [E, out_dim, d/32]). out_dtype F32 or BF16. */
+size_t lmoe_fc2_workspace_bytes(int T, int K, int out_dim);
+lmoe_status lmoe_fc2_combine(int T, int E, int K, int d, int out_dim, int tile_m,
+                             lmoe_dtype act_dtype, const void* act, const uint8_t* act_scale,
+                             const int32_t* row_to_pair, const int32_t* tile_expert,
+                             lmoe_dtype w_dtype, const void* w2, const uint8_t* w2_scale,
+                             const float* topk_weights, lmoe_dtype out_dtype, void* out,
+                             int rows_cap, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* a11 + a12 -- latent tail ([P1] commit 7: the routed output is summed before the
+ * output transform because it contains an RMSNorm; [P3] _shard_up_proj_tail: norm of
+ * the reduced latent, then shared += latent @ up_proj^T in the GEMM's epilogue; [P1]
+ * commit 6: the up projection folds in the shared-expert add).
+ *   norm_out[t, :] = latent[t, :] / sqrt(mean(latent[t, :]^2) + eps) * gamma   (fp32 math)
+ *   out[t, :]      = shared[t, :] + norm_out[t, :] @ w_up^T
+ * latent fp32 [T, L]; gamma [L] in io_dtype (NULL = ones); w_up [H, L] in io_dtype;
+ * shared, out [T, H] in io_dtype (shared NULL = no add; out may alias shared);
+ * norm_out [T, L] in io_dtype (caller-owned, also returned). io_dtype F32 or BF16.
+ * eps >= 0. L % 128 == 0 (BF16) / 64 (F32), H % 16 == 0. */
+lmoe_status lmoe_tail(int T, int L, int H, const float* latent, const void* gamma, float eps,
+                      const void* w_up, const void* shared, lmoe_dtype io_dtype, void* out,
+                      void* norm_out, hipStream_t stream);
+
+/* Masked SituGLU over the batched [E, T_max, 2d] expert layout ([P1] commit 2:
+ * masked_situ_and_mul reads expert_num_tokens and leaves padded rows untouched).
+ *   For e < E and r < clamp(expert_num_tokens[e], 0, T_max):
+ *     out[e, r, j] = SituGLU(in[e, r, j], in[e, r, d + j]), fp32 math;
+ *   every other element of `out` is left exactly as it was.
+ * in [E, T_max, 2d], out [E, T_max, d], both `dtype` (F32 or BF16); d % 8 == 0. */
+lmoe_status lmoe_situ_masked(int E, int T_max, int d, lmoe_dtype dtype, const void* in,
+                             const int32_t* expert_num_tokens, float beta, float linear_beta,
+                             void* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LMOE_H */

@@ -1,0 +1,198 @@
+// Bandwidth-bound kernels of the layer for gfx950: masked SituGLU, MXFP8 quantization,
+// the fixed-order combine of per-pair expert outputs and the latent RMSNorm.
+// All use 16-byte (or wider) coalesced accesses; no MFMA (nothing here is a contraction).
+#include "common.h"
+#include "kernels.h"
+
+namespace lmoe {
+
+// ---- masked SituGLU over [E, T_max, 2d] (vLLM PR 50088, commit 2: masked_situ_and_mul
+// reads expert_num_tokens and leaves padded rows untouched; fp32 math).
+// Thread = 8 consecutive outputs of one row; grid.y = expert.
+template <Elt ELT>
+__global__ __launch_bounds__(256) void situ_masked_kernel(int T_max, int d, const void* __restrict__ in,
+                                                          const int32_t* __restrict__ counts, float beta,
+                                                          float lbeta, void* __restrict__ out) {
+  const int e = blockIdx.y;
+  int v = counts[e];
+  v = v < 0 ? 0 : (v > T_max ? T_max : v);
+  const int vpr = d >> 3;   // vectors per row
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= v * vpr) return;
+  const int r = idx / vpr, c = idx - r * vpr;
+  const size_t in_row = ((size_t)e * T_max + r) * (size_t)(2 * d);
+  const size_t out_row = ((size_t)e * T_max + r) * (size_t)d;
+  const float inv_b = 1.0f / beta, inv_lb = lbeta > 0.0f ? 1.0f / lbeta : 0.0f;
+  float g[8], u[8], o[8];
+  if (ELT == Elt::BF16) {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(in);
+    const uint4 gv = *reinterpret_cast<const uint4*>(p + in_row + c * 8);
+    const uint4 uv = *reinterpret_cast<const uint4*>(p + in_row + d + c * 8);
+    const uint16_t* gs = reinterpret_cast<const uint16_t*>(&gv);
+    const uint16_t* us = reinterpret_cast<const uint16_t*>(&uv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      g[i] = bf16_to_f32(gs[i]);
+      u[i] = bf16_to_f32(us[i]);
+    }
+  } else {
+    const float* p = reinterpret_cast<const float*>(in);
+    const float4* gp = reinterpret_cast<const float4*>(p + in_row + c * 8);
+    const float4* up = reinterpret_cast<const float4*>(p + in_row + d + c * 8);
+    const float4 g0 = gp[0], g1 = gp[1], u0 = up[0], u1 = up[1];
+    g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w; g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
+    u[0] = u0.x; u[1] = u0.y; u[2] = u0.z; u[3] = u0.w; u[4] = u1.x; u[5] = u1.y; u[6] = u1.z; u[7] = u1.w;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = situ(g[i], u[i], beta, inv_b, lbeta, inv_lb);
+  if (ELT == Elt::BF16) {
+    uint4 ov;
+    uint16_t* os = reinterpret_cast<uint16_t*>(&ov);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) os[i] = f32_to_bf16(o[i]);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + out_row + c * 8) = ov;
+  } else {
+    float4* op = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + out_row + c * 8);
+    op[0] = make_float4(o[0], o[1], o[2], o[3]);
+    op[1] = make_float4(o[4], o[5], o[6], o[7]);
+  }
+}
+
+hipError_t launch_situ_masked(int E, int T_max, int d, Elt elt, const void* in, const int32_t* counts,
+                              float beta, float lbeta, void* out, hipStream_t stream) {
+  const long vecs = (long)T_max * (d / 8);
+  const dim3 grid((unsigned)((vecs + 255) / 256), (unsigned)E), block(256);
+  if (elt == Elt::BF16)
+    hipLaunchKernelGGL(situ_masked_kernel<Elt::BF16>, grid, block, 0, stream, T_max, d, in, counts, beta, lbeta,
+                       out);
+  else
+    hipLaunchKernelGGL(situ_masked_kernel<Elt::F32>, grid, block, 0, stream, T_max, d, in, counts, beta, lbeta, out);
+  return hipGetLastError();
+}
+
+// ---- MXFP8 E4M3 quantization along rows (OCP MX v1.0; TensorRT-LLM PR 20541
+// "Description": input quantization before the MXE4M3 x MXE2M1 experts).
+// Thread = 8 elements; 4 consecutive lanes = one 32-element block.
+template <Elt ELT>
+__global__ __launch_bounds__(256) void quant_mxfp8_kernel(long nvec, const void* __restrict__ in,
+                                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  const bool live = idx < nvec;
+  float v[8];
+  if (live) {
+    if (ELT == Elt::BF16) {
+      const uint4 q = reinterpret_cast<const uint4*>(in)[idx];
+      const uint16_t* s = reinterpret_cast<const uint16_t*>(&q);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = bf16_to_f32(s[i]);
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(in) + 2 * idx;
+      const float4 a = p[0], b = p[1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, WAVE));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, WAVE));
+  if (!live) return;
+  const int X = mx_e4m3_exponent(amax);
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lo |= e4m3_encode(__builtin_ldexpf(v[i], -X)) << (8 * i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hi |= e4m3_encode(__builtin_ldexpf(v[4 + i], -X)) << (8 * i);
+  reinterpret_cast<uint2*>(codes)[idx] = make_uint2(lo, hi);
+  if ((idx & 3) == 0) scales[idx >> 2] = (uint8_t)(X + 127);
+}
+
+hipError_t launch_quant_mxfp8(int rows, int cols, Elt elt, const void* in, uint8_t* codes, uint8_t* scales,
+                              hipStream_t stream) {
+  const long nvec = (long)rows * cols / 8;
+  const dim3 grid((unsigned)((nvec + 255) / 256)), block(256);
+  if (elt == Elt::BF16)
+    hipLaunchKernelGGL(quant_mxfp8_kernel<Elt::BF16>, grid, block, 0, stream, nvec, in, codes, scales);
+  else
+    hipLaunchKernelGGL(quant_mxfp8_kernel<Elt::F32>, grid, block, 0, stream, nvec, in, codes, scales);
+  return hipGetLastError();
+}
+
+// ---- combine: out[t, :] = sum_{k ascending} ws[t*K + k, :]  (weights already applied).
+__global__ __launch_bounds__(256) void combine_kernel(int K, int N, const float* __restrict__ ws, int out_bf16,
+                                                      void* __restrict__ out) {
+  const int t = blockIdx.y;
+  const int c4 = blockIdx.x * 256 + threadIdx.x;   // float4 column index
+  if (c4 * 4 >= N) return;
+  const float4* src = reinterpret_cast<const float4*>(ws + (size_t)t * K * N) + c4;
+  float4 s = src[0];
+  for (int k = 1; k < K; ++k) {
+    const float4 v = src[(size_t)k * (N / 4)];
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  if (out_bf16) {
+    uint2 o;
+    o.x = (uint32_t)f32_to_bf16(s.x) | ((uint32_t)f32_to_bf16(s.y) << 16);
+    o.y = (uint32_t)f32_to_bf16(s.z) | ((uint32_t)f32_to_bf16(s.w) << 16);
+    reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + (size_t)t * N)[c4] = o;
+  } else {
+    reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + (size_t)t * N)[c4] = s;
+  }
+}
+
+hipError_t launch_combine(int T, int K, int N, const float* ws, Elt out_elt, void* out, hipStream_t stream) {
+  const dim3 grid((unsigned)((N / 4 + 255) / 256), (unsigned)T), block(256);
+  hipLaunchKernelGGL(combine_kernel, grid, block, 0, stream, K, N, ws, out_elt == Elt::BF16 ? 1 : 0, out);
+  return hipGetLastError();
+}
+
+// ---- latent RMSNorm (vLLM PR 50088, commit 7: normalize the summed routed output):
+// n = z / sqrt(mean(z^2) + eps) * gamma in fp32; one workgroup per token row.
+__global__ __launch_bounds__(256) void rmsnorm_kernel(int L, const float* __restrict__ z,
+                                                      const void* __restrict__ gamma, int gamma_bf16, float eps,
+                                                      int out_bf16, void* __restrict__ out) {
+  __shared__ float s_part[4];
+  const int t = blockIdx.x;
+  const float* row = z + (size_t)t * L;
+  float ss = 0.0f;
+  for (int i = threadIdx.x * 4; i < L; i += 256 * 4) {
+    const float4 v = *reinterpret_cast<const float4*>(row + i);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+  const float r = 1.0f / sqrtf(tot / (float)L + eps);
+  for (int i = threadIdx.x * 4; i < L; i += 256 * 4) {
+    const float4 v = *reinterpret_cast<const float4*>(row + i);
+    float o[4] = {v.x * r, v.y * r, v.z * r, v.w * r};
+    if (gamma) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] *= gamma_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(gamma)[i + q])
+                           : reinterpret_cast<const float*>(gamma)[i + q];
+    }
+    if (out_bf16) {
+      uint2 p;
+      p.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+      p.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + (size_t)t * L + i) = p;
+    } else {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + (size_t)t * L + i) =
+          make_float4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
+hipError_t launch_rmsnorm(int T, int L, const float* z, const void* gamma, float eps, Elt elt, void* out,
+                          hipStream_t stream) {
+  const int bf = elt == Elt::BF16 ? 1 : 0;
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(256), 0, stream, L, z, gamma, bf, eps, bf, out);
+  return hipGetLastError();
+}
+
+}  // namespace lmoe

@@ -1,0 +1,69 @@
+// Host-side launchers of the gfx950 kernels (internal to liblmoe).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lmoe {
+
+enum class Elt : int { F32 = 0, BF16 = 1 };
+
+// Epilogue of the weight-streaming GEMM.
+enum class Epi : int {
+  STORE = 0,    // y[row, n] = acc                        (out_elt)
+  SITU = 1,     // act[row, j] = SituGLU(acc[j], acc[d+j]) (out_elt)
+  PAIR = 2,     // ws[pair, n] = w[pair] * acc            (fp32, combined afterwards)
+  TOKEN = 3,    // out[token, n] = w[pair] * acc          (out_elt; K == 1)
+  ADD = 4,      // out[row, n] = add[row, n] + acc        (out_elt)
+  SITU_MX = 5   // SituGLU then MXFP8 requant per 32 outputs (codes + scales)
+};
+
+struct StreamGemm {
+  // A operand: rows of `a` ([*, lda] elements). Grouped mode gathers token rows
+  // (row_to_pair / K) or, with a_by_row, the row itself; dense mode uses row r < M.
+  const void* a;
+  int lda;
+  const uint8_t* a_scale;    // MX only: [*, Kd/32]
+  const void* w;             // [E, n_total, Kd]
+  const uint8_t* w_scale;    // MX only
+  int n_total;               // rows of one expert's weight
+  int Kd;
+  int M;                     // dense: rows; grouped: rows_cap
+  const int32_t* row_to_pair;  // NULL = dense
+  const int32_t* tile_expert;
+  int tile_m;
+  int topk;
+  int a_by_row;              // A row index = row (FC2) instead of the pair's token (FC1)
+  // output
+  Epi epi;
+  Elt out_elt;
+  void* out;
+  int ldo;
+  uint8_t* out_scale;        // SITU_MX
+  const float* pair_w;       // PAIR / TOKEN weights (NULL = 1)
+  const void* add;           // ADD
+  float beta, lbeta;
+  int d;                     // SITU: gate/up split
+};
+
+// live_tiles: expected number of 16-row tiles that hold rows (sizes the split-K factor).
+hipError_t launch_stream_gemm(const StreamGemm& g, Elt elt, int n_out_cols, int live_tiles, hipStream_t stream);
+hipError_t launch_stream_gemm_mx(const StreamGemm& g, int n_out_cols, int live_tiles, hipStream_t stream);
+
+hipError_t launch_route(int T, int E, int K, const float* logits, const float* bias, float rsf, int renorm,
+                        int32_t* ids, float* weights, hipStream_t stream);
+
+size_t permute_workspace_bytes(int npairs, int E);
+hipError_t launch_permute(int npairs, int E, int tile_m, int max_tiles, const int32_t* ids, int32_t* counts,
+                          int32_t* offsets, int32_t* tile_offsets, int32_t* row_to_pair, int32_t* tile_expert,
+                          int32_t* pair_to_row, void* workspace, hipStream_t stream);
+
+hipError_t launch_situ_masked(int E, int T_max, int d, Elt elt, const void* in, const int32_t* counts,
+                              float beta, float lbeta, void* out, hipStream_t stream);
+hipError_t launch_quant_mxfp8(int rows, int cols, Elt elt, const void* in, uint8_t* codes, uint8_t* scales,
+                              hipStream_t stream);
+hipError_t launch_combine(int T, int K, int N, const float* ws, Elt out_elt, void* out, hipStream_t stream);
+hipError_t launch_rmsnorm(int T, int L, const float* z, const void* gamma, float eps, Elt elt, void* out,
+                          hipStream_t stream);
+
+}  // namespace lmoe

@@ -1,0 +1,269 @@
+// C ABI of liblmoe: argument validation and kernel dispatch. Declarations and the
+// contract of every entry point are in include/lmoe.h.
+#include <math.h>
+
+#include "kernels.h"
+#include "lmoe.h"
+
+using namespace lmoe;
+
+namespace {
+
+bool dense_elt(lmoe_dtype t) { return t == LMOE_F32 || t == LMOE_BF16; }
+Elt elt_of(lmoe_dtype t) { return t == LMOE_F32 ? Elt::F32 : Elt::BF16; }
+int kchunk_of(lmoe_dtype t) { return t == LMOE_F32 ? 64 : 128; }
+bool tile_ok(int tile_m) {
+  return tile_m == 16 || tile_m == 32 || tile_m == 64 || tile_m == 128 || tile_m == 256;
+}
+lmoe_status hip_status(hipError_t e) { return e == hipSuccess ? LMOE_OK : LMOE_ERR_HIP; }
+long rows_bound(long pairs, int E, int tile_m) {
+  const long nonempty = pairs < E ? pairs : E;
+  const long cap = pairs + nonempty * (tile_m - 1);
+  return (cap + tile_m - 1) / tile_m * tile_m;
+}
+// expected 16-row tiles holding rows: pairs / 16 plus one partial tile per touched expert
+int live_tiles(long pairs, int E) {
+  const long nonempty = pairs < E ? pairs : E;
+  return (int)((pairs + 15) / 16 + nonempty);
+}
+
+}  // namespace
+
+extern "C" {
+
+int lmoe_abi_version(void) { return LMOE_ABI_VERSION; }
+
+const char* lmoe_status_string(lmoe_status s) {
+  switch (s) {
+    case LMOE_OK: return "ok";
+    case LMOE_ERR_INVALID_ARG: return "invalid argument";
+    case LMOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case LMOE_ERR_WORKSPACE: return "workspace or capacity too small";
+    case LMOE_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+lmoe_status lmoe_linear(int M, int N, int Kd, lmoe_dtype x_dtype, const void* x, lmoe_dtype w_dtype,
+                        const void* w, lmoe_dtype y_dtype, void* y, hipStream_t stream) {
+  if (M < 0 || N <= 0 || Kd <= 0) return LMOE_ERR_INVALID_ARG;
+  if (!dense_elt(x_dtype) || x_dtype != w_dtype || !dense_elt(y_dtype)) return LMOE_ERR_INVALID_ARG;
+  if (Kd % kchunk_of(x_dtype) != 0 || N % 16 != 0) return LMOE_ERR_UNSUPPORTED;
+  if (M == 0) return LMOE_OK;
+  if (!x || !w || !y) return LMOE_ERR_INVALID_ARG;
+  StreamGemm g{};
+  g.a = x;
+  g.lda = Kd;
+  g.w = w;
+  g.n_total = N;
+  g.Kd = Kd;
+  g.M = M;
+  g.topk = 1;
+  g.epi = Epi::STORE;
+  g.out_elt = elt_of(y_dtype);
+  g.out = y;
+  g.ldo = N;
+  g.beta = 1.0f;
+  return hip_status(launch_stream_gemm(g, elt_of(x_dtype), N, (M + 15) / 16, stream));
+}
+
+lmoe_status lmoe_route(int T, int E, int K, const float* logits, const float* bias, float rsf, int renormalize,
+                       int32_t* topk_ids, float* topk_weights, hipStream_t stream) {
+  if (T < 0 || E < 1 || K < 1 || K > E || K > 64 || !isfinite(rsf)) return LMOE_ERR_INVALID_ARG;
+  if (E > 1024) return LMOE_ERR_UNSUPPORTED;
+  if (T == 0) return LMOE_OK;
+  if (!logits || !topk_ids || !topk_weights) return LMOE_ERR_INVALID_ARG;
+  return hip_status(launch_route(T, E, K, logits, bias, rsf, renormalize, topk_ids, topk_weights, stream));
+}
+
+size_t lmoe_permute_workspace_bytes(int T, int E, int K) {
+  if (T <= 0 || E < 1 || K < 1) return 0;
+  return permute_workspace_bytes((int)((long)T * K), E);
+}
+
+int lmoe_permute_rows_cap(int T, int E, int K, int tile_m) {
+  if (T < 0 || E < 1 || K < 1 || !tile_ok(tile_m)) return -1;
+  const long b = rows_bound((long)T * K, E, tile_m);
+  return b > 0x7FFFFFFFL ? -1 : (int)b;
+}
+
+lmoe_status lmoe_permute(int T, int E, int K, int tile_m, const int32_t* topk_ids, int32_t* expert_counts,
+                         int32_t* expert_offsets, int32_t* tile_offsets, int32_t* row_to_pair, int32_t* tile_expert,
+                         int32_t* pair_to_row, int rows_cap, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  if (T < 0 || E < 1 || K < 1 || K > E || K > 64 || !tile_ok(tile_m)) return LMOE_ERR_INVALID_ARG;
+  if (E > 1024) return LMOE_ERR_UNSUPPORTED;
+  if ((long)T * K > 0x3FFFFFFFL) return LMOE_ERR_UNSUPPORTED;
+  if (T == 0) return LMOE_OK;
+  if (!topk_ids || !expert_counts || !expert_offsets || !tile_offsets || !row_to_pair || !tile_expert ||
+      !pair_to_row)
+    return LMOE_ERR_INVALID_ARG;
+  const long npairs = (long)T * K;
+  if (rows_cap < rows_bound(npairs, E, tile_m) || rows_cap % tile_m != 0) return LMOE_ERR_WORKSPACE;
+  const size_t need = permute_workspace_bytes((int)npairs, E);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return LMOE_ERR_WORKSPACE;
+  return hip_status(launch_permute((int)npairs, E, tile_m, rows_cap / tile_m, topk_ids, expert_counts,
+                                   expert_offsets, tile_offsets, row_to_pair, tile_expert, pair_to_row, workspace,
+                                   stream));
+}
+
+lmoe_status lmoe_quant_mxfp8(int rows, int cols, lmoe_dtype in_dtype, const void* in, uint8_t* codes,
+                             uint8_t* scales, hipStream_t stream) {
+  if (rows < 0 || cols <= 0 || !dense_elt(in_dtype)) return LMOE_ERR_INVALID_ARG;
+  if (cols % 32 != 0) return LMOE_ERR_UNSUPPORTED;
+  if (rows == 0) return LMOE_OK;
+  if (!in || !codes || !scales) return LMOE_ERR_INVALID_ARG;
+  return hip_status(launch_quant_mxfp8(rows, cols, elt_of(in_dtype), in, codes, scales, stream));
+}
+
+// Common checks of the grouped expert GEMMs; returns LMOE_OK when the mode is valid.
+static lmoe_status check_grouped(int T, int E, int K, int tile_m, const int32_t* row_to_pair,
+                                 const int32_t* tile_expert, int rows_cap, bool* dense) {
+  if (T < 0 || E < 1 || K < 1 || K > 64) return LMOE_ERR_INVALID_ARG;
+  if (!row_to_pair && !tile_expert) {
+    if (E != 1 || K != 1 || rows_cap < T) return LMOE_ERR_INVALID_ARG;
+    *dense = true;
+    return LMOE_OK;
+  }
+  if (!row_to_pair || !tile_expert || !tile_ok(tile_m)) return LMOE_ERR_INVALID_ARG;
+  if (rows_cap % tile_m != 0 || rows_cap < rows_bound((long)T * K, E, tile_m)) return LMOE_ERR_WORKSPACE;
+  *dense = false;
+  return LMOE_OK;
+}
+
+lmoe_status lmoe_fc1_situ(int T, int E, int K, int in_dim, int d, int tile_m, lmoe_dtype a_dtype, const void* a,
+                          const uint8_t* a_scale, const int32_t* row_to_pair, const int32_t* tile_expert,
+                          lmoe_dtype w_dtype, const void* w1, const uint8_t* w1_scale, float beta, float linear_beta,
+                          lmoe_dtype act_dtype, void* act, uint8_t* act_scale, int rows_cap, hipStream_t stream) {
+  bool dense = false;
+  lmoe_status st = check_grouped(T, E, K, tile_m, row_to_pair, tile_expert, rows_cap, &dense);
+  if (st != LMOE_OK) return st;
+  if (in_dim <= 0 || d <= 0) return LMOE_ERR_INVALID_ARG;
+  if (!(beta > 0.0f) || !isfinite(beta) || isnan(linear_beta) || isinf(linear_beta)) return LMOE_ERR_INVALID_ARG;
+  const bool mx = a_dtype == LMOE_MXFP8_E4M3 || w_dtype == LMOE_MXFP4_E2M1;
+  if (mx) {
+    if (a_dtype != LMOE_MXFP8_E4M3 || w_dtype != LMOE_MXFP4_E2M1) return LMOE_ERR_INVALID_ARG;
+    return LMOE_ERR_UNSUPPORTED;
+  }
+  if (!dense_elt(a_dtype) || a_dtype != w_dtype || act_dtype != a_dtype) return LMOE_ERR_INVALID_ARG;
+  if (in_dim % kchunk_of(a_dtype) != 0 || d % 16 != 0) return LMOE_ERR_UNSUPPORTED;
+  if (T == 0) return LMOE_OK;
+  if (!a || !w1 || !act) return LMOE_ERR_INVALID_ARG;
+  StreamGemm g{};
+  g.a = a;
+  g.lda = in_dim;
+  g.w = w1;
+  g.n_total = 2 * d;
+  g.Kd = in_dim;
+  g.M = dense ? T : rows_cap;
+  g.row_to_pair = dense ? nullptr : row_to_pair;
+  g.tile_expert = dense ? nullptr : tile_expert;
+  g.tile_m = tile_m;
+  g.topk = K;
+  g.a_by_row = 0;
+  g.epi = Epi::SITU;
+  g.out_elt = elt_of(act_dtype);
+  g.out = act;
+  g.ldo = d;
+  g.beta = beta;
+  g.lbeta = linear_beta;
+  g.d = d;
+  const int live = dense ? (T + 15) / 16 : live_tiles((long)T * K, E);
+  return hip_status(launch_stream_gemm(g, elt_of(a_dtype), d, live, stream));
+}
+
+size_t lmoe_fc2_workspace_bytes(int T, int K, int out_dim) {
+  if (T <= 0 || K <= 1 || out_dim <= 0) return 0;
+  return (size_t)T * K * out_dim * sizeof(float);
+}
+
+lmoe_status lmoe_fc2_combine(int T, int E, int K, int d, int out_dim, int tile_m, lmoe_dtype act_dtype,
+                             const void* act, const uint8_t* act_scale, const int32_t* row_to_pair,
+                             const int32_t* tile_expert, lmoe_dtype w_dtype, const void* w2,
+                             const uint8_t* w2_scale, const float* topk_weights, lmoe_dtype out_dtype, void* out,
+                             int rows_cap, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  bool dense = false;
+  lmoe_status st = check_grouped(T, E, K, tile_m, row_to_pair, tile_expert, rows_cap, &dense);
+  if (st != LMOE_OK) return st;
+  if (d <= 0 || out_dim <= 0 || !dense_elt(out_dtype)) return LMOE_ERR_INVALID_ARG;
+  const bool mx = act_dtype == LMOE_MXFP8_E4M3 || w_dtype == LMOE_MXFP4_E2M1;
+  if (mx) {
+    if (act_dtype != LMOE_MXFP8_E4M3 || w_dtype != LMOE_MXFP4_E2M1) return LMOE_ERR_INVALID_ARG;
+    return LMOE_ERR_UNSUPPORTED;
+  }
+  if (!dense_elt(act_dtype) || act_dtype != w_dtype) return LMOE_ERR_INVALID_ARG;
+  if (d % kchunk_of(act_dtype) != 0 || out_dim % 16 != 0) return LMOE_ERR_UNSUPPORTED;
+  if (T == 0) return LMOE_OK;
+  if (!act || !w2 || !out) return LMOE_ERR_INVALID_ARG;
+  if (K > 1 && (!workspace || workspace_bytes < lmoe_fc2_workspace_bytes(T, K, out_dim))) return LMOE_ERR_WORKSPACE;
+  StreamGemm g{};
+  g.a = act;
+  g.lda = d;
+  g.w = w2;
+  g.n_total = out_dim;
+  g.Kd = d;
+  g.M = dense ? T : rows_cap;
+  g.row_to_pair = dense ? nullptr : row_to_pair;
+  g.tile_expert = dense ? nullptr : tile_expert;
+  g.tile_m = tile_m;
+  g.topk = K;
+  g.a_by_row = 1;
+  g.pair_w = topk_weights;
+  g.beta = 1.0f;
+  if (K == 1) {
+    g.epi = Epi::TOKEN;
+    g.out_elt = elt_of(out_dtype);
+    g.out = out;
+    g.ldo = out_dim;
+  } else {
+    g.epi = Epi::PAIR;
+    g.out_elt = Elt::F32;
+    g.out = workspace;
+    g.ldo = out_dim;
+  }
+  const int live = dense ? (T + 15) / 16 : live_tiles((long)T * K, E);
+  hipError_t err = launch_stream_gemm(g, elt_of(act_dtype), out_dim, live, stream);
+  if (err != hipSuccess) return LMOE_ERR_HIP;
+  if (K > 1) err = launch_combine(T, K, out_dim, (const float*)workspace, elt_of(out_dtype), out, stream);
+  return hip_status(err);
+}
+
+lmoe_status lmoe_tail(int T, int L, int H, const float* latent, const void* gamma, float eps, const void* w_up,
+                      const void* shared, lmoe_dtype io_dtype, void* out, void* norm_out, hipStream_t stream) {
+  if (T < 0 || L <= 0 || H <= 0) return LMOE_ERR_INVALID_ARG;
+  if (!dense_elt(io_dtype) || !(eps >= 0.0f) || !isfinite(eps)) return LMOE_ERR_INVALID_ARG;
+  if (L % kchunk_of(io_dtype) != 0 || H % 16 != 0) return LMOE_ERR_UNSUPPORTED;
+  if (T == 0) return LMOE_OK;
+  if (!latent || !w_up || !out || !norm_out) return LMOE_ERR_INVALID_ARG;
+  hipError_t err = launch_rmsnorm(T, L, latent, gamma, eps, elt_of(io_dtype), norm_out, stream);
+  if (err != hipSuccess) return LMOE_ERR_HIP;
+  StreamGemm g{};
+  g.a = norm_out;
+  g.lda = L;
+  g.w = w_up;
+  g.n_total = H;
+  g.Kd = L;
+  g.M = T;
+  g.topk = 1;
+  g.epi = Epi::ADD;
+  g.out_elt = elt_of(io_dtype);
+  g.out = out;
+  g.ldo = H;
+  g.add = shared;
+  g.beta = 1.0f;
+  return hip_status(launch_stream_gemm(g, elt_of(io_dtype), H, (T + 15) / 16, stream));
+}
+
+lmoe_status lmoe_situ_masked(int E, int T_max, int d, lmoe_dtype dtype, const void* in,
+                             const int32_t* expert_num_tokens, float beta, float linear_beta, void* out,
+                             hipStream_t stream) {
+  if (E < 0 || T_max < 0 || d <= 0 || !dense_elt(dtype)) return LMOE_ERR_INVALID_ARG;
+  if (!(beta > 0.0f) || !isfinite(beta) || isnan(linear_beta) || isinf(linear_beta)) return LMOE_ERR_INVALID_ARG;
+  if (d % 8 != 0) return LMOE_ERR_UNSUPPORTED;
+  if (E == 0 || T_max == 0) return LMOE_OK;
+  if (!in || !expert_num_tokens || !out) return LMOE_ERR_INVALID_ARG;
+  return hip_status(
+      launch_situ_masked(E, T_max, d, elt_of(dtype), in, expert_num_tokens, beta, linear_beta, out, stream));
+}
+
+}  // extern "C"

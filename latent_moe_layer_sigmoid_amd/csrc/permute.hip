@@ -1,0 +1,218 @@
+// Stable expert-sorted permutation of the (token, slot) pairs for gfx950 (TensorRT-LLM
+// PR 20541, "Commit 1: routing as its own op": the routing workspace that FC1 / FC2 /
+// finalize read, computed for the runner's tile).
+//
+// Pairs p = t*K + k are cut into blocks of 1024. Counts are order-free (LDS atomics);
+// ranks inside an expert must follow pair order, so each block ranks its pairs with
+// wave ballots: lanes holding the same expert are matched bit by bit over the expert id
+// (one ballot per bit), the rank inside the wave is the popcount of matching lower
+// lanes, and the per-wave counts in LDS give the offset of each earlier wave.
+//   1 block  : one fused kernel (count, scan, rank, scatter).
+//   >1 blocks: count per block -> one-block scan over (expert, block) -> rank + scatter.
+#include "common.h"
+#include "kernels.h"
+
+namespace lmoe {
+
+constexpr int PB = 1024;          // pairs per block (one per thread)
+constexpr int PW = PB / WAVE;     // waves per block
+
+// Mask of the lanes whose expert equals this lane's (inactive lanes pass e = -1).
+LMOE_DEV uint64_t match_lanes(int e, int nbits) {
+  uint64_t m = __ballot(e >= 0);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = e >= 0 && ((e >> b) & 1);
+    const uint64_t on = __ballot(bit);
+    m &= bit ? on : ~on;
+  }
+  return e >= 0 ? m : 0;
+}
+
+LMOE_DEV int lanes_below(uint64_t m, int lane) {
+  return __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+}
+
+// Block-wide exclusive scan of v over PB threads; returns the prefix and sets *total.
+LMOE_DEV int block_exclusive_scan(int v, int* s_wave, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, WAVE);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s_wave[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    int s = lane < PW ? s_wave[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(s, off, WAVE);
+      if (lane >= off) s += y;
+    }
+    if (lane < PW) s_wave[lane] = s;   // inclusive per-wave totals
+  }
+  __syncthreads();
+  const int before = (w ? s_wave[w - 1] : 0) + x - v;
+  *total = s_wave[PW - 1];
+  __syncthreads();
+  return before;
+}
+
+// Scan of counts over experts (each thread owns a contiguous range of experts), writing
+// offsets, tile_offsets, pad rows and the tile -> expert map. s_cnt holds counts[E].
+LMOE_DEV void scan_experts(const int* s_cnt, int E, int tile_m, int max_tiles, int32_t* counts,
+                           int32_t* offsets, int32_t* tile_offsets, int32_t* row_to_pair,
+                           int32_t* tile_expert, int* s_scratch, int* s_tile_off) {
+  const int per = (E + PB - 1) / PB;
+  const int e0 = threadIdx.x * per, e1 = min(E, e0 + per);
+  int c_sum = 0, p_sum = 0;
+  for (int e = e0; e < e1; ++e) {
+    const int c = s_cnt[e];
+    c_sum += c;
+    p_sum += (c + tile_m - 1) / tile_m * tile_m;
+  }
+  int c_tot, p_tot;
+  int c_pre = block_exclusive_scan(c_sum, s_scratch, &c_tot);
+  int p_pre = block_exclusive_scan(p_sum, s_scratch, &p_tot);
+  for (int e = e0; e < e1; ++e) {
+    const int c = s_cnt[e];
+    const int pc = (c + tile_m - 1) / tile_m * tile_m;
+    counts[e] = c;
+    offsets[e] = c_pre;
+    tile_offsets[e] = p_pre;
+    if (s_tile_off) s_tile_off[e] = p_pre;
+    for (int r = p_pre + c; r < p_pre + pc; ++r) row_to_pair[r] = -1;
+    for (int tt = p_pre / tile_m; tt < (p_pre + pc) / tile_m; ++tt) tile_expert[tt] = e;
+    c_pre += c;
+    p_pre += pc;
+  }
+  if (threadIdx.x == 0) {
+    offsets[E] = c_tot;
+    tile_offsets[E] = p_tot;
+  }
+  for (int tt = p_tot / tile_m + threadIdx.x; tt < max_tiles; tt += PB) tile_expert[tt] = -1;
+}
+
+// Rank the block's pairs inside their experts (pair order) and scatter them.
+// base(e): first row for this block's pairs of expert e.
+template <typename BaseFn>
+LMOE_DEV void rank_scatter(const int32_t* ids, int npairs, int E, int nbits, int block0,
+                           unsigned short* s_wcnt, BaseFn base, int32_t* row_to_pair,
+                           int32_t* pair_to_row) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int p = block0 + threadIdx.x;
+  const int e = p < npairs ? ids[p] : -1;
+  for (int i = threadIdx.x; i < PW * E; i += PB) s_wcnt[i] = 0;
+  __syncthreads();
+  const uint64_t m = match_lanes(e, nbits);
+  const int r_in_wave = lanes_below(m, lane);
+  if (e >= 0 && r_in_wave == 0) s_wcnt[w * E + e] = (unsigned short)__popcll(m);
+  __syncthreads();
+  if (e >= 0) {
+    int r = r_in_wave;
+    for (int w2 = 0; w2 < w; ++w2) r += s_wcnt[w2 * E + e];
+    const int row = base(e) + r;
+    row_to_pair[row] = p;
+    pair_to_row[p] = row;
+  }
+}
+
+LMOE_DEV int id_bits(int E) {
+  int b = 0;
+  while ((1 << b) < E) ++b;
+  return b;
+}
+
+// ---- single block: everything in one launch ---------------------------------------------
+__global__ __launch_bounds__(PB) void permute_fused_kernel(int npairs, int E, int tile_m, int max_tiles,
+                                                           const int32_t* __restrict__ ids, int32_t* counts,
+                                                           int32_t* offsets, int32_t* tile_offsets,
+                                                           int32_t* row_to_pair, int32_t* tile_expert,
+                                                           int32_t* pair_to_row) {
+  extern __shared__ int smem[];
+  int* s_cnt = smem;                      // [E]
+  int* s_toff = s_cnt + E;                // [E]
+  int* s_scr = s_toff + E;                // [PW]
+  unsigned short* s_wcnt = (unsigned short*)(s_scr + PW);   // [PW * E]
+  for (int e = threadIdx.x; e < E; e += PB) s_cnt[e] = 0;
+  __syncthreads();
+  if ((int)threadIdx.x < npairs) atomicAdd(&s_cnt[ids[threadIdx.x]], 1);
+  __syncthreads();
+  scan_experts(s_cnt, E, tile_m, max_tiles, counts, offsets, tile_offsets, row_to_pair, tile_expert,
+               s_scr, s_toff);
+  __syncthreads();
+  rank_scatter(ids, npairs, E, id_bits(E), 0, s_wcnt, [&](int e) { return s_toff[e]; }, row_to_pair,
+               pair_to_row);
+}
+
+// ---- several blocks ------------------------------------------------------------------------
+__global__ __launch_bounds__(PB) void permute_count_kernel(int npairs, int E, const int32_t* __restrict__ ids,
+                                                           int32_t* __restrict__ block_counts) {
+  extern __shared__ int s_cnt[];
+  for (int e = threadIdx.x; e < E; e += PB) s_cnt[e] = 0;
+  __syncthreads();
+  const int p = blockIdx.x * PB + threadIdx.x;
+  if (p < npairs) atomicAdd(&s_cnt[ids[p]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += PB) block_counts[(size_t)blockIdx.x * E + e] = s_cnt[e];
+}
+
+// One block: per expert, exclusive scan over blocks (in place), then the expert scan.
+__global__ __launch_bounds__(PB) void permute_scan_kernel(int nblk, int E, int tile_m, int max_tiles,
+                                                          int32_t* __restrict__ block_counts, int32_t* counts,
+                                                          int32_t* offsets, int32_t* tile_offsets,
+                                                          int32_t* row_to_pair, int32_t* tile_expert) {
+  extern __shared__ int smem[];
+  int* s_cnt = smem;          // [E]
+  int* s_scr = s_cnt + E;     // [PW]
+  for (int e = threadIdx.x; e < E; e += PB) {
+    int run = 0;
+    for (int b = 0; b < nblk; ++b) {
+      const int c = block_counts[(size_t)b * E + e];
+      block_counts[(size_t)b * E + e] = run;
+      run += c;
+    }
+    s_cnt[e] = run;
+  }
+  __syncthreads();
+  scan_experts(s_cnt, E, tile_m, max_tiles, counts, offsets, tile_offsets, row_to_pair, tile_expert,
+               s_scr, nullptr);
+}
+
+__global__ __launch_bounds__(PB) void permute_scatter_kernel(int npairs, int E, const int32_t* __restrict__ ids,
+                                                             const int32_t* __restrict__ block_base,
+                                                             const int32_t* __restrict__ tile_offsets,
+                                                             int32_t* row_to_pair, int32_t* pair_to_row) {
+  extern __shared__ unsigned short s_wcnt[];   // [PW * E]
+  const int32_t* bb = block_base + (size_t)blockIdx.x * E;
+  rank_scatter(ids, npairs, E, id_bits(E), blockIdx.x * PB, s_wcnt,
+               [&](int e) { return tile_offsets[e] + bb[e]; }, row_to_pair, pair_to_row);
+}
+
+size_t permute_workspace_bytes(int npairs, int E) {
+  const int nblk = (npairs + PB - 1) / PB;
+  return nblk <= 1 ? 0 : (size_t)nblk * E * sizeof(int32_t);
+}
+
+hipError_t launch_permute(int npairs, int E, int tile_m, int max_tiles, const int32_t* ids, int32_t* counts,
+                          int32_t* offsets, int32_t* tile_offsets, int32_t* row_to_pair,
+                          int32_t* tile_expert, int32_t* pair_to_row, void* workspace, hipStream_t stream) {
+  const int nblk = (npairs + PB - 1) / PB;
+  if (nblk <= 1) {
+    const size_t sm = (size_t)(2 * E + PW) * sizeof(int) + (size_t)PW * E * sizeof(unsigned short);
+    hipLaunchKernelGGL(permute_fused_kernel, dim3(1), dim3(PB), sm, stream, npairs, E, tile_m, max_tiles, ids,
+                       counts, offsets, tile_offsets, row_to_pair, tile_expert, pair_to_row);
+    return hipGetLastError();
+  }
+  int32_t* block_counts = (int32_t*)workspace;
+  hipLaunchKernelGGL(permute_count_kernel, dim3(nblk), dim3(PB), (size_t)E * sizeof(int), stream, npairs, E,
+                     ids, block_counts);
+  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(PB), (size_t)(E + PW) * sizeof(int), stream, nblk, E,
+                     tile_m, max_tiles, block_counts, counts, offsets, tile_offsets, row_to_pair, tile_expert);
+  hipLaunchKernelGGL(permute_scatter_kernel, dim3(nblk), dim3(PB), (size_t)PW * E * sizeof(unsigned short),
+                     stream, npairs, E, ids, block_counts, tile_offsets, row_to_pair, pair_to_row);
+  return hipGetLastError();
+}
+
+}  // namespace lmoe

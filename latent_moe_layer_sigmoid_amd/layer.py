@@ -1,0 +1,183 @@
+"""One latent-MoE layer forward composed from the C ABI (TensorRT-LLM PR 20541,
+"Description": router GEMM, latent down projection, input quantization, routing, FC1 /
+FC2, then the routed reduction with RMSNorm and the latent up projection; vLLM PR 50088,
+commit 7 and the vLLM latent_moe_runner API page for the latent tail).
+
+This module only sequences library calls and owns device buffers (allocated with torch
+once per token count); every step runs in liblmoe's HIP kernels.
+"""
+from dataclasses import dataclass
+
+import torch
+
+from . import binding as B
+
+
+@dataclass
+class LayerShape:
+    H: int
+    L: int
+    E: int
+    K: int
+    d: int
+    I: int
+    dtype: str            # "f32" or "bf16"
+    experts: str          # "dense" or "mx"
+    beta: float
+    linear_beta: float
+    rsf: float
+    eps: float
+    tile_m: int = 16
+
+
+def _lmoe_dtype(dtype):
+    return B.LMOE_F32 if dtype == "f32" else B.LMOE_BF16
+
+
+def _torch_dtype(dtype):
+    return torch.float32 if dtype == "f32" else torch.bfloat16
+
+
+class LatentMoELayer:
+    """Holds device weights and runs the layer through liblmoe.
+
+    weights: dict of device tensors W_r [E,H], bias [E] fp32, W_down [L,H], W1 [E,2d,L] /
+    W2 [E,L,d] (or W1_codes/W1_scales/W2_codes/W2_scales for MX experts), W_s1 [2I,H],
+    W_s2 [H,I], gamma [L], W_up [H,L]."""
+
+    def __init__(self, shape: LayerShape, weights: dict, device="cuda"):
+        self.s = shape
+        self.w = weights
+        self.device = torch.device(device)
+        self._bufs = {}
+        B.lib()   # fail loudly now if the library is missing
+
+    def buffers(self, T):
+        if T in self._bufs:
+            return self._bufs[T]
+        s, dev = self.s, self.device
+        dt = _torch_dtype(s.dtype)
+        rows_cap = B.lmoe_permute_rows_cap(T, s.E, s.K, s.tile_m)
+        pw = B.lmoe_permute_workspace_bytes(T, s.E, s.K)
+        fw = B.lmoe_fc2_workspace_bytes(T, s.K, s.L)
+        i32 = dict(dtype=torch.int32, device=dev)
+        b = dict(
+            rows_cap=rows_cap,
+            logits=torch.empty(T, s.E, dtype=torch.float32, device=dev),
+            ids=torch.empty(T, s.K, **i32),
+            weights=torch.empty(T, s.K, dtype=torch.float32, device=dev),
+            counts=torch.empty(s.E, **i32),
+            offsets=torch.empty(s.E + 1, **i32),
+            tile_offsets=torch.empty(s.E + 1, **i32),
+            row_to_pair=torch.empty(max(rows_cap, 1), **i32),
+            tile_expert=torch.empty(max(rows_cap // s.tile_m, 1), **i32),
+            pair_to_row=torch.empty(max(T * s.K, 1), **i32),
+            perm_ws=torch.empty(max(pw, 1), dtype=torch.uint8, device=dev),
+            perm_ws_bytes=pw,
+            x=torch.empty(T, s.L, dtype=dt, device=dev),
+            z=torch.empty(T, s.L, dtype=torch.float32, device=dev),
+            fc2_ws=torch.empty(max(fw // 4, 1), dtype=torch.float32, device=dev),
+            fc2_ws_bytes=fw,
+            act_s=torch.empty(T, s.I, dtype=dt, device=dev),
+            sh=torch.empty(T, s.H, dtype=dt, device=dev),
+            n=torch.empty(T, s.L, dtype=dt, device=dev),
+            out=torch.empty(T, s.H, dtype=dt, device=dev),
+        )
+        if s.experts == "mx":
+            b["xq"] = torch.empty(T, s.L, dtype=torch.uint8, device=dev)
+            b["xs"] = torch.empty(T, s.L // 32, dtype=torch.uint8, device=dev)
+            b["act"] = torch.empty(max(rows_cap, 1), s.d, dtype=torch.uint8, device=dev)
+            b["act_scale"] = torch.empty(max(rows_cap, 1), s.d // 32, dtype=torch.uint8, device=dev)
+        else:
+            b["act"] = torch.empty(max(rows_cap, 1), s.d, dtype=dt, device=dev)
+            b["act_scale"] = None
+        self._bufs[T] = b
+        return b
+
+    def forward(self, X, stream=None, timer=None):
+        """Run the layer on X [T, H]; returns the output buffer [T, H] (overwritten by the
+        next call with the same T). Intermediates stay in self.buffers(T).
+
+        timer: optional StepTimer; it records HIP events on the launch stream between the
+        library calls (one pair per step of the layer)."""
+        s, w = self.s, self.w
+        T = X.shape[0]
+        b = self.buffers(T)
+        dt = _lmoe_dtype(s.dtype)
+        rc = b["rows_cap"]
+        mark = timer.mark if timer is not None else (lambda name: None)
+        # a1 router GEMM -> fp32 logits
+        mark("router")
+        B.lmoe_linear(T, s.E, s.H, dt, X, dt, w["W_r"], B.LMOE_F32, b["logits"], stream)
+        # a2 routing
+        mark("route")
+        B.lmoe_route(T, s.E, s.K, b["logits"], w["bias"], s.rsf, 1, b["ids"], b["weights"], stream)
+        # a5 expert-sorted permutation
+        mark("permute")
+        B.lmoe_permute(T, s.E, s.K, s.tile_m, b["ids"], b["counts"], b["offsets"], b["tile_offsets"],
+                       b["row_to_pair"], b["tile_expert"], b["pair_to_row"], rc, b["perm_ws"],
+                       b["perm_ws_bytes"], stream)
+        # a3 latent down projection
+        mark("down")
+        B.lmoe_linear(T, s.L, s.H, dt, X, dt, w["W_down"], dt, b["x"], stream)
+        if s.experts == "mx":
+            # a4 input quantization, a6-a8 FC1 + SituGLU + requant, a9 FC2 + combine
+            mark("quant")
+            B.lmoe_quant_mxfp8(T, s.L, dt, b["x"], b["xq"], b["xs"], stream)
+            mark("fc1")
+            B.lmoe_fc1_situ(T, s.E, s.K, s.L, s.d, s.tile_m, B.LMOE_MXFP8_E4M3, b["xq"], b["xs"], b["row_to_pair"],
+                            b["tile_expert"], B.LMOE_MXFP4_E2M1, w["W1_codes"], w["W1_scales"], s.beta,
+                            s.linear_beta, B.LMOE_MXFP8_E4M3, b["act"], b["act_scale"], rc, stream)
+            mark("fc2")
+            B.lmoe_fc2_combine(T, s.E, s.K, s.d, s.L, s.tile_m, B.LMOE_MXFP8_E4M3, b["act"], b["act_scale"],
+                               b["row_to_pair"], b["tile_expert"], B.LMOE_MXFP4_E2M1, w["W2_codes"],
+                               w["W2_scales"], b["weights"], B.LMOE_F32, b["z"], rc, b["fc2_ws"],
+                               b["fc2_ws_bytes"], stream)
+        else:
+            # a6 + a7 FC1 with the SituGLU epilogue, a9 FC2 + weighted combine
+            mark("fc1")
+            B.lmoe_fc1_situ(T, s.E, s.K, s.L, s.d, s.tile_m, dt, b["x"], None, b["row_to_pair"], b["tile_expert"],
+                            dt, w["W1"], None, s.beta, s.linear_beta, dt, b["act"], None, rc, stream)
+            mark("fc2")
+            B.lmoe_fc2_combine(T, s.E, s.K, s.d, s.L, s.tile_m, dt, b["act"], None, b["row_to_pair"],
+                               b["tile_expert"], dt, w["W2"], None, b["weights"], B.LMOE_F32, b["z"], rc,
+                               b["fc2_ws"], b["fc2_ws_bytes"], stream)
+        # a10 shared expert (dense mode: E = K = 1)
+        mark("shared_fc1")
+        B.lmoe_fc1_situ(T, 1, 1, s.H, s.I, 16, dt, X, None, None, None, dt, w["W_s1"], None, s.beta,
+                        s.linear_beta, dt, b["act_s"], None, T, stream)
+        mark("shared_fc2")
+        B.lmoe_fc2_combine(T, 1, 1, s.I, s.H, 16, dt, b["act_s"], None, None, None, dt, w["W_s2"], None, None,
+                           dt, b["sh"], T, None, 0, stream)
+        # a11 + a12 latent RMSNorm, up projection with the shared add in its epilogue
+        mark("tail")
+        B.lmoe_tail(T, s.L, s.H, b["z"], w["gamma"], s.eps, w["W_up"], b["sh"], dt, b["out"], b["n"], stream)
+        mark(None)
+        return b["out"]
+
+
+class StepTimer:
+    """HIP events recorded on the launch stream between the layer's library calls;
+    durations() gives the mean milliseconds of each step over the recorded calls."""
+
+    def __init__(self, stream=None):
+        self.stream = stream
+        self.marks = []          # per forward call: list of (name, event)
+        self._cur = None
+
+    def mark(self, name):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(self.stream if self.stream is not None else torch.cuda.current_stream())
+        if self._cur is None:
+            self._cur = []
+        self._cur.append((name, ev))
+        if name is None:
+            self.marks.append(self._cur)
+            self._cur = None
+
+    def durations(self):
+        acc = {}
+        for call in self.marks:
+            for (name, a), (_, b) in zip(call[:-1], call[1:]):
+                acc.setdefault(name, []).append(a.elapsed_time(b))
+        return {k: sum(v) / len(v) for k, v in acc.items()}

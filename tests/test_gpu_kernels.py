@@ -1,0 +1,333 @@
+"""Parity of each HIP kernel (through the C ABI) against the CPU oracle on the same
+seeded inputs: bit-exact for ids, permutation, counts and MX codes; toleranced for
+floating point."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import lmoe_inputs as LI
+import oracle
+from gpu_helpers import bf16_ulp_diff, f64, guarded_route_logits, norm_err, tile_expert_from_offsets
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def B():
+    from latent_moe_layer_sigmoid_amd import binding
+    binding.lib()
+    return binding
+
+
+# ----------------------------------------------------------------------------- routing
+
+def _run_route(B, logits, bias, K, rsf, renorm=1):
+    T, E = logits.shape
+    ids = torch.full((T, K), -7, dtype=torch.int32, device=DEV)
+    w = torch.full((T, K), float("nan"), dtype=torch.float32, device=DEV)
+    B.lmoe_route(T, E, K, logits.to(DEV), None if bias is None else bias.to(DEV), rsf, renorm, ids, w)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), w.cpu().numpy()
+
+
+@pytest.mark.parametrize("E,K,T", [(16, 4, 4), (16, 16, 9), (64, 8, 33), (100, 6, 50), (256, 16, 70),
+                                   (300, 64, 17), (512, 1, 40), (896, 16, 1024), (1000, 32, 65), (1024, 64, 8)])
+def test_route_matches_oracle(B, E, K, T):
+    cfg = LI.scaled(LI.ROUTE_MASKED, T=T, E=E, K=K)
+    logits, bias, _ = guarded_route_logits(cfg, seed=1000 + E + K)
+    ids, w = _run_route(B, logits, bias, K, cfg.rsf)
+    rid, rw, _ = oracle.route(logits.double().numpy(), bias.double().numpy(), K, cfg.rsf)
+    assert np.array_equal(ids, rid)
+    np.testing.assert_allclose(w, rw, rtol=1e-5, atol=0)
+
+
+def test_route_full_microbench_shape_both_seeds(B):
+    for seed in (3, 103):
+        cfg = LI.ROUTE_MASKED
+        logits, bias, att = guarded_route_logits(cfg, seed)
+        ids, w = _run_route(B, logits, bias, cfg.K, cfg.rsf)
+        rid, rw, _ = oracle.route(logits.double().numpy(), bias.double().numpy(), cfg.K, cfg.rsf)
+        assert np.array_equal(ids, rid)
+        np.testing.assert_allclose(w, rw, rtol=1e-5)
+        np.testing.assert_allclose(w.sum(1), cfg.rsf, rtol=1e-5)
+
+
+def test_route_ties_pick_lower_index(B):
+    T, E, K = 6, 896, 16
+    logits = torch.zeros(T, E)
+    bias = torch.zeros(E)
+    bias[[5, 700, 64, 3]] = 0.25            # four raised experts, then ties among the rest
+    logits[1, 800:] = 1.0                   # token 1: a tied block at the top
+    logits[2, ::7] = -1.0
+    ids, w = _run_route(B, logits, bias, K, 2.5)
+    rid, rw, _ = oracle.route(logits.double().numpy(), bias.double().numpy(), K, 2.5)
+    assert np.array_equal(ids, rid)
+    assert ids[0].tolist() == [3, 5, 64, 700, 0, 1, 2, 4, 6, 7, 8, 9, 10, 11, 12, 13]
+    np.testing.assert_allclose(w, rw, rtol=1e-5)
+
+
+def test_route_no_bias_no_renormalize_and_k_equals_e(B):
+    cfg = LI.scaled(LI.ROUTE_MASKED, T=40, E=64, K=64)
+    logits, _, _ = guarded_route_logits(LI.scaled(cfg, K=63), seed=77)
+    ids, w = _run_route(B, logits, None, 64, 1.5, renorm=0)
+    rid, rw, _ = oracle.route(logits.double().numpy(), None, 64, 1.5, renormalize=False)
+    assert np.array_equal(ids, rid)
+    np.testing.assert_allclose(w, rw, rtol=1e-5)
+
+
+def test_route_deterministic_and_empty(B):
+    cfg = LI.scaled(LI.ROUTE_MASKED, T=256)
+    logits, bias, _ = guarded_route_logits(cfg, seed=5)
+    a = _run_route(B, logits, bias, cfg.K, cfg.rsf)
+    b = _run_route(B, logits, bias, cfg.K, cfg.rsf)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    B.lmoe_route(0, 896, 16, None, None, 1.0, 1, None, None)    # T == 0: no-op
+
+
+# --------------------------------------------------------------------------- permutation
+
+def _random_ids(T, E, K, rng, skew=0.0):
+    if skew:
+        p = np.exp(rng.standard_normal(E) * skew)
+        p /= p.sum()
+        ids = np.stack([rng.choice(E, K, replace=False, p=p) for _ in range(T)])
+    else:
+        ids = np.argsort(rng.random((T, E)), axis=1)[:, :K]
+    return ids.astype(np.int32)
+
+
+def _run_permute(B, ids, E, tile_m):
+    T, K = ids.shape
+    rc = B.lmoe_permute_rows_cap(T, E, K, tile_m)
+    wsb = B.lmoe_permute_workspace_bytes(T, E, K)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    o = dict(counts=torch.full((E,), -9, **i32), offsets=torch.full((E + 1,), -9, **i32),
+             tile_offsets=torch.full((E + 1,), -9, **i32), row_to_pair=torch.full((rc,), -9, **i32),
+             tile_expert=torch.full((rc // tile_m,), -9, **i32), pair_to_row=torch.full((T * K,), -9, **i32))
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=DEV)
+    B.lmoe_permute(T, E, K, tile_m, torch.from_numpy(ids).to(DEV), o["counts"], o["offsets"], o["tile_offsets"],
+                   o["row_to_pair"], o["tile_expert"], o["pair_to_row"], rc, ws, wsb)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in o.items()}, rc
+
+
+@pytest.mark.parametrize("T,E,K,tile_m,skew", [(4, 16, 4, 16, 0), (8, 896, 16, 16, 0), (64, 896, 16, 16, 1.0),
+                                               (65, 100, 16, 32, 0), (1024, 896, 16, 16, 0.7),
+                                               (3000, 512, 8, 128, 1.5), (8192, 896, 16, 128, 1.0),
+                                               (777, 1024, 64, 256, 0.3), (1, 1, 1, 16, 0)])
+def test_permute_matches_oracle(B, T, E, K, tile_m, skew):
+    rng = np.random.default_rng(T * 7 + E)
+    ids = _random_ids(T, E, K, rng, skew)
+    got, rc = _run_permute(B, ids, E, tile_m)
+    ref = oracle.permute(ids, E, tile_m)
+    nrows = int(ref["tile_offsets"][E])
+    assert np.array_equal(got["counts"], ref["counts"])
+    assert np.array_equal(got["offsets"], ref["offsets"])
+    assert np.array_equal(got["tile_offsets"], ref["tile_offsets"])
+    assert np.array_equal(got["row_to_pair"][:nrows], ref["row_to_pair"])
+    assert np.array_equal(got["pair_to_row"], ref["pair_to_row"])
+    assert np.array_equal(got["tile_expert"], tile_expert_from_offsets(ref["tile_offsets"], tile_m, rc // tile_m))
+    # permute then unpermute is the identity
+    assert np.array_equal(got["row_to_pair"][got["pair_to_row"]], np.arange(T * K))
+
+
+def test_permute_capacity_checks(B):
+    ids = torch.zeros(4, 2, dtype=torch.int32, device=DEV)
+    z = torch.zeros(64, dtype=torch.int32, device=DEV)
+    from latent_moe_layer_sigmoid_amd.binding import LmoeError
+    with pytest.raises(LmoeError) as ei:
+        B.lmoe_permute(4, 8, 2, 16, ids, z, z, z, z, z, z, 16, None, 0)   # rows_cap too small
+    assert ei.value.status == B.LMOE_ERR_WORKSPACE
+    with pytest.raises(LmoeError) as ei:
+        B.lmoe_permute(4, 8, 2, 24, ids, z, z, z, z, z, z, 192, None, 0)  # unsupported tile
+    assert ei.value.status == B.LMOE_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------------- masked SituGLU
+
+def test_situ_masked_full_shape(B):
+    cfg = LI.ROUTE_MASKED
+    logits, bias, _ = guarded_route_logits(cfg, seed=3)
+    ids, _, _ = oracle.route(logits.double().numpy(), bias.double().numpy(), cfg.K, cfg.rsf)
+    counts = np.bincount(ids.reshape(-1), minlength=cfg.E)
+    counts_t = torch.from_numpy(counts.astype(np.int32))
+    inp = LI.make_masked_input(cfg, seed=3, counts=counts_t, device=DEV)
+    out = torch.empty(cfg.E, cfg.T_max, cfg.d, dtype=torch.bfloat16, device=DEV)
+    out.view(torch.int16).fill_(LI.BF16_SENTINEL - 65536)
+    B.lmoe_situ_masked(cfg.E, cfg.T_max, cfg.d, B.LMOE_BF16, inp, counts_t.to(DEV), cfg.beta, cfg.linear_beta, out)
+    torch.cuda.synchronize()
+    got_bits = out.view(torch.int16).cpu().numpy().astype(np.int64) & 0xFFFF
+    v = np.clip(counts, 0, cfg.T_max)
+    pad = np.arange(cfg.T_max)[None, :] >= v[:, None]
+    assert np.all(got_bits[pad] == LI.BF16_SENTINEL)          # padded rows bit-untouched
+    ref = oracle.situ_masked(f64(inp), counts, cfg.beta, cfg.linear_beta, np.zeros((cfg.E, cfg.T_max, cfg.d)))
+    valid = ~pad
+    g = f64(out)[valid]
+    r = ref[valid]
+    assert norm_err(g, r) <= 1e-2
+    ref_bits = (torch.from_numpy(r).to(torch.bfloat16).view(torch.int16).numpy().astype(np.int64) & 0xFFFF)
+    assert bf16_ulp_diff(got_bits[valid], ref_bits) <= 2
+
+
+def test_situ_masked_f32_and_clamps(B):
+    E, Tm, d = 5, 7, 24
+    rng = np.random.default_rng(0)
+    inp = torch.from_numpy(rng.standard_normal((E, Tm, 2 * d)).astype(np.float32))
+    counts = np.array([0, 3, 7, 11, -4], dtype=np.int32)
+    out = torch.full((E, Tm, d), float("nan"), device=DEV)
+    B.lmoe_situ_masked(E, Tm, d, B.LMOE_F32, inp.to(DEV), torch.from_numpy(counts).to(DEV), 0.7, 0.0, out)
+    torch.cuda.synchronize()
+    ref = oracle.situ_masked(inp.double().numpy(), counts, 0.7, 0.0, np.full((E, Tm, d), np.nan), dtype="f32")
+    got = out.cpu().double().numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_allclose(got[ok], ref[ok], rtol=2e-5, atol=1e-6)
+
+
+# -------------------------------------------------------------------------- MXFP8 quant
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quant_mxfp8_bit_exact(B, dtype):
+    rng = np.random.default_rng(9)
+    rows, cols = 67, 2048
+    v = rng.standard_normal((rows, cols)) * 10.0 ** rng.integers(-4, 4, (rows, 1))
+    v[3, :32] = 0.0                              # all-zero block
+    v[4, 32:64] = 1.0                            # power-of-two block
+    v[5, 64:96] = 0.75
+    v[5, 70] = 480.0                             # saturating element
+    v[6, 96:128] = -1e-6                         # tiny block
+    v[7, 0:32] *= 1e-30                          # very small exponent
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    x = torch.from_numpy(v).to(td)
+    codes = torch.zeros(rows, cols, dtype=torch.uint8, device=DEV)
+    scales = torch.zeros(rows, cols // 32, dtype=torch.uint8, device=DEV)
+    B.lmoe_quant_mxfp8(rows, cols, B.LMOE_BF16 if dtype == "bf16" else B.LMOE_F32, x.to(DEV), codes, scales)
+    torch.cuda.synchronize()
+    rc, rs = oracle.mxfp8_quantize(f64(x))
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+# ------------------------------------------------------------------------- dense linear
+
+@pytest.mark.parametrize("M,N,Kd,dt,yt", [(1, 16, 128, "bf16", "f32"), (8, 896, 7168, "bf16", "f32"),
+                                          (8, 2048, 7168, "bf16", "bf16"), (17, 48, 256, "bf16", "bf16"),
+                                          (4, 16, 256, "f32", "f32"), (33, 128, 192, "f32", "f32"),
+                                          (200, 64, 384, "bf16", "f32")])
+def test_linear_matches_oracle(B, M, N, Kd, dt, yt):
+    rng = np.random.default_rng(M + N + Kd)
+    td = torch.bfloat16 if dt == "bf16" else torch.float32
+    x = torch.from_numpy(rng.standard_normal((M, Kd))).to(td)
+    w = torch.from_numpy(rng.standard_normal((N, Kd)) / math.sqrt(Kd)).to(td)
+    y = torch.empty(M, N, dtype=torch.float32 if yt == "f32" else torch.bfloat16, device=DEV)
+    B.lmoe_linear(M, N, Kd, B.LMOE_BF16 if dt == "bf16" else B.LMOE_F32, x.to(DEV),
+                  B.LMOE_BF16 if dt == "bf16" else B.LMOE_F32, w.to(DEV),
+                  B.LMOE_F32 if yt == "f32" else B.LMOE_BF16, y)
+    torch.cuda.synchronize()
+    ref = oracle.round_to(oracle.linear(f64(x), f64(w)), yt)
+    assert norm_err(f64(y), ref) <= (1e-5 if yt == "f32" else 8e-3)
+
+
+# -------------------------------------------------------------------- grouped expert GEMMs
+
+def _expert_case(B, T, E, K, L, d, tile_m, dt, seed):
+    rng = np.random.default_rng(seed)
+    td = torch.bfloat16 if dt == "bf16" else torch.float32
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    w = rng.random((T, K)).astype(np.float32) + 0.1
+    x = torch.from_numpy(rng.standard_normal((T, L))).to(td)
+    W1 = torch.from_numpy(rng.standard_normal((E, 2 * d, L)) / math.sqrt(L)).to(td)
+    W2 = torch.from_numpy(rng.standard_normal((E, L, d)) / math.sqrt(d)).to(td)
+    perm = oracle.permute(ids, E, tile_m)
+    rc = B.lmoe_permute_rows_cap(T, E, K, tile_m)
+    i32 = lambda a, n: torch.from_numpy(np.concatenate([a, np.full(n - len(a), -1)]).astype(np.int32)).to(DEV)
+    r2p = i32(perm["row_to_pair"], rc)
+    te = torch.from_numpy(tile_expert_from_offsets(perm["tile_offsets"], tile_m, rc // tile_m).astype(np.int32)).to(DEV)
+    return dict(ids=ids, w=w, x=x, W1=W1, W2=W2, perm=perm, rc=rc, r2p=r2p, te=te, td=td)
+
+
+@pytest.mark.parametrize("T,E,K,L,d,tile_m,dt", [(4, 16, 4, 128, 64, 16, "f32"), (8, 64, 16, 2048, 512, 16, "bf16"),
+                                                 (50, 32, 4, 256, 128, 32, "bf16"),
+                                                 (300, 16, 2, 256, 128, 128, "bf16")])
+def test_fc1_fc2_grouped_match_oracle(B, T, E, K, L, d, tile_m, dt):
+    c = _expert_case(B, T, E, K, L, d, tile_m, dt, seed=T + E)
+    ldt = B.LMOE_BF16 if dt == "bf16" else B.LMOE_F32
+    rc = c["rc"]
+    sentinel = -12345.0
+    act = torch.full((rc, d), sentinel, dtype=c["td"], device=DEV)
+    B.lmoe_fc1_situ(T, E, K, L, d, tile_m, ldt, c["x"].to(DEV), None, c["r2p"], c["te"], ldt, c["W1"].to(DEV), None,
+                    1.0, 0.5, ldt, act, None, rc)
+    torch.cuda.synchronize()
+    r2p = c["perm"]["row_to_pair"]
+    x64, W1_64, W2_64 = f64(c["x"]), f64(c["W1"]), f64(c["W2"])
+    act64 = f64(act)
+    ref_act = np.zeros((len(r2p), d))
+    for r, p in enumerate(r2p):
+        if p >= 0:
+            e = c["ids"].reshape(-1)[p]
+            h = oracle.linear(x64[p // K][None, :], W1_64[e])
+            ref_act[r] = oracle.round_to(oracle.situ_glu_rows(h, 1.0, 0.5), dt)[0]
+    valid = r2p >= 0
+    assert norm_err(act64[:len(r2p)][valid], ref_act[valid]) <= 1e-2
+    assert np.all(act64[:len(r2p)][~valid] == sentinel)        # pad rows never written
+    assert np.all(act64[len(r2p):] == sentinel)
+    # FC2 + combine on the GPU's own activations (isolates FC2)
+    z = torch.full((T, L), float("nan"), device=DEV)
+    wsb = B.lmoe_fc2_workspace_bytes(T, K, L)
+    ws = torch.empty(max(wsb // 4, 1), device=DEV)
+    B.lmoe_fc2_combine(T, E, K, d, L, tile_m, ldt, act, None, c["r2p"], c["te"], ldt, c["W2"].to(DEV), None,
+                       torch.from_numpy(c["w"]).to(DEV), B.LMOE_F32, z, rc, ws, wsb)
+    torch.cuda.synchronize()
+    ref_z = np.zeros((T, L))
+    p2r = c["perm"]["pair_to_row"]
+    for t in range(T):
+        for k in range(K):
+            e = c["ids"][t, k]
+            y = oracle.linear(act64[p2r[t * K + k]][None, :], W2_64[e])[0]
+            ref_z[t] += c["w"][t, k].astype(np.float64) * y
+    assert norm_err(f64(z), oracle.f32_round(ref_z)) <= 1e-4
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_dense_mode_shared_expert(B, dt):
+    rng = np.random.default_rng(4)
+    T, H, I = 8, 256, 128
+    td = torch.bfloat16 if dt == "bf16" else torch.float32
+    ldt = B.LMOE_BF16 if dt == "bf16" else B.LMOE_F32
+    X = torch.from_numpy(rng.standard_normal((T, H))).to(td)
+    Ws1 = torch.from_numpy(rng.standard_normal((2 * I, H)) / 16).to(td)
+    Ws2 = torch.from_numpy(rng.standard_normal((H, I)) / 11).to(td)
+    a = torch.empty(T, I, dtype=td, device=DEV)
+    sh = torch.empty(T, H, dtype=td, device=DEV)
+    B.lmoe_fc1_situ(T, 1, 1, H, I, 16, ldt, X.to(DEV), None, None, None, ldt, Ws1.to(DEV), None, 1.0, 0.0, ldt, a,
+                    None, T)
+    B.lmoe_fc2_combine(T, 1, 1, I, H, 16, ldt, a, None, None, None, ldt, Ws2.to(DEV), None, None, ldt, sh, T, None, 0)
+    torch.cuda.synchronize()
+    ref = oracle.shared_expert(f64(X), f64(Ws1), f64(Ws2), 1.0, 0.0, dt)
+    assert norm_err(f64(sh), ref) <= 1e-2
+
+
+# ------------------------------------------------------------------------------- tail
+
+@pytest.mark.parametrize("T,L,H,dt,alias", [(8, 2048, 7168, "bf16", False), (4, 128, 256, "f32", True),
+                                            (33, 256, 512, "bf16", True)])
+def test_tail_matches_oracle(B, T, L, H, dt, alias):
+    rng = np.random.default_rng(T + L)
+    td = torch.bfloat16 if dt == "bf16" else torch.float32
+    ldt = B.LMOE_BF16 if dt == "bf16" else B.LMOE_F32
+    z = torch.from_numpy(rng.standard_normal((T, L)) * 0.3).float()
+    gamma = torch.from_numpy(rng.uniform(0.9, 1.1, L)).to(td)
+    Wup = torch.from_numpy(rng.standard_normal((H, L)) / math.sqrt(L)).to(td)
+    sh = torch.from_numpy(rng.standard_normal((T, H))).to(td)
+    sh_d = sh.to(DEV)
+    out = sh_d if alias else torch.empty(T, H, dtype=td, device=DEV)
+    n = torch.empty(T, L, dtype=td, device=DEV)
+    B.lmoe_tail(T, L, H, z.to(DEV), gamma.to(DEV), 1e-6, Wup.to(DEV), sh_d, ldt, out, n)
+    torch.cuda.synchronize()
+    rn, rout = oracle.tail(f64(z), f64(gamma), 1e-6, f64(Wup), f64(sh), dt)
+    assert norm_err(f64(n), rn) <= 1e-2
+    assert norm_err(f64(out), rout) <= 1e-2

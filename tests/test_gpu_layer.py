@@ -1,0 +1,99 @@
+"""End-to-end parity of the latent-MoE layer forward (HIP path through the C ABI)
+against the CPU oracle: ids, permutation and counts bit-exact; routing weights within
+1e-5 relative; every stored float tensor and the layer output within
+max|gpu - oracle| / max|oracle| <= 1e-2 (bf16 / fp32) or 3e-2 (MX experts)."""
+import numpy as np
+import pytest
+import torch
+
+import lmoe_inputs as LI
+import oracle
+from gpu_helpers import f64, guarded_x, norm_err, oracle_weights, run_oracle_layer, tile_expert_from_offsets
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def build_layer(cfg, seed):
+    from latent_moe_layer_sigmoid_amd import LatentMoELayer, LayerShape
+    w_dev = LI.make_layer_weights(cfg, seed, device=DEV)
+    shape = LayerShape(H=cfg.H, L=cfg.L, E=cfg.E, K=cfg.K, d=cfg.d, I=cfg.I, dtype=cfg.dtype, experts=cfg.experts,
+                       beta=cfg.beta, linear_beta=cfg.linear_beta, rsf=cfg.rsf, eps=cfg.eps, tile_m=cfg.tile_m)
+    return LatentMoELayer(shape, w_dev), w_dev
+
+
+def check_layer(cfg, seed, tokens=None, out_tol=1e-2):
+    """Run the layer on the GPU for all T tokens; compare routing / permutation for all
+    tokens and the float outputs for `tokens` (all when None) against the oracle."""
+    print(f"[layer parity] {cfg.name} T={cfg.T} seed={seed}", flush=True)
+    layer, w_dev = build_layer(cfg, seed)
+    w_cpu = LI.make_layer_weights(cfg, seed, device="cpu", experts=False)
+    o = oracle_weights(cfg, seed, w_cpu)
+    X, _ = guarded_x(cfg, seed, o["W_r"], o["bias"])
+    out = layer.forward(X.to(DEV))
+    torch.cuda.synchronize()
+    b = layer.buffers(cfg.T)
+
+    # routing and permutation for every token: bit-exact
+    logits_all = oracle.router_logits(f64(X), o["W_r"])
+    ids_all, w_all, _ = oracle.route(logits_all, o["bias"], cfg.K, cfg.rsf)
+    assert np.array_equal(b["ids"].cpu().numpy(), ids_all)
+    np.testing.assert_allclose(b["weights"].cpu().numpy(), w_all, rtol=1e-5)
+    assert norm_err(b["logits"].cpu().numpy(), logits_all) <= 1e-5
+    perm = oracle.permute(ids_all, cfg.E, cfg.tile_m)
+    nrows = int(perm["tile_offsets"][cfg.E])
+    assert np.array_equal(b["counts"].cpu().numpy(), perm["counts"])
+    assert np.array_equal(b["offsets"].cpu().numpy(), perm["offsets"])
+    assert np.array_equal(b["tile_offsets"].cpu().numpy(), perm["tile_offsets"])
+    assert np.array_equal(b["row_to_pair"][:nrows].cpu().numpy(), perm["row_to_pair"])
+    assert np.array_equal(b["pair_to_row"].cpu().numpy(), perm["pair_to_row"])
+    rc = b["rows_cap"]
+    assert np.array_equal(b["tile_expert"].cpu().numpy(),
+                          tile_expert_from_offsets(perm["tile_offsets"], cfg.tile_m, rc // cfg.tile_m))
+
+    # float outputs for the sampled tokens
+    sel = np.arange(cfg.T) if tokens is None else np.asarray(tokens)
+    ref = run_oracle_layer(cfg, o, f64(X)[sel])
+    assert np.array_equal(ref["ids"], ids_all[sel])
+    assert norm_err(f64(b["x"])[sel], ref["x"]) <= 1e-2
+    p2r = b["pair_to_row"].cpu().numpy().reshape(cfg.T, cfg.K)[sel]
+    if cfg.experts != "mx":
+        act = f64(b["act"])[p2r]                     # [len(sel), K, d]
+        assert norm_err(act, ref["act"]) <= 1e-2
+    assert norm_err(f64(b["z"])[sel], ref["z"]) <= 1e-2
+    assert norm_err(f64(b["sh"])[sel], ref["sh"]) <= 1e-2
+    assert norm_err(f64(b["n"])[sel], ref["n"]) <= 1e-2
+    err = norm_err(f64(out)[sel], ref["out"])
+    print(f"[layer parity] {cfg.name}: out err {err:.3e}", flush=True)
+    assert err <= out_tol
+    return layer, X
+
+
+@pytest.mark.parametrize("seed", [1, 101])
+def test_layer_tiny_fp32(seed):
+    check_layer(LI.TINY, seed)
+
+
+def test_layer_decode_bf16_full_size():
+    layer, X = check_layer(LI.DECODE, 2)
+    # a second call on the same buffers reproduces the output bit for bit
+    first = layer.buffers(LI.DECODE.T)["out"].clone()
+    layer.forward(X.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), layer.buffers(LI.DECODE.T)["out"].view(torch.int16))
+
+
+def test_layer_decode_second_seed():
+    check_layer(LI.DECODE, 102)
+
+
+def test_layer_prefill_reduced_dims_ragged_tiles():
+    # prefill structure (tile 128, skewed load) at dimensions the oracle finishes in seconds
+    cfg = LI.scaled(LI.PREFILL, name="prefill_reduced", T=300, H=1024, L=512, E=64, K=8, d=128, I=256)
+    check_layer(cfg, 4)
+
+
+def test_layer_prefill_full_size_sampled_tokens():
+    cfg = LI.PREFILL
+    check_layer(cfg, 4, tokens=[0, 1, 2, 4095, 8190, 8191])
