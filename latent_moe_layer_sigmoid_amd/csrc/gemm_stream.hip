@@ -5,14 +5,13 @@
 // routed experts' FC1 / FC2 (a handful of rows per touched expert), the shared expert
 // and the up projection.
 //
-// One wavefront owns 16 rows x (16 * NT) output columns. Because the dot product does
-// not care in which order the contraction runs, each lane loads 64 contiguous bytes of
-// its row per K-chunk (lane l: row l % 16, bytes [64 * (l / 16), +64) of the chunk) for
-// both the activation row and the weight rows, and feeds them to four
-// v_mfma_f32_16x16x32_bf16 (or sixteen v_mfma_f32_16x16x4_f32): A and B agree on the
-// k-order, so the products pair up. Weight rows are therefore streamed in 256-byte
-// contiguous runs per 4 lanes, with the next chunk's loads issued before the current
-// chunk's MFMAs. Up to 8 wavefronts of a workgroup split the K range; their fp32
+// One wavefront owns 16 rows x (16 * NT) output columns. Per 256-byte K-chunk of a row,
+// lane l (row l % 16) loads the four 16-byte pieces at offsets 16 * (l / 16) + 64 * q,
+// q = 0..3, of the activation row and of its weight rows; piece q feeds one
+// v_mfma_f32_16x16x32_bf16 (or four v_mfma_f32_16x16x4_f32) whose k-slots then cover
+// chunk elements [32q, 32q + 32) in order, for A and B alike. Each load instruction
+// reads 64 contiguous bytes of 16 rows, and the next chunk's loads are issued before
+// the current chunk's MFMAs. Up to 8 wavefronts of a workgroup split the K range; their fp32
 // partial tiles are summed in LDS in fixed wave order (deterministic), and wave 0 runs
 // the fused epilogue: plain store, SituGLU (vLLM PR 50088, commit 2: gate = first d
 // columns, up = last d), weighted per-pair store for the combine (TensorRT-LLM PR
@@ -27,13 +26,25 @@ struct Chunk {
   uint4 v[4];
 };
 
-LMOE_DEV Chunk load_chunk(const char* p) {
-  const uint4* q = reinterpret_cast<const uint4*>(p);
+// Operands are read with buffer loads: a wave-uniform resource (base address and byte
+// size, range-checked by the hardware: reads past the end return zeros), a per-lane
+// 32-bit byte offset that never changes, and the chunk offset in a scalar register, so
+// the K loop carries no per-lane address arithmetic.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+LMOE_DEV rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Lane l's share of a 256-byte chunk row: four 16-byte pieces at byte offsets
+// 16 * (l / 16) + 64 * q, q = 0..3 (voff already includes 16 * (l / 16)). Each load
+// instruction q therefore reads 64 contiguous bytes of every row (4 lanes per row).
+LMOE_DEV Chunk load_chunk(rsrc_t r, uint32_t voff, uint32_t soff) {
   Chunk c;
-  c.v[0] = q[0];
-  c.v[1] = q[1];
-  c.v[2] = q[2];
-  c.v[3] = q[3];
+  c.v[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+  c.v[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 64, soff, 0));
+  c.v[2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 128, soff, 0));
+  c.v[3] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 192, soff, 0));
   return c;
 }
 
@@ -121,11 +132,14 @@ __global__ __launch_bounds__(512) void stream_gemm_kernel(const StreamGemm g, in
   } else {
     arow = min(row0 + m, g.M - 1);
   }
-  const char* a_ptr = reinterpret_cast<const char*>(g.a) + ((size_t)arow * g.lda) * TR::BYTES + g4 * 64;
+  const rsrc_t a_rs = make_rsrc(g.a, g.a_bytes);
+  const uint32_t a_off = (uint32_t)arow * (uint32_t)(g.lda * TR::BYTES) + g4 * 16;
 
   // ---- weight rows (one per tile j)
   const int half = NT / 2;
-  const char* b_ptr[NT];
+  const uint32_t w_bytes = (uint32_t)g.n_total * (uint32_t)(g.Kd * TR::BYTES);   // one expert
+  const rsrc_t w_rs = make_rsrc(reinterpret_cast<const char*>(g.w) + (size_t)e * w_bytes, w_bytes);
+  uint32_t b_off[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     int n;
@@ -133,36 +147,49 @@ __global__ __launch_bounds__(512) void stream_gemm_kernel(const StreamGemm g, in
       n = (j < half) ? nb * half * 16 + j * 16 + m : g.d + nb * half * 16 + (j - half) * 16 + m;
     else
       n = nb * NT * 16 + j * 16 + m;
-    b_ptr[j] = reinterpret_cast<const char*>(g.w) + (((size_t)e * g.n_total + n) * g.Kd) * TR::BYTES + g4 * 64;
+    b_off[j] = (uint32_t)n * (uint32_t)(g.Kd * TR::BYTES) + g4 * 16;
   }
 
-  // ---- K range of this wave
-  const int c0 = (int)((long)kchunks * wid / splits);
-  const int c1 = (int)((long)kchunks * (wid + 1) / splits);
+  // ---- K range of this wave (wave-uniform)
+  const int wu = __builtin_amdgcn_readfirstlane(wid);
+  const int c0 = (int)((long)kchunks * wu / splits);
+  const int c1 = (int)((long)kchunks * (wu + 1) / splits);
   constexpr int CB = TR::KCH * TR::BYTES;   // bytes per chunk row (256)
 
   floatx4 acc[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  // Ping-pong buffers: chunk c + 1 is requested before chunk c is consumed. The request
+  // index is clamped to the wave's last chunk, so the final requests re-read a chunk that
+  // is still cached instead of running past the range; they are never consumed.
   if (c0 < c1) {
-    Chunk a_cur = load_chunk(a_ptr + (size_t)c0 * CB);
-    Chunk b_cur[NT];
+    Chunk a0, a1, b0[NT], b1[NT];
+    a0 = load_chunk(a_rs, a_off, (uint32_t)c0 * CB);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) b_cur[j] = load_chunk(b_ptr[j] + (size_t)c0 * CB);
-    for (int c = c0; c < c1; ++c) {
-      Chunk a_nxt = a_cur;
-      Chunk b_nxt[NT];
-      if (c + 1 < c1) {
-        a_nxt = load_chunk(a_ptr + (size_t)(c + 1) * CB);
+    for (int j = 0; j < NT; ++j) b0[j] = load_chunk(w_rs, b_off[j], (uint32_t)c0 * CB);
+    int c = c0;
+    // sched_barrier keeps the compiler from sinking the requests below the MFMAs that
+    // consume the older buffer (which would serialize every chunk on memory latency).
+    while (true) {
+      const uint32_t o1 = (uint32_t)min(c + 1, c1 - 1) * CB;
+      a1 = load_chunk(a_rs, a_off, o1);
 #pragma unroll
-        for (int j = 0; j < NT; ++j) b_nxt[j] = load_chunk(b_ptr[j] + (size_t)(c + 1) * CB);
-      }
+      for (int j = 0; j < NT; ++j) b1[j] = load_chunk(w_rs, b_off[j], o1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) acc[j] = mfma_chunk<ELT>(a_cur, b_cur[j], acc[j]);
-      a_cur = a_nxt;
+      for (int j = 0; j < NT; ++j) acc[j] = mfma_chunk<ELT>(a0, b0[j], acc[j]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (++c >= c1) break;
+      const uint32_t o2 = (uint32_t)min(c + 1, c1 - 1) * CB;
+      a0 = load_chunk(a_rs, a_off, o2);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) b_cur[j] = b_nxt[j];
+      for (int j = 0; j < NT; ++j) b0[j] = load_chunk(w_rs, b_off[j], o2);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[j] = mfma_chunk<ELT>(a1, b1[j], acc[j]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (++c >= c1) break;
     }
   }
 

@@ -22,6 +22,7 @@ struct StreamGemm {
   // A operand: rows of `a` ([*, lda] elements). Grouped mode gathers token rows
   // (row_to_pair / K) or, with a_by_row, the row itself; dense mode uses row r < M.
   const void* a;
+  uint32_t a_bytes;          // size of the `a` buffer (hardware range check of the loads)
   int lda;
   const uint8_t* a_scale;    // MX only: [*, Kd/32]
   const void* w;             // [E, n_total, Kd]

@@ -12,6 +12,9 @@ namespace {
 bool dense_elt(lmoe_dtype t) { return t == LMOE_F32 || t == LMOE_BF16; }
 Elt elt_of(lmoe_dtype t) { return t == LMOE_F32 ? Elt::F32 : Elt::BF16; }
 int kchunk_of(lmoe_dtype t) { return t == LMOE_F32 ? 64 : 128; }
+long esize_of(lmoe_dtype t) { return t == LMOE_F32 ? 4 : 2; }
+// operand buffers are addressed with 32-bit byte offsets
+bool fits32(long rows, long cols, lmoe_dtype t) { return rows * cols * esize_of(t) < 0xFFFFFFFFL; }
 bool tile_ok(int tile_m) {
   return tile_m == 16 || tile_m == 32 || tile_m == 64 || tile_m == 128 || tile_m == 256;
 }
@@ -51,8 +54,10 @@ lmoe_status lmoe_linear(int M, int N, int Kd, lmoe_dtype x_dtype, const void* x,
   if (Kd % kchunk_of(x_dtype) != 0 || N % 16 != 0) return LMOE_ERR_UNSUPPORTED;
   if (M == 0) return LMOE_OK;
   if (!x || !w || !y) return LMOE_ERR_INVALID_ARG;
+  if (!fits32(M, Kd, x_dtype) || !fits32(N, Kd, w_dtype)) return LMOE_ERR_UNSUPPORTED;
   StreamGemm g{};
   g.a = x;
+  g.a_bytes = (uint32_t)(M * (long)Kd * esize_of(x_dtype));
   g.lda = Kd;
   g.w = w;
   g.n_total = N;
@@ -149,8 +154,10 @@ lmoe_status lmoe_fc1_situ(int T, int E, int K, int in_dim, int d, int tile_m, lm
   if (in_dim % kchunk_of(a_dtype) != 0 || d % 16 != 0) return LMOE_ERR_UNSUPPORTED;
   if (T == 0) return LMOE_OK;
   if (!a || !w1 || !act) return LMOE_ERR_INVALID_ARG;
+  if (!fits32(T, in_dim, a_dtype) || !fits32(2L * d, in_dim, w_dtype)) return LMOE_ERR_UNSUPPORTED;
   StreamGemm g{};
   g.a = a;
+  g.a_bytes = (uint32_t)((long)T * in_dim * esize_of(a_dtype));
   g.lda = in_dim;
   g.w = w1;
   g.n_total = 2 * d;
@@ -196,8 +203,11 @@ lmoe_status lmoe_fc2_combine(int T, int E, int K, int d, int out_dim, int tile_m
   if (T == 0) return LMOE_OK;
   if (!act || !w2 || !out) return LMOE_ERR_INVALID_ARG;
   if (K > 1 && (!workspace || workspace_bytes < lmoe_fc2_workspace_bytes(T, K, out_dim))) return LMOE_ERR_WORKSPACE;
+  const long act_rows = dense ? T : rows_cap;
+  if (!fits32(act_rows, d, act_dtype) || !fits32(out_dim, d, w_dtype)) return LMOE_ERR_UNSUPPORTED;
   StreamGemm g{};
   g.a = act;
+  g.a_bytes = (uint32_t)(act_rows * d * esize_of(act_dtype));
   g.lda = d;
   g.w = w2;
   g.n_total = out_dim;
@@ -235,10 +245,12 @@ lmoe_status lmoe_tail(int T, int L, int H, const float* latent, const void* gamm
   if (L % kchunk_of(io_dtype) != 0 || H % 16 != 0) return LMOE_ERR_UNSUPPORTED;
   if (T == 0) return LMOE_OK;
   if (!latent || !w_up || !out || !norm_out) return LMOE_ERR_INVALID_ARG;
+  if (!fits32(T, L, io_dtype) || !fits32(H, L, io_dtype)) return LMOE_ERR_UNSUPPORTED;
   hipError_t err = launch_rmsnorm(T, L, latent, gamma, eps, elt_of(io_dtype), norm_out, stream);
   if (err != hipSuccess) return LMOE_ERR_HIP;
   StreamGemm g{};
   g.a = norm_out;
+  g.a_bytes = (uint32_t)((long)T * L * esize_of(io_dtype));
   g.lda = L;
   g.w = w_up;
   g.n_total = H;

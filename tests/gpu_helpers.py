@@ -53,7 +53,7 @@ class ExpertBank:
         return self.cache[e]
 
 
-def guarded_route_logits(cfg, seed, max_rounds=40):
+def guarded_route_logits(cfg, seed, max_rounds=100):
     """fp32 logits [T, E] (cpu) whose oracle selection keys have every adjacent gap among
     each token's top K+1 >= MIN_GAP; failing rows are redrawn with the next attempt."""
     bias = LI.make_bias(cfg, seed)

@@ -38,7 +38,9 @@ def _run_route(B, logits, bias, K, rsf, renorm=1):
                                    (300, 64, 17), (512, 1, 40), (896, 16, 1024), (1000, 32, 65), (1024, 64, 8)])
 def test_route_matches_oracle(B, E, K, T):
     cfg = LI.scaled(LI.ROUTE_MASKED, T=T, E=E, K=K)
-    logits, bias, _ = guarded_route_logits(cfg, seed=1000 + E + K)
+    if K == 64:   # 64 guarded gaps per token: a narrower logit spread keeps the guard satisfiable
+        cfg = LI.scaled(cfg, logit_var=0.25)
+    logits, bias, _ = guarded_route_logits(cfg, seed=1000 + E + K, max_rounds=400)
     ids, w = _run_route(B, logits, bias, K, cfg.rsf)
     rid, rw, _ = oracle.route(logits.double().numpy(), bias.double().numpy(), K, cfg.rsf)
     assert np.array_equal(ids, rid)
@@ -257,7 +259,7 @@ def test_fc1_fc2_grouped_match_oracle(B, T, E, K, L, d, tile_m, dt):
     c = _expert_case(B, T, E, K, L, d, tile_m, dt, seed=T + E)
     ldt = B.LMOE_BF16 if dt == "bf16" else B.LMOE_F32
     rc = c["rc"]
-    sentinel = -12345.0
+    sentinel = -12288.0   # exact in bf16 and fp32
     act = torch.full((rc, d), sentinel, dtype=c["td"], device=DEV)
     B.lmoe_fc1_situ(T, E, K, L, d, tile_m, ldt, c["x"].to(DEV), None, c["r2p"], c["te"], ldt, c["W1"].to(DEV), None,
                     1.0, 0.5, ldt, act, None, rc)
