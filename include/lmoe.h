@@ -15,9 +15,11 @@
  *   [OCP-MX] OCP Microscaling Formats (MX) v1.0 (E4M3, E2M1, E8M0, blocks of 32).
  *
  * Conventions for every entry point:
- *   - Tensor pointers are DEVICE pointers, row-major and densely packed. Weights are
- *     stored [out, in] (the contraction dimension is contiguous), the nn.Linear layout
- *     that [P3] _shard_up_proj_tail multiplies by weight.t().
+ *   - Tensor pointers are DEVICE pointers, densely packed. Activations are row-major.
+ *     Weights have the logical shape [out, in] (the nn.Linear layout that [P3]
+ *     _shard_up_proj_tail multiplies by weight.t()) and are passed to the compute calls
+ *     in the packed layout written by lmoe_pack_weights (an MFMA-operand order in which
+ *     every wave-wide load reads 1 KB of contiguous HBM).
  *   - The caller owns every buffer and the stream. A call validates its arguments on
  *     the host, enqueues kernels on `stream` and returns; results are valid once the
  *     stream reaches the call ([P2] "Commit 1": routing is an op on the current stream
@@ -63,6 +65,18 @@ typedef enum {
 
 int lmoe_abi_version(void);
 const char* lmoe_status_string(lmoe_status s);
+
+/* Weight packing: the HBM layout of every weight argument below. src holds `batch`
+ * row-major matrices [N, Kd]; dst (same byte size, not overlapping src) receives them
+ * packed. Let KCH = 256 / esize (128 bf16 or 64 fp32 elements = 256 bytes of a row). For
+ * 16-row group n16 and K chunk c, the 4 KB block at byte (n16 * (Kd / KCH) + c) * 4096
+ * of a matrix holds, at byte q*1024 + g*256 + r*16 + i*esize (q, g < 4; r < 16;
+ * i < 16 / esize), the element W[16*n16 + r][c*KCH + q*KCH/4 + g*KCH/16 + i].
+ * Lane l = 16g + r of a wavefront reading 16 bytes at q*1024 + 16l thus receives the
+ * B operand of one MFMA (column r, k-group g). dtype F32 or BF16; N % 16 == 0,
+ * Kd % KCH == 0, else LMOE_ERR_UNSUPPORTED. */
+lmoe_status lmoe_pack_weights(int batch, int N, int Kd, lmoe_dtype dtype, const void* src, void* dst,
+                              hipStream_t stream);
 
 /* a1 / a3 -- dense projection y[M,N] = x[M,Kd] @ w[N,Kd]^T with fp32 accumulation.
  * Used for the router GEMM (y LMOE_F32: [P1] commit 4, DeepSeekV3 routing takes FP32

@@ -32,6 +32,7 @@ _i, _f, _p, _z = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 SIGNATURES = [
     ("lmoe_abi_version", _i, []),
     ("lmoe_status_string", ctypes.c_char_p, [_i]),
+    ("lmoe_pack_weights", _i, [_i, _i, _i, _i, _p, _p, _p]),
     ("lmoe_linear", _i, [_i, _i, _i, _i, _p, _i, _p, _i, _p, _p]),
     ("lmoe_route", _i, [_i, _i, _i, _p, _p, _f, _i, _p, _p, _p]),
     ("lmoe_permute_workspace_bytes", _z, [_i, _i, _i]),
@@ -98,6 +99,20 @@ def lmoe_abi_version():
 
 def lmoe_status_string(status):
     return lib().lmoe_status_string(status).decode()
+
+
+def lmoe_pack_weights(batch, N, Kd, dtype, src, dst, stream=None):
+    _check("lmoe_pack_weights", lib().lmoe_pack_weights(batch, N, Kd, dtype, _ptr(src), _ptr(dst), _stream(stream)))
+
+
+def packed(w, dtype=None, stream=None):
+    """A packed copy of weight tensor w ([N, Kd] or [batch, N, Kd], F32 or BF16)."""
+    if dtype is None:
+        dtype = LMOE_F32 if w.dtype == torch.float32 else LMOE_BF16
+    batch = w.shape[0] if w.dim() == 3 else 1
+    out = torch.empty_like(w)
+    lmoe_pack_weights(batch, w.shape[-2], w.shape[-1], dtype, w, out, stream)
+    return out
 
 
 def lmoe_linear(M, N, Kd, x_dtype, x, w_dtype, w, y_dtype, y, stream=None):

@@ -195,4 +195,31 @@ hipError_t launch_rmsnorm(int T, int L, const float* z, const void* gamma, float
   return hipGetLastError();
 }
 
+// ---- weight packing for the MFMA operand layout. Per matrix [N, Kd] (row-major source),
+// 16-row group n16 and K chunk c (256 bytes of a row: 128 bf16 / 64 fp32) form a 4 KB
+// block at (n16 * nch + c) * 4096; inside it, byte q*1024 + g*256 + r*16 + i*esize holds
+// W[16*n16 + r][c*KCH + q*(KCH/4) + g*(KCH/16) + i]. Thread = one destination 16 bytes.
+__global__ __launch_bounds__(256) void pack_weights_kernel(long pieces, int N, int Kd, int esize,
+                                                           const uint4* __restrict__ src, uint4* __restrict__ dst) {
+  const long p = (long)blockIdx.x * 256 + threadIdx.x;
+  if (p >= pieces) return;
+  const int kch = 256 / esize;                 // elements per 256-byte chunk row
+  const int nch = Kd / kch;
+  const long per_matrix = (long)N * Kd * esize / 16;
+  const long b = p / per_matrix, pm = p - b * per_matrix;
+  const long blk = pm >> 8;
+  const int w = (int)(pm & 255), q = w >> 6, l = w & 63, g = l >> 4, r = l & 15;
+  const long n16 = blk / nch, c = blk - n16 * nch;
+  const long n = n16 * 16 + r;
+  const long k0 = c * kch + q * (kch / 4) + g * (kch / 16);
+  dst[p] = src[b * per_matrix + (n * Kd + k0) * esize / 16];
+}
+
+hipError_t launch_pack_weights(int batch, int N, int Kd, int esize, const void* src, void* dst, hipStream_t stream) {
+  const long pieces = (long)batch * N * Kd * esize / 16;
+  hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, stream, pieces, N, Kd,
+                     esize, (const uint4*)src, (uint4*)dst);
+  return hipGetLastError();
+}
+
 }  // namespace lmoe

@@ -5,13 +5,13 @@
 // routed experts' FC1 / FC2 (a handful of rows per touched expert), the shared expert
 // and the up projection.
 //
-// One wavefront owns 16 rows x (16 * NT) output columns. Per 256-byte K-chunk of a row,
-// lane l (row l % 16) loads the four 16-byte pieces at offsets 16 * (l / 16) + 64 * q,
-// q = 0..3, of the activation row and of its weight rows; piece q feeds one
-// v_mfma_f32_16x16x32_bf16 (or four v_mfma_f32_16x16x4_f32) whose k-slots then cover
-// chunk elements [32q, 32q + 32) in order, for A and B alike. Each load instruction
-// reads 64 contiguous bytes of 16 rows, and the next chunk's loads are issued before
-// the current chunk's MFMAs. Up to 8 wavefronts of a workgroup split the K range; their fp32
+// One wavefront owns 16 rows x (16 * NT) output columns. Per 256-byte K-chunk, lane l
+// (row / column l % 16, k-group l / 16) loads four 16-byte pieces of its activation row
+// (row-major) and of each weight tile (packed MFMA layout: one contiguous 1 KB per load
+// instruction, which streams HBM at full rate where row-major 64-byte pieces do not);
+// piece q feeds one v_mfma_f32_16x16x32_bf16 (or four v_mfma_f32_16x16x4_f32) covering
+// chunk elements [32q, 32q + 32) in the same order for A and B. The next chunk's loads
+// are issued before the current chunk's MFMAs. Up to 8 wavefronts of a workgroup split the K range; their fp32
 // partial tiles are summed in LDS in fixed wave order (deterministic), and wave 0 runs
 // the fused epilogue: plain store, SituGLU (vLLM PR 50088, commit 2: gate = first d
 // columns, up = last d), weighted per-pair store for the combine (TensorRT-LLM PR
@@ -36,15 +36,27 @@ LMOE_DEV rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Lane l's share of a 256-byte chunk row: four 16-byte pieces at byte offsets
-// 16 * (l / 16) + 64 * q, q = 0..3 (voff already includes 16 * (l / 16)). Each load
-// instruction q therefore reads 64 contiguous bytes of every row (4 lanes per row).
-LMOE_DEV Chunk load_chunk(rsrc_t r, uint32_t voff, uint32_t soff) {
+// Activation rows are row-major: lane l's share of a 256-byte chunk row is the four
+// 16-byte pieces at 16 * (l / 16) + 64 * q, q = 0..3 (voff includes 16 * (l / 16)), so
+// piece q holds k-slots [32q, 32q + 32) of the chunk in MFMA order.
+LMOE_DEV Chunk load_chunk_a(rsrc_t r, uint32_t voff, uint32_t soff) {
   Chunk c;
   c.v[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
   c.v[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 64, soff, 0));
   c.v[2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 128, soff, 0));
   c.v[3] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 192, soff, 0));
+  return c;
+}
+
+// Weights are in the packed layout (see lmoe_pack_weights): the 16 rows x 256 bytes of
+// one (row group, chunk) form a 4 KB block whose piece q is the 1 KB at q * 1024 + 16 * l
+// for lane l. Every load instruction reads 1 KB contiguous.
+LMOE_DEV Chunk load_chunk_w(rsrc_t r, uint32_t voff, uint32_t soff) {
+  Chunk c;
+  c.v[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+  c.v[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 1024, soff, 0));
+  c.v[2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 2048, soff, 0));
+  c.v[3] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 3072, soff, 0));
   return c;
 }
 
@@ -139,15 +151,15 @@ __global__ __launch_bounds__(512) void stream_gemm_kernel(const StreamGemm g, in
   const int half = NT / 2;
   const uint32_t w_bytes = (uint32_t)g.n_total * (uint32_t)(g.Kd * TR::BYTES);   // one expert
   const rsrc_t w_rs = make_rsrc(reinterpret_cast<const char*>(g.w) + (size_t)e * w_bytes, w_bytes);
-  uint32_t b_off[NT];
+  uint32_t b_off[NT];   // start of tile j's row group in the packed layout, plus the lane's 16 bytes
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    int n;
+    int n0;
     if (g.epi == Epi::SITU)
-      n = (j < half) ? nb * half * 16 + j * 16 + m : g.d + nb * half * 16 + (j - half) * 16 + m;
+      n0 = (j < half) ? nb * half * 16 + j * 16 : g.d + nb * half * 16 + (j - half) * 16;
     else
-      n = nb * NT * 16 + j * 16 + m;
-    b_off[j] = (uint32_t)n * (uint32_t)(g.Kd * TR::BYTES) + g4 * 16;
+      n0 = nb * NT * 16 + j * 16;
+    b_off[j] = (uint32_t)(n0 / 16) * (uint32_t)kchunks * 4096u + lane * 16;
   }
 
   // ---- K range of this wave (wave-uniform)
@@ -165,26 +177,26 @@ __global__ __launch_bounds__(512) void stream_gemm_kernel(const StreamGemm g, in
   // is still cached instead of running past the range; they are never consumed.
   if (c0 < c1) {
     Chunk a0, a1, b0[NT], b1[NT];
-    a0 = load_chunk(a_rs, a_off, (uint32_t)c0 * CB);
+    a0 = load_chunk_a(a_rs, a_off, (uint32_t)c0 * CB);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) b0[j] = load_chunk(w_rs, b_off[j], (uint32_t)c0 * CB);
+    for (int j = 0; j < NT; ++j) b0[j] = load_chunk_w(w_rs, b_off[j], (uint32_t)c0 * 4096u);
     int c = c0;
     // sched_barrier keeps the compiler from sinking the requests below the MFMAs that
     // consume the older buffer (which would serialize every chunk on memory latency).
     while (true) {
-      const uint32_t o1 = (uint32_t)min(c + 1, c1 - 1) * CB;
-      a1 = load_chunk(a_rs, a_off, o1);
+      const uint32_t o1 = (uint32_t)min(c + 1, c1 - 1);
+      a1 = load_chunk_a(a_rs, a_off, o1 * CB);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) b1[j] = load_chunk(w_rs, b_off[j], o1);
+      for (int j = 0; j < NT; ++j) b1[j] = load_chunk_w(w_rs, b_off[j], o1 * 4096u);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < NT; ++j) acc[j] = mfma_chunk<ELT>(a0, b0[j], acc[j]);
       __builtin_amdgcn_sched_barrier(0);
       if (++c >= c1) break;
-      const uint32_t o2 = (uint32_t)min(c + 1, c1 - 1) * CB;
-      a0 = load_chunk(a_rs, a_off, o2);
+      const uint32_t o2 = (uint32_t)min(c + 1, c1 - 1);
+      a0 = load_chunk_a(a_rs, a_off, o2 * CB);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) b0[j] = load_chunk(w_rs, b_off[j], o2);
+      for (int j = 0; j < NT; ++j) b0[j] = load_chunk_w(w_rs, b_off[j], o2 * 4096u);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < NT; ++j) acc[j] = mfma_chunk<ELT>(a1, b1[j], acc[j]);

@@ -64,6 +64,7 @@ hipError_t launch_situ_masked(int E, int T_max, int d, Elt elt, const void* in, 
 hipError_t launch_quant_mxfp8(int rows, int cols, Elt elt, const void* in, uint8_t* codes, uint8_t* scales,
                               hipStream_t stream);
 hipError_t launch_combine(int T, int K, int N, const float* ws, Elt out_elt, void* out, hipStream_t stream);
+hipError_t launch_pack_weights(int batch, int N, int Kd, int esize, const void* src, void* dst, hipStream_t stream);
 hipError_t launch_rmsnorm(int T, int L, const float* z, const void* gamma, float eps, Elt elt, void* out,
                           hipStream_t stream);
 

@@ -47,6 +47,16 @@ const char* lmoe_status_string(lmoe_status s) {
   return "unknown status";
 }
 
+lmoe_status lmoe_pack_weights(int batch, int N, int Kd, lmoe_dtype dtype, const void* src, void* dst,
+                              hipStream_t stream) {
+  if (batch < 0 || N < 0 || Kd < 0) return LMOE_ERR_INVALID_ARG;
+  if (!dense_elt(dtype)) return dtype == LMOE_MXFP8_E4M3 ? LMOE_ERR_INVALID_ARG : LMOE_ERR_UNSUPPORTED;
+  if (N % 16 != 0 || Kd % kchunk_of(dtype) != 0) return LMOE_ERR_UNSUPPORTED;
+  if (batch == 0 || N == 0 || Kd == 0) return LMOE_OK;
+  if (!src || !dst || src == dst) return LMOE_ERR_INVALID_ARG;
+  return hip_status(launch_pack_weights(batch, N, Kd, (int)esize_of(dtype), src, dst, stream));
+}
+
 lmoe_status lmoe_linear(int M, int N, int Kd, lmoe_dtype x_dtype, const void* x, lmoe_dtype w_dtype,
                         const void* w, lmoe_dtype y_dtype, void* y, hipStream_t stream) {
   if (M < 0 || N <= 0 || Kd <= 0) return LMOE_ERR_INVALID_ARG;

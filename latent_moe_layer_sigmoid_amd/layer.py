@@ -41,16 +41,24 @@ def _torch_dtype(dtype):
 class LatentMoELayer:
     """Holds device weights and runs the layer through liblmoe.
 
-    weights: dict of device tensors W_r [E,H], bias [E] fp32, W_down [L,H], W1 [E,2d,L] /
-    W2 [E,L,d] (or W1_codes/W1_scales/W2_codes/W2_scales for MX experts), W_s1 [2I,H],
-    W_s2 [H,I], gamma [L], W_up [H,L]."""
+    weights: dict of row-major device tensors W_r [E,H], bias [E] fp32, W_down [L,H],
+    W1 [E,2d,L] / W2 [E,L,d] (or W1_codes/W1_scales/W2_codes/W2_scales for MX experts),
+    W_s1 [2I,H], W_s2 [H,I], gamma [L], W_up [H,L]; the projections are packed on the
+    device (lmoe_pack_weights) when the layer is built."""
 
     def __init__(self, shape: LayerShape, weights: dict, device="cuda"):
+        B.lib()   # fail loudly now if the library is missing
         self.s = shape
-        self.w = weights
         self.device = torch.device(device)
         self._bufs = {}
-        B.lib()   # fail loudly now if the library is missing
+        # weights go to HBM in the packed MFMA-operand layout once, at construction
+        self.w = {}
+        for k, v in weights.items():
+            if k in ("W_r", "W_down", "W1", "W2", "W_s1", "W_s2", "W_up"):
+                self.w[k] = B.packed(v)
+            else:
+                self.w[k] = v
+        torch.cuda.synchronize(self.device)
 
     def buffers(self, T):
         if T in self._bufs:

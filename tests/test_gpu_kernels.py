@@ -214,6 +214,45 @@ def test_quant_mxfp8_bit_exact(B, dtype):
     assert np.array_equal(codes.cpu().numpy(), rc)
 
 
+# ------------------------------------------------------------------------- weight packing
+
+def _pack_reference(w):
+    """Packed layout from its definition (include/lmoe.h, lmoe_pack_weights), in numpy."""
+    N, Kd = w.shape
+    es = w.itemsize
+    kch = 256 // es
+    nch = Kd // kch
+    v = 16 // es
+    out = np.empty(N * Kd, dtype=w.dtype)
+    for n16 in range(N // 16):
+        for c in range(nch):
+            blk = (n16 * nch + c) * (4096 // es)
+            for q in range(4):
+                for g in range(4):
+                    for r in range(16):
+                        k0 = c * kch + q * (kch // 4) + g * (kch // 16)
+                        dst = blk + (q * 1024 + g * 256 + r * 16) // es
+                        out[dst:dst + v] = w[n16 * 16 + r, k0:k0 + v]
+    return out.reshape(N, Kd)
+
+
+@pytest.mark.parametrize("N,Kd,dt", [(16, 128, "bf16"), (48, 384, "bf16"), (32, 64, "f32"), (16, 192, "f32")])
+def test_pack_weights_layout(B, N, Kd, dt):
+    rng = np.random.default_rng(N + Kd)
+    if dt == "bf16":
+        bits = rng.integers(0, 1 << 16, (3, N, Kd)).astype(np.uint16)
+        src = torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+    else:
+        src = torch.from_numpy(rng.standard_normal((3, N, Kd)).astype(np.float32)).to(DEV)
+    got = B.packed(src)
+    torch.cuda.synchronize()
+    view = torch.int16 if dt == "bf16" else torch.int32
+    g = got.view(view).cpu().numpy()
+    s_np = src.view(view).cpu().numpy()
+    for b in range(3):
+        assert np.array_equal(g[b], _pack_reference(s_np[b]))
+
+
 # ------------------------------------------------------------------------- dense linear
 
 @pytest.mark.parametrize("M,N,Kd,dt,yt", [(1, 16, 128, "bf16", "f32"), (8, 896, 7168, "bf16", "f32"),
@@ -227,7 +266,7 @@ def test_linear_matches_oracle(B, M, N, Kd, dt, yt):
     w = torch.from_numpy(rng.standard_normal((N, Kd)) / math.sqrt(Kd)).to(td)
     y = torch.empty(M, N, dtype=torch.float32 if yt == "f32" else torch.bfloat16, device=DEV)
     B.lmoe_linear(M, N, Kd, B.LMOE_BF16 if dt == "bf16" else B.LMOE_F32, x.to(DEV),
-                  B.LMOE_BF16 if dt == "bf16" else B.LMOE_F32, w.to(DEV),
+                  B.LMOE_BF16 if dt == "bf16" else B.LMOE_F32, B.packed(w.to(DEV)),
                   B.LMOE_F32 if yt == "f32" else B.LMOE_BF16, y)
     torch.cuda.synchronize()
     ref = oracle.round_to(oracle.linear(f64(x), f64(w)), yt)
@@ -261,7 +300,7 @@ def test_fc1_fc2_grouped_match_oracle(B, T, E, K, L, d, tile_m, dt):
     rc = c["rc"]
     sentinel = -12288.0   # exact in bf16 and fp32
     act = torch.full((rc, d), sentinel, dtype=c["td"], device=DEV)
-    B.lmoe_fc1_situ(T, E, K, L, d, tile_m, ldt, c["x"].to(DEV), None, c["r2p"], c["te"], ldt, c["W1"].to(DEV), None,
+    B.lmoe_fc1_situ(T, E, K, L, d, tile_m, ldt, c["x"].to(DEV), None, c["r2p"], c["te"], ldt, B.packed(c["W1"].to(DEV)), None,
                     1.0, 0.5, ldt, act, None, rc)
     torch.cuda.synchronize()
     r2p = c["perm"]["row_to_pair"]
@@ -281,7 +320,7 @@ def test_fc1_fc2_grouped_match_oracle(B, T, E, K, L, d, tile_m, dt):
     z = torch.full((T, L), float("nan"), device=DEV)
     wsb = B.lmoe_fc2_workspace_bytes(T, K, L)
     ws = torch.empty(max(wsb // 4, 1), device=DEV)
-    B.lmoe_fc2_combine(T, E, K, d, L, tile_m, ldt, act, None, c["r2p"], c["te"], ldt, c["W2"].to(DEV), None,
+    B.lmoe_fc2_combine(T, E, K, d, L, tile_m, ldt, act, None, c["r2p"], c["te"], ldt, B.packed(c["W2"].to(DEV)), None,
                        torch.from_numpy(c["w"]).to(DEV), B.LMOE_F32, z, rc, ws, wsb)
     torch.cuda.synchronize()
     ref_z = np.zeros((T, L))
@@ -305,9 +344,10 @@ def test_dense_mode_shared_expert(B, dt):
     Ws2 = torch.from_numpy(rng.standard_normal((H, I)) / 11).to(td)
     a = torch.empty(T, I, dtype=td, device=DEV)
     sh = torch.empty(T, H, dtype=td, device=DEV)
-    B.lmoe_fc1_situ(T, 1, 1, H, I, 16, ldt, X.to(DEV), None, None, None, ldt, Ws1.to(DEV), None, 1.0, 0.0, ldt, a,
-                    None, T)
-    B.lmoe_fc2_combine(T, 1, 1, I, H, 16, ldt, a, None, None, None, ldt, Ws2.to(DEV), None, None, ldt, sh, T, None, 0)
+    B.lmoe_fc1_situ(T, 1, 1, H, I, 16, ldt, X.to(DEV), None, None, None, ldt, B.packed(Ws1.to(DEV)), None, 1.0, 0.0,
+                    ldt, a, None, T)
+    B.lmoe_fc2_combine(T, 1, 1, I, H, 16, ldt, a, None, None, None, ldt, B.packed(Ws2.to(DEV)), None, None, ldt, sh, T,
+                       None, 0)
     torch.cuda.synchronize()
     ref = oracle.shared_expert(f64(X), f64(Ws1), f64(Ws2), 1.0, 0.0, dt)
     assert norm_err(f64(sh), ref) <= 1e-2
@@ -328,7 +368,7 @@ def test_tail_matches_oracle(B, T, L, H, dt, alias):
     sh_d = sh.to(DEV)
     out = sh_d if alias else torch.empty(T, H, dtype=td, device=DEV)
     n = torch.empty(T, L, dtype=td, device=DEV)
-    B.lmoe_tail(T, L, H, z.to(DEV), gamma.to(DEV), 1e-6, Wup.to(DEV), sh_d, ldt, out, n)
+    B.lmoe_tail(T, L, H, z.to(DEV), gamma.to(DEV), 1e-6, B.packed(Wup.to(DEV)), sh_d, ldt, out, n)
     torch.cuda.synchronize()
     rn, rout = oracle.tail(f64(z), f64(gamma), 1e-6, f64(Wup), f64(sh), dt)
     assert norm_err(f64(n), rn) <= 1e-2
