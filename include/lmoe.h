@@ -88,6 +88,21 @@ lmoe_status lmoe_linear(int M, int N, int Kd, lmoe_dtype x_dtype, const void* x,
                         lmoe_dtype w_dtype, const void* w, lmoe_dtype y_dtype, void* y,
                         hipStream_t stream);
 
+/* a1 + a3 + a10 (first half) in one launch -- up to four projections of the same input:
+ *   y_i = x @ w_i^T                                    (situ == NULL or situ[i] == 0), or
+ *   y_i = SituGLU(x @ w_i^T) with w_i of 2*N[i] rows   (situ[i] != 0; gate rows first)
+ * for i < n_proj <= 4. The decode-time projections of the hidden input -- the router GEMM
+ * (fp32 logits), the latent down projection and the shared expert's FC1 with its SituGLU
+ * ([P2] "Commit 2": router GEMM, shared experts and latent down projection all start
+ * from the hidden states; [P3] _fused_forward: the shared experts take the untransformed
+ * hidden) -- read x once per column block and share one launch. Per projection: N[i]
+ * output columns (N[i] % 16 == 0), packed weights w[i], output y[i] [M, N[i]] of
+ * y_dtype[i] (F32 or BF16). beta / linear_beta as in lmoe_fc1_situ (checked only when
+ * some situ[i] != 0). x_dtype F32 or BF16 (also the weights' dtype); Kd as lmoe_linear. */
+lmoe_status lmoe_linear_multi(int M, int Kd, lmoe_dtype x_dtype, const void* x, int n_proj, const int* N,
+                              const void* const* w, const lmoe_dtype* y_dtype, void* const* y, const int* situ,
+                              float beta, float linear_beta, hipStream_t stream);
+
 /* a2 -- single-group DeepSeekV3 top-k routing ([P1] commit 1: with one group the
  * grouped top-k is a plain top-k over all experts, result k held in lane k; [P1]
  * commit 4: sigmoid scores, selection bias, routed scaling factor, FP32 logits).
@@ -189,6 +204,20 @@ lmoe_status lmoe_fc2_combine(int T, int E, int K, int d, int out_dim, int tile_m
 lmoe_status lmoe_tail(int T, int L, int H, const float* latent, const void* gamma, float eps,
                       const void* w_up, const void* shared, lmoe_dtype io_dtype, void* out,
                       void* norm_out, hipStream_t stream);
+
+/* a10 (second half) + a11 + a12 in two launches -- the tail with the shared expert's FC2
+ * folded into the up projection ([P3] _shard_up_proj_tail: hidden += latent @ up_proj^T
+ * accumulated into the shared output; [P1] commit 6: the up projection folds in the
+ * shared-expert add):
+ *   norm_out = RMSNorm(latent; gamma, eps)                        (as lmoe_tail)
+ *   out[t, :] = round(round(shared_act[t, :] @ w_s2^T) + norm_out[t, :] @ w_up^T)
+ * where round() rounds to io_dtype: the shared-expert output is rounded exactly as if
+ * it had been stored, then added in fp32. shared_act [T, I] is the shared expert's
+ * SituGLU activation, w_s2 [H, I] and w_up [H, L] packed weights. out must not alias
+ * shared_act or norm_out. L % 128 and I % 128 == 0 (BF16; 64 for F32), H % 16 == 0. */
+lmoe_status lmoe_tail_shared(int T, int L, int H, int I, const float* latent, const void* gamma, float eps,
+                             const void* w_up, const void* shared_act, const void* w_s2, lmoe_dtype io_dtype,
+                             void* out, void* norm_out, hipStream_t stream);
 
 /* Masked SituGLU over the batched [E, T_max, 2d] expert layout ([P1] commit 2:
  * masked_situ_and_mul reads expert_num_tokens and leaves padded rows untouched).

@@ -34,6 +34,7 @@ SIGNATURES = [
     ("lmoe_status_string", ctypes.c_char_p, [_i]),
     ("lmoe_pack_weights", _i, [_i, _i, _i, _i, _p, _p, _p]),
     ("lmoe_linear", _i, [_i, _i, _i, _i, _p, _i, _p, _i, _p, _p]),
+    ("lmoe_linear_multi", _i, [_i, _i, _i, _p, _i, _p, _p, _p, _p, _p, _f, _f, _p]),
     ("lmoe_route", _i, [_i, _i, _i, _p, _p, _f, _i, _p, _p, _p]),
     ("lmoe_permute_workspace_bytes", _z, [_i, _i, _i]),
     ("lmoe_permute_rows_cap", _i, [_i, _i, _i, _i]),
@@ -45,6 +46,7 @@ SIGNATURES = [
     ("lmoe_fc2_combine", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _i, _p, _p, _p, _i, _p, _i, _p,
                               _z, _p]),
     ("lmoe_tail", _i, [_i, _i, _i, _p, _p, _f, _p, _p, _i, _p, _p, _p]),
+    ("lmoe_tail_shared", _i, [_i, _i, _i, _i, _p, _p, _f, _p, _p, _p, _i, _p, _p, _p]),
     ("lmoe_situ_masked", _i, [_i, _i, _i, _i, _p, _p, _f, _f, _p, _p]),
 ]
 
@@ -120,6 +122,18 @@ def lmoe_linear(M, N, Kd, x_dtype, x, w_dtype, w, y_dtype, y, stream=None):
                                             _stream(stream)))
 
 
+def lmoe_linear_multi(M, Kd, x_dtype, x, n_proj, N, w, y_dtype, y, situ, beta, linear_beta, stream=None):
+    """N, w, y_dtype, y, situ: sequences of length n_proj (situ may be None)."""
+    n = int(n_proj)
+    Na = (ctypes.c_int * n)(*N)
+    wa = (ctypes.c_void_p * n)(*[_ptr(t) for t in w])
+    ta = (ctypes.c_int * n)(*y_dtype)
+    ya = (ctypes.c_void_p * n)(*[_ptr(t) for t in y])
+    sa = None if situ is None else (ctypes.c_int * n)(*[int(v) for v in situ])
+    _check("lmoe_linear_multi", lib().lmoe_linear_multi(M, Kd, x_dtype, _ptr(x), n, Na, wa, ta, ya, sa,
+                                                        float(beta), float(linear_beta), _stream(stream)))
+
+
 def lmoe_route(T, E, K, logits, bias, routed_scaling_factor, renormalize, topk_ids, topk_weights, stream=None):
     _check("lmoe_route", lib().lmoe_route(T, E, K, _ptr(logits), _ptr(bias), float(routed_scaling_factor),
                                           int(renormalize), _ptr(topk_ids), _ptr(topk_weights), _stream(stream)))
@@ -170,6 +184,12 @@ def lmoe_fc2_combine(T, E, K, d, out_dim, tile_m, act_dtype, act, act_scale, row
 def lmoe_tail(T, L, H, latent, gamma, eps, w_up, shared, io_dtype, out, norm_out, stream=None):
     _check("lmoe_tail", lib().lmoe_tail(T, L, H, _ptr(latent), _ptr(gamma), float(eps), _ptr(w_up), _ptr(shared),
                                         io_dtype, _ptr(out), _ptr(norm_out), _stream(stream)))
+
+
+def lmoe_tail_shared(T, L, H, I, latent, gamma, eps, w_up, shared_act, w_s2, io_dtype, out, norm_out, stream=None):
+    _check("lmoe_tail_shared", lib().lmoe_tail_shared(T, L, H, I, _ptr(latent), _ptr(gamma), float(eps), _ptr(w_up),
+                                                      _ptr(shared_act), _ptr(w_s2), io_dtype, _ptr(out),
+                                                      _ptr(norm_out), _stream(stream)))
 
 
 def lmoe_situ_masked(E, T_max, d, dtype, inp, expert_num_tokens, beta, linear_beta, out, stream=None):

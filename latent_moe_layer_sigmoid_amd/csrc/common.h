@@ -34,7 +34,7 @@ LMOE_DEV float fast_tanh(float x) { return 1.0f - 2.0f * fast_rcp(fast_exp(2.0f 
 
 // SituGLU of one (gate, up) pair in fp32: beta*tanh(g/beta)*sigmoid(g) times
 // (linear_beta > 0 ? linear_beta*tanh(u/linear_beta) : u).
-LMOE_DEV float situ(float g, float u, float beta, float inv_beta, float lbeta, float inv_lbeta) {
+LMOE_DEV float situ_f(float g, float u, float beta, float inv_beta, float lbeta, float inv_lbeta) {
   float gate = beta * fast_tanh(g * inv_beta) * fast_sigmoid(g);
   float up = lbeta > 0.0f ? lbeta * fast_tanh(u * inv_lbeta) : u;
   return gate * up;

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void situ_masked_kernel(int T_max, int d, cons
     u[0] = u0.x; u[1] = u0.y; u[2] = u0.z; u[3] = u0.w; u[4] = u1.x; u[5] = u1.y; u[6] = u1.z; u[7] = u1.w;
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = situ(g[i], u[i], beta, inv_b, lbeta, inv_lb);
+  for (int i = 0; i < 8; ++i) o[i] = situ_f(g[i], u[i], beta, inv_b, lbeta, inv_lb);
   if (ELT == Elt::BF16) {
     uint4 ov;
     uint16_t* os = reinterpret_cast<uint16_t*>(&ov);

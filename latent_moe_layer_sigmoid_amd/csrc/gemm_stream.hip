@@ -110,17 +110,30 @@ LMOE_DEV float load_elt(Elt elt, const void* base, size_t idx) {
                          : bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
 }
 
-template <Elt ELT, int NT>
-__global__ __launch_bounds__(512) void stream_gemm_kernel(const StreamGemm g, int n_blocks, int kchunks) {
+template <Elt ELT, int NT, bool DUAL>
+__global__ __launch_bounds__(512) void stream_gemm_kernel(const StreamGemm g, int blocks_total, int nch0,
+                                                          int nch1) {
   using TR = EltTraits<ELT>;
-  extern __shared__ float s_red[];   // [splits][NT][4][64] when splits > 1
+  constexpr int CB = TR::KCH * TR::BYTES;   // bytes per chunk row (256)
+  constexpr int NACC = DUAL ? 2 * NT : NT;
+  extern __shared__ float s_red[];         // [splits][NACC][4][64] when splits > 1
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   const int splits = blockDim.x >> 6;
-  const int mt = blockIdx.x / n_blocks;
-  const int nb = blockIdx.x - mt * n_blocks;
+  const int mt = blockIdx.x / blocks_total;
+  const int nb_all = blockIdx.x - mt * blocks_total;
   const int row0 = mt * 16;
   if (row0 >= g.M) return;
+
+  // ---- output segment of this workgroup (uniform)
+  int s = 0;
+#pragma unroll
+  for (int i = 1; i < 4; ++i)
+    if (i < g.nseg && nb_all >= g.seg[i].block0) s = i;
+  const Seg sg = g.seg[s];
+  const int nb = nb_all - sg.block0;
+  const bool situ = sg.epi == Epi::SITU;
+
   const bool grouped = g.row_to_pair != nullptr;
   int e = 0;
   if (grouped) {
@@ -130,96 +143,142 @@ __global__ __launch_bounds__(512) void stream_gemm_kernel(const StreamGemm g, in
   const int m = lane & 15;
   const int g4 = lane >> 4;
 
+  // Start-up is a chain of dependent lookups (tile -> expert, row -> pair -> token row);
+  // the row -> pair entries of the A row and of the four epilogue rows are requested
+  // together, and the first weight chunk is requested as soon as the expert is known.
+  int pair_a = 0, pair_o[4] = {0, 0, 0, 0};
+  if (grouped) {
+    pair_a = g.row_to_pair[row0 + m];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pair_o[i] = g.row_to_pair[row0 + 4 * g4 + i];
+  }
+
+  // ---- weight tiles: start of tile j's row group in the packed layout, plus the lane's 16 bytes
+  const int half = NT / 2;
+  const uint32_t w_bytes = (uint32_t)sg.n_total * (uint32_t)(g.Kd * TR::BYTES);   // one expert
+  const rsrc_t w_rs = make_rsrc(reinterpret_cast<const char*>(sg.w) + (size_t)e * w_bytes, w_bytes);
+  uint32_t b_off[NT], b1_off[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    int n0;
+    if (situ)
+      n0 = (j < half) ? nb * half * 16 + j * 16 : sg.n_out + nb * half * 16 + (j - half) * 16;
+    else
+      n0 = nb * NT * 16 + j * 16;
+    b_off[j] = (uint32_t)(n0 / 16) * (uint32_t)nch0 * 4096u + lane * 16;
+    b1_off[j] = (uint32_t)(n0 / 16) * (uint32_t)nch1 * 4096u + lane * 16;
+  }
+  rsrc_t w1_rs = w_rs;
+  if (DUAL) {
+    const uint32_t w1_bytes = (uint32_t)sg.n_total * (uint32_t)(g.Kd1 * TR::BYTES);
+    w1_rs = make_rsrc(g.w1, w1_bytes);
+  }
+
+  // ---- K range of this wave (wave-uniform), over the chunks of both phases
+  const int nch = nch0 + (DUAL ? nch1 : 0);
+  const int wu = __builtin_amdgcn_readfirstlane(wid);
+  const int v0 = (int)((long)nch * wu / splits);
+  const int v1 = (int)((long)nch * (wu + 1) / splits);
+
+  Chunk a0, a1, b0[NT], b1[NT];
+  if (v0 < v1) {   // first weight chunk (phase 0 unless the range starts in phase 1)
+    if (!DUAL || v0 < nch0) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) b0[j] = load_chunk_w(w_rs, b_off[j], (uint32_t)v0 * 4096u);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) b0[j] = load_chunk_w(w1_rs, b1_off[j], (uint32_t)(v0 - nch0) * 4096u);
+    }
+  }
+
   // ---- A row of this lane
   int arow;
   if (grouped) {
-    const int pair = g.row_to_pair[row0 + m];
-    const uint64_t valid = __ballot(pair >= 0);
+    const uint64_t valid = __ballot(pair_a >= 0);
     if (valid == 0) return;                          // all-padding sub-tile (uniform per block)
     const int src = __ffsll((unsigned long long)valid) - 1;
-    const int fill = __shfl(pair, src, WAVE);
-    const int p = pair >= 0 ? pair : fill;
-    const int r = pair >= 0 ? row0 + m : row0 + src;
+    const int fill = __shfl(pair_a, src, WAVE);
+    const int p = pair_a >= 0 ? pair_a : fill;
+    const int r = pair_a >= 0 ? row0 + m : row0 + src;
     arow = g.a_by_row ? r : p / g.topk;
   } else {
     arow = min(row0 + m, g.M - 1);
   }
   const rsrc_t a_rs = make_rsrc(g.a, g.a_bytes);
   const uint32_t a_off = (uint32_t)arow * (uint32_t)(g.lda * TR::BYTES) + g4 * 16;
-
-  // ---- weight rows (one per tile j)
-  const int half = NT / 2;
-  const uint32_t w_bytes = (uint32_t)g.n_total * (uint32_t)(g.Kd * TR::BYTES);   // one expert
-  const rsrc_t w_rs = make_rsrc(reinterpret_cast<const char*>(g.w) + (size_t)e * w_bytes, w_bytes);
-  uint32_t b_off[NT];   // start of tile j's row group in the packed layout, plus the lane's 16 bytes
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    int n0;
-    if (g.epi == Epi::SITU)
-      n0 = (j < half) ? nb * half * 16 + j * 16 : g.d + nb * half * 16 + (j - half) * 16;
-    else
-      n0 = nb * NT * 16 + j * 16;
-    b_off[j] = (uint32_t)(n0 / 16) * (uint32_t)kchunks * 4096u + lane * 16;
+  rsrc_t a1_rs = a_rs;
+  uint32_t a1_off = 0;
+  if (DUAL) {
+    a1_rs = make_rsrc(g.a1, g.a1_bytes);
+    a1_off = (uint32_t)arow * (uint32_t)(g.lda1 * TR::BYTES) + g4 * 16;
   }
 
-  // ---- K range of this wave (wave-uniform)
-  const int wu = __builtin_amdgcn_readfirstlane(wid);
-  const int c0 = (int)((long)kchunks * wu / splits);
-  const int c1 = (int)((long)kchunks * (wu + 1) / splits);
-  constexpr int CB = TR::KCH * TR::BYTES;   // bytes per chunk row (256)
-
-  floatx4 acc[NT];
+  floatx4 acc[NACC];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NACC; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // Ping-pong buffers: chunk c + 1 is requested before chunk c is consumed. The request
+  auto issue = [&](int v, Chunk& a, Chunk (&b)[NT]) {
+    if (!DUAL || v < nch0) {
+      a = load_chunk_a(a_rs, a_off, (uint32_t)v * CB);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) b[j] = load_chunk_w(w_rs, b_off[j], (uint32_t)v * 4096u);
+    } else {
+      const uint32_t c = (uint32_t)(v - nch0);
+      a = load_chunk_a(a1_rs, a1_off, c * CB);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) b[j] = load_chunk_w(w1_rs, b1_off[j], c * 4096u);
+    }
+  };
+  auto consume = [&](int v, const Chunk& a, const Chunk (&b)[NT]) {
+    if (!DUAL || v < nch0) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[j] = mfma_chunk<ELT>(a, b[j], acc[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[NT + j] = mfma_chunk<ELT>(a, b[j], acc[NT + j]);
+    }
+  };
+
+  // Ping-pong buffers: chunk v + 1 is requested before chunk v is consumed. The request
   // index is clamped to the wave's last chunk, so the final requests re-read a chunk that
   // is still cached instead of running past the range; they are never consumed.
-  if (c0 < c1) {
-    Chunk a0, a1, b0[NT], b1[NT];
-    a0 = load_chunk_a(a_rs, a_off, (uint32_t)c0 * CB);
-#pragma unroll
-    for (int j = 0; j < NT; ++j) b0[j] = load_chunk_w(w_rs, b_off[j], (uint32_t)c0 * 4096u);
-    int c = c0;
-    // sched_barrier keeps the compiler from sinking the requests below the MFMAs that
-    // consume the older buffer (which would serialize every chunk on memory latency).
+  // sched_barrier keeps the compiler from sinking the requests below the MFMAs that
+  // consume the older buffer (which would serialize every chunk on memory latency).
+  if (v0 < v1) {
+    if (!DUAL || v0 < nch0)
+      a0 = load_chunk_a(a_rs, a_off, (uint32_t)v0 * CB);
+    else
+      a0 = load_chunk_a(a1_rs, a1_off, (uint32_t)(v0 - nch0) * CB);
+    int v = v0;
     while (true) {
-      const uint32_t o1 = (uint32_t)min(c + 1, c1 - 1);
-      a1 = load_chunk_a(a_rs, a_off, o1 * CB);
-#pragma unroll
-      for (int j = 0; j < NT; ++j) b1[j] = load_chunk_w(w_rs, b_off[j], o1 * 4096u);
+      issue(min(v + 1, v1 - 1), a1, b1);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < NT; ++j) acc[j] = mfma_chunk<ELT>(a0, b0[j], acc[j]);
+      consume(v, a0, b0);
       __builtin_amdgcn_sched_barrier(0);
-      if (++c >= c1) break;
-      const uint32_t o2 = (uint32_t)min(c + 1, c1 - 1);
-      a0 = load_chunk_a(a_rs, a_off, o2 * CB);
-#pragma unroll
-      for (int j = 0; j < NT; ++j) b0[j] = load_chunk_w(w_rs, b_off[j], o2 * 4096u);
+      if (++v >= v1) break;
+      issue(min(v + 1, v1 - 1), a0, b0);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < NT; ++j) acc[j] = mfma_chunk<ELT>(a1, b1[j], acc[j]);
+      consume(v, a1, b1);
       __builtin_amdgcn_sched_barrier(0);
-      if (++c >= c1) break;
+      if (++v >= v1) break;
     }
   }
 
   // ---- split-K reduction in fixed wave order
   if (splits > 1) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
+    for (int j = 0; j < NACC; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_red[((wid * NT + j) * 4 + i) * 64 + lane] = acc[j][i];
+      for (int i = 0; i < 4; ++i) s_red[((wid * NACC + j) * 4 + i) * 64 + lane] = acc[j][i];
     __syncthreads();
     if (wid != 0) return;
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
+    for (int j = 0; j < NACC; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float s = s_red[((0 * NT + j) * 4 + i) * 64 + lane];
-        for (int w = 1; w < splits; ++w) s += s_red[((w * NT + j) * 4 + i) * 64 + lane];
-        acc[j][i] = s;
+        float t = s_red[(j * 4 + i) * 64 + lane];
+        for (int w = 1; w < splits; ++w) t += s_red[((w * NACC + j) * 4 + i) * 64 + lane];
+        acc[j][i] = t;
       }
   }
 
@@ -229,75 +288,111 @@ __global__ __launch_bounds__(512) void stream_gemm_kernel(const StreamGemm g, in
     const int orow = row0 + 4 * g4 + i;
     int pair = -1;
     if (grouped) {
-      pair = g.row_to_pair[orow];
+      pair = pair_o[i];
       if (pair < 0) continue;
     } else {
       if (orow >= g.M) continue;
       pair = orow;
     }
-    if (g.epi == Epi::SITU) {
+    if (situ) {
       const float inv_b = 1.0f / g.beta;
       const float inv_lb = g.lbeta > 0.0f ? 1.0f / g.lbeta : 0.0f;
 #pragma unroll
       for (int j = 0; j < half; ++j) {
         const int col = nb * half * 16 + j * 16 + m;
-        const float v = situ(acc[j][i], acc[j + half][i], g.beta, inv_b, g.lbeta, inv_lb);
-        store_elt(g.out_elt, g.out, (size_t)orow * g.ldo + col, v);
+        if (col >= sg.n_out) continue;   // partial last block of the segment
+        const float v = situ_f(acc[j][i], acc[j + half][i], g.beta, inv_b, g.lbeta, inv_lb);
+        store_elt(sg.out_elt, sg.out, (size_t)orow * sg.ldo + col, v);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         const int col = nb * NT * 16 + j * 16 + m;
-        const float v = acc[j][i];
-        if (g.epi == Epi::STORE) {
-          store_elt(g.out_elt, g.out, (size_t)orow * g.ldo + col, v);
-        } else if (g.epi == Epi::PAIR) {
+        if (col >= sg.n_out) continue;   // partial last block of the segment
+        float v = acc[j][i];
+        if (sg.epi == Epi::STORE) {
+          store_elt(sg.out_elt, sg.out, (size_t)orow * sg.ldo + col, v);
+        } else if (sg.epi == Epi::PAIR) {
           const float wgt = g.pair_w ? g.pair_w[pair] : 1.0f;
-          reinterpret_cast<float*>(g.out)[(size_t)pair * g.ldo + col] = wgt * v;
-        } else if (g.epi == Epi::TOKEN) {
+          reinterpret_cast<float*>(sg.out)[(size_t)pair * sg.ldo + col] = wgt * v;
+        } else if (sg.epi == Epi::TOKEN) {
           const float wgt = g.pair_w ? g.pair_w[pair] : 1.0f;
-          store_elt(g.out_elt, g.out, (size_t)(pair / g.topk) * g.ldo + col, wgt * v);
-        } else {   // ADD
-          const size_t idx = (size_t)orow * g.ldo + col;
-          const float add = g.add ? load_elt(g.out_elt, g.add, idx) : 0.0f;
-          store_elt(g.out_elt, g.out, idx, add + v);
+          store_elt(sg.out_elt, sg.out, (size_t)(pair / g.topk) * sg.ldo + col, wgt * v);
+        } else if (sg.epi == Epi::ADD) {
+          const size_t idx = (size_t)orow * sg.ldo + col;
+          const float add = g.add ? load_elt(sg.out_elt, g.add, idx) : 0.0f;
+          store_elt(sg.out_elt, sg.out, idx, add + v);
+        } else if (DUAL) {   // ADD2: the first phase's result rounded to the output type, plus the second's
+          if (sg.out_elt == Elt::BF16) v = bf16_to_f32(f32_to_bf16(v));
+          store_elt(sg.out_elt, sg.out, (size_t)orow * sg.ldo + col, v + acc[NT + j][i]);
         }
       }
     }
   }
 }
 
+template <Elt ELT, int NT>
+static void launch_nt(bool dual, dim3 grid, dim3 block, size_t lds, hipStream_t stream, const StreamGemm& g,
+                      int blocks_total, int nch0, int nch1) {
+  if (dual)
+    hipLaunchKernelGGL((stream_gemm_kernel<ELT, NT, true>), grid, block, lds, stream, g, blocks_total, nch0, nch1);
+  else
+    hipLaunchKernelGGL((stream_gemm_kernel<ELT, NT, false>), grid, block, lds, stream, g, blocks_total, nch0, nch1);
+}
+
+// Waves a launch aims for (8 per CU). More, thinner waves measured slower: each wave
+// pays a fixed start-up chain of dependent lookups before its loads stream.
+constexpr long kTargetWaves = 2048;
+
 template <Elt ELT>
-static hipError_t launch_elt(const StreamGemm& g, int n_out_cols, int live, hipStream_t stream) {
+static hipError_t launch_elt(StreamGemm g, int live, hipStream_t stream) {
   using TR = EltTraits<ELT>;
-  const int kchunks = g.Kd / TR::KCH;
+  const bool dual = g.nseg == 1 && g.seg[0].epi == Epi::ADD2;
+  const int nch0 = g.Kd / TR::KCH;
+  const int nch1 = dual ? g.Kd1 / TR::KCH : 0;
   const int m_tiles = (g.M + 15) / 16;
-  const bool situ = g.epi == Epi::SITU;
-  const int tiles16 = n_out_cols / 16;   // output-column tiles (gate tiles for SituGLU)
   if (live < 1) live = 1;
-  // tile columns per wave: as many as keep >= ~2048 waves alive
-  int nt_out = 4;   // output tiles per wave (for SituGLU: gate tiles, each paired with its up tile)
-  if (situ) nt_out = 2;
-  while (nt_out > 1 && (tiles16 % nt_out != 0 || (long)live * (tiles16 / nt_out) < 2048)) nt_out >>= 1;
-  const int n_blocks = tiles16 / nt_out;
-  int splits = (int)((2048 + (long)live * n_blocks - 1) / ((long)live * n_blocks));
+  // Columns per wave: NT tiles of 16 (a SituGLU segment pairs NT/2 gate tiles with their
+  // up tiles; a segment's last block may be partial). Take the largest NT that still gives
+  // kTargetWaves live waves, else the smallest allowed; then split K over up to 8 waves of
+  // a workgroup to reach that count.
+  bool any_situ = false;
+  for (int i = 0; i < g.nseg; ++i) any_situ |= g.seg[i].epi == Epi::SITU;
+  auto blocks_of = [&](int i, int NT) {
+    const int tiles = g.seg[i].n_out / 16;
+    const int per = g.seg[i].epi == Epi::SITU ? NT / 2 : NT;
+    return (tiles + per - 1) / per;
+  };
+  int NT = 0, blocks_total = 0;
+  for (int cand : {4, 2, 1}) {
+    if (any_situ && cand < 2) break;
+    int t = 0;
+    for (int i = 0; i < g.nseg; ++i) t += blocks_of(i, cand);
+    NT = cand;
+    blocks_total = t;
+    if ((long)live * t >= kTargetWaves) break;
+  }
+  for (int i = 0, b0 = 0; i < g.nseg; ++i) {
+    g.seg[i].blocks = blocks_of(i, NT);
+    g.seg[i].block0 = b0;
+    b0 += g.seg[i].blocks;
+  }
+  int splits = (int)((kTargetWaves + (long)live * blocks_total - 1) / ((long)live * blocks_total));
   splits = splits < 1 ? 1 : (splits > 8 ? 8 : splits);
-  if (splits > kchunks) splits = kchunks;
-  const dim3 grid((unsigned)(m_tiles * n_blocks)), block(64 * splits);
-  const int NT = situ ? 2 * nt_out : nt_out;
-  const size_t lds = splits > 1 ? (size_t)splits * NT * 4 * 64 * sizeof(float) : 0;
+  if (splits > nch0 + nch1) splits = nch0 + nch1;
+  const dim3 grid((unsigned)(m_tiles * blocks_total)), block(64 * splits);
+  const size_t lds = splits > 1 ? (size_t)splits * (dual ? 2 : 1) * NT * 4 * 64 * sizeof(float) : 0;
   switch (NT) {
-    case 1: hipLaunchKernelGGL((stream_gemm_kernel<ELT, 1>), grid, block, lds, stream, g, n_blocks, kchunks); break;
-    case 2: hipLaunchKernelGGL((stream_gemm_kernel<ELT, 2>), grid, block, lds, stream, g, n_blocks, kchunks); break;
-    case 4: hipLaunchKernelGGL((stream_gemm_kernel<ELT, 4>), grid, block, lds, stream, g, n_blocks, kchunks); break;
-    default: return hipErrorInvalidValue;
+    case 1: launch_nt<ELT, 1>(dual, grid, block, lds, stream, g, blocks_total, nch0, nch1); break;
+    case 2: launch_nt<ELT, 2>(dual, grid, block, lds, stream, g, blocks_total, nch0, nch1); break;
+    default: launch_nt<ELT, 4>(dual, grid, block, lds, stream, g, blocks_total, nch0, nch1); break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_stream_gemm(const StreamGemm& g, Elt elt, int n_out_cols, int live_tiles, hipStream_t stream) {
-  return elt == Elt::BF16 ? launch_elt<Elt::BF16>(g, n_out_cols, live_tiles, stream)
-                          : launch_elt<Elt::F32>(g, n_out_cols, live_tiles, stream);
+hipError_t launch_stream_gemm(StreamGemm g, Elt elt, int live_tiles, hipStream_t stream) {
+  return elt == Elt::BF16 ? launch_elt<Elt::BF16>(g, live_tiles, stream)
+                          : launch_elt<Elt::F32>(g, live_tiles, stream);
 }
 
 }  // namespace lmoe

@@ -10,12 +10,26 @@ enum class Elt : int { F32 = 0, BF16 = 1 };
 
 // Epilogue of the weight-streaming GEMM.
 enum class Epi : int {
-  STORE = 0,    // y[row, n] = acc                        (out_elt)
-  SITU = 1,     // act[row, j] = SituGLU(acc[j], acc[d+j]) (out_elt)
-  PAIR = 2,     // ws[pair, n] = w[pair] * acc            (fp32, combined afterwards)
-  TOKEN = 3,    // out[token, n] = w[pair] * acc          (out_elt; K == 1)
-  ADD = 4,      // out[row, n] = add[row, n] + acc        (out_elt)
-  SITU_MX = 5   // SituGLU then MXFP8 requant per 32 outputs (codes + scales)
+  STORE = 0,    // y[row, n] = acc                                    (out_elt)
+  SITU = 1,     // y[row, j] = SituGLU(acc[j], acc[d + j])             (out_elt)
+  PAIR = 2,     // ws[pair, n] = w[pair] * acc                         (fp32, combined afterwards)
+  TOKEN = 3,    // out[token, n] = w[pair] * acc                       (out_elt; K == 1)
+  ADD = 4,      // out[row, n] = add[row, n] + acc                     (out_elt)
+  ADD2 = 5      // out[row, n] = round(acc) + acc1 (second K phase)    (out_elt)
+};
+
+// One group of output columns with its own weight and epilogue. Several segments that
+// share the activation rows run in one launch.
+struct Seg {
+  const void* w;       // packed weights [E or 1][n_total][Kd]
+  int n_total;         // rows of one expert's weight matrix
+  int n_out;           // output columns (SituGLU: d, the weight has 2d rows)
+  Epi epi;
+  Elt out_elt;
+  void* out;
+  int ldo;
+  int blocks;          // filled by the launcher
+  int block0;          // filled by the launcher
 };
 
 struct StreamGemm {
@@ -24,32 +38,28 @@ struct StreamGemm {
   const void* a;
   uint32_t a_bytes;          // size of the `a` buffer (hardware range check of the loads)
   int lda;
-  const uint8_t* a_scale;    // MX only: [*, Kd/32]
-  const void* w;             // [E, n_total, Kd]
-  const uint8_t* w_scale;    // MX only
-  int n_total;               // rows of one expert's weight
   int Kd;
+  // optional second K phase (dense, one segment): acc1 = a1 @ w1^T, epilogue ADD2
+  const void* a1;
+  uint32_t a1_bytes;
+  int lda1;
+  int Kd1;
+  const void* w1;
   int M;                     // dense: rows; grouped: rows_cap
   const int32_t* row_to_pair;  // NULL = dense
   const int32_t* tile_expert;
   int tile_m;
   int topk;
   int a_by_row;              // A row index = row (FC2) instead of the pair's token (FC1)
-  // output
-  Epi epi;
-  Elt out_elt;
-  void* out;
-  int ldo;
-  uint8_t* out_scale;        // SITU_MX
+  Seg seg[4];
+  int nseg;
   const float* pair_w;       // PAIR / TOKEN weights (NULL = 1)
   const void* add;           // ADD
   float beta, lbeta;
-  int d;                     // SITU: gate/up split
 };
 
 // live_tiles: expected number of 16-row tiles that hold rows (sizes the split-K factor).
-hipError_t launch_stream_gemm(const StreamGemm& g, Elt elt, int n_out_cols, int live_tiles, hipStream_t stream);
-hipError_t launch_stream_gemm_mx(const StreamGemm& g, int n_out_cols, int live_tiles, hipStream_t stream);
+hipError_t launch_stream_gemm(StreamGemm g, Elt elt, int live_tiles, hipStream_t stream);
 
 hipError_t launch_route(int T, int E, int K, const float* logits, const float* bias, float rsf, int renorm,
                         int32_t* ids, float* weights, hipStream_t stream);

@@ -69,17 +69,50 @@ lmoe_status lmoe_linear(int M, int N, int Kd, lmoe_dtype x_dtype, const void* x,
   g.a = x;
   g.a_bytes = (uint32_t)(M * (long)Kd * esize_of(x_dtype));
   g.lda = Kd;
-  g.w = w;
-  g.n_total = N;
   g.Kd = Kd;
   g.M = M;
   g.topk = 1;
-  g.epi = Epi::STORE;
-  g.out_elt = elt_of(y_dtype);
-  g.out = y;
-  g.ldo = N;
   g.beta = 1.0f;
-  return hip_status(launch_stream_gemm(g, elt_of(x_dtype), N, (M + 15) / 16, stream));
+  g.nseg = 1;
+  g.seg[0] = Seg{w, N, N, Epi::STORE, elt_of(y_dtype), y, N, 0, 0};
+  return hip_status(launch_stream_gemm(g, elt_of(x_dtype), (M + 15) / 16, stream));
+}
+
+lmoe_status lmoe_linear_multi(int M, int Kd, lmoe_dtype x_dtype, const void* x, int n_proj, const int* N,
+                              const void* const* w, const lmoe_dtype* y_dtype, void* const* y, const int* situ,
+                              float beta, float linear_beta, hipStream_t stream) {
+  if (M < 0 || Kd <= 0 || n_proj < 1 || n_proj > 4 || !N || !w || !y_dtype || !y) return LMOE_ERR_INVALID_ARG;
+  if (!dense_elt(x_dtype)) return LMOE_ERR_INVALID_ARG;
+  bool any_situ = false;
+  for (int i = 0; i < n_proj; ++i) {
+    if (N[i] <= 0 || !dense_elt(y_dtype[i])) return LMOE_ERR_INVALID_ARG;
+    if (N[i] % 16 != 0) return LMOE_ERR_UNSUPPORTED;
+    any_situ |= situ && situ[i];
+  }
+  if (any_situ && (!(beta > 0.0f) || !isfinite(beta) || isnan(linear_beta) || isinf(linear_beta)))
+    return LMOE_ERR_INVALID_ARG;
+  if (Kd % kchunk_of(x_dtype) != 0) return LMOE_ERR_UNSUPPORTED;
+  if (M == 0) return LMOE_OK;
+  if (!x) return LMOE_ERR_INVALID_ARG;
+  if (!fits32(M, Kd, x_dtype)) return LMOE_ERR_UNSUPPORTED;
+  StreamGemm g{};
+  g.a = x;
+  g.a_bytes = (uint32_t)(M * (long)Kd * esize_of(x_dtype));
+  g.lda = Kd;
+  g.Kd = Kd;
+  g.M = M;
+  g.topk = 1;
+  g.beta = beta;
+  g.lbeta = linear_beta;
+  g.nseg = n_proj;
+  for (int i = 0; i < n_proj; ++i) {
+    const bool si = situ && situ[i];
+    if (!w[i] || !y[i]) return LMOE_ERR_INVALID_ARG;
+    if (!fits32(si ? 2L * N[i] : N[i], Kd, x_dtype)) return LMOE_ERR_UNSUPPORTED;
+    g.seg[i] = Seg{w[i], si ? 2 * N[i] : N[i], N[i], si ? Epi::SITU : Epi::STORE, elt_of(y_dtype[i]), y[i], N[i], 0,
+                   0};
+  }
+  return hip_status(launch_stream_gemm(g, elt_of(x_dtype), (M + 15) / 16, stream));
 }
 
 lmoe_status lmoe_route(int T, int E, int K, const float* logits, const float* bias, float rsf, int renormalize,
@@ -169,8 +202,6 @@ lmoe_status lmoe_fc1_situ(int T, int E, int K, int in_dim, int d, int tile_m, lm
   g.a = a;
   g.a_bytes = (uint32_t)((long)T * in_dim * esize_of(a_dtype));
   g.lda = in_dim;
-  g.w = w1;
-  g.n_total = 2 * d;
   g.Kd = in_dim;
   g.M = dense ? T : rows_cap;
   g.row_to_pair = dense ? nullptr : row_to_pair;
@@ -178,15 +209,12 @@ lmoe_status lmoe_fc1_situ(int T, int E, int K, int in_dim, int d, int tile_m, lm
   g.tile_m = tile_m;
   g.topk = K;
   g.a_by_row = 0;
-  g.epi = Epi::SITU;
-  g.out_elt = elt_of(act_dtype);
-  g.out = act;
-  g.ldo = d;
   g.beta = beta;
   g.lbeta = linear_beta;
-  g.d = d;
+  g.nseg = 1;
+  g.seg[0] = Seg{w1, 2 * d, d, Epi::SITU, elt_of(act_dtype), act, d, 0, 0};
   const int live = dense ? (T + 15) / 16 : live_tiles((long)T * K, E);
-  return hip_status(launch_stream_gemm(g, elt_of(a_dtype), d, live, stream));
+  return hip_status(launch_stream_gemm(g, elt_of(a_dtype), live, stream));
 }
 
 size_t lmoe_fc2_workspace_bytes(int T, int K, int out_dim) {
@@ -219,8 +247,6 @@ lmoe_status lmoe_fc2_combine(int T, int E, int K, int d, int out_dim, int tile_m
   g.a = act;
   g.a_bytes = (uint32_t)(act_rows * d * esize_of(act_dtype));
   g.lda = d;
-  g.w = w2;
-  g.n_total = out_dim;
   g.Kd = d;
   g.M = dense ? T : rows_cap;
   g.row_to_pair = dense ? nullptr : row_to_pair;
@@ -230,19 +256,13 @@ lmoe_status lmoe_fc2_combine(int T, int E, int K, int d, int out_dim, int tile_m
   g.a_by_row = 1;
   g.pair_w = topk_weights;
   g.beta = 1.0f;
-  if (K == 1) {
-    g.epi = Epi::TOKEN;
-    g.out_elt = elt_of(out_dtype);
-    g.out = out;
-    g.ldo = out_dim;
-  } else {
-    g.epi = Epi::PAIR;
-    g.out_elt = Elt::F32;
-    g.out = workspace;
-    g.ldo = out_dim;
-  }
+  g.nseg = 1;
+  if (K == 1)
+    g.seg[0] = Seg{w2, out_dim, out_dim, Epi::TOKEN, elt_of(out_dtype), out, out_dim, 0, 0};
+  else
+    g.seg[0] = Seg{w2, out_dim, out_dim, Epi::PAIR, Elt::F32, workspace, out_dim, 0, 0};
   const int live = dense ? (T + 15) / 16 : live_tiles((long)T * K, E);
-  hipError_t err = launch_stream_gemm(g, elt_of(act_dtype), out_dim, live, stream);
+  hipError_t err = launch_stream_gemm(g, elt_of(act_dtype), live, stream);
   if (err != hipSuccess) return LMOE_ERR_HIP;
   if (K > 1) err = launch_combine(T, K, out_dim, (const float*)workspace, elt_of(out_dtype), out, stream);
   return hip_status(err);
@@ -262,18 +282,45 @@ lmoe_status lmoe_tail(int T, int L, int H, const float* latent, const void* gamm
   g.a = norm_out;
   g.a_bytes = (uint32_t)((long)T * L * esize_of(io_dtype));
   g.lda = L;
-  g.w = w_up;
-  g.n_total = H;
   g.Kd = L;
   g.M = T;
   g.topk = 1;
-  g.epi = Epi::ADD;
-  g.out_elt = elt_of(io_dtype);
-  g.out = out;
-  g.ldo = H;
   g.add = shared;
   g.beta = 1.0f;
-  return hip_status(launch_stream_gemm(g, elt_of(io_dtype), H, (T + 15) / 16, stream));
+  g.nseg = 1;
+  g.seg[0] = Seg{w_up, H, H, Epi::ADD, elt_of(io_dtype), out, H, 0, 0};
+  return hip_status(launch_stream_gemm(g, elt_of(io_dtype), (T + 15) / 16, stream));
+}
+
+lmoe_status lmoe_tail_shared(int T, int L, int H, int I, const float* latent, const void* gamma, float eps,
+                             const void* w_up, const void* shared_act, const void* w_s2, lmoe_dtype io_dtype,
+                             void* out, void* norm_out, hipStream_t stream) {
+  if (T < 0 || L <= 0 || H <= 0 || I <= 0) return LMOE_ERR_INVALID_ARG;
+  if (!dense_elt(io_dtype) || !(eps >= 0.0f) || !isfinite(eps)) return LMOE_ERR_INVALID_ARG;
+  if (L % kchunk_of(io_dtype) != 0 || I % kchunk_of(io_dtype) != 0 || H % 16 != 0) return LMOE_ERR_UNSUPPORTED;
+  if (T == 0) return LMOE_OK;
+  if (!latent || !w_up || !shared_act || !w_s2 || !out || !norm_out) return LMOE_ERR_INVALID_ARG;
+  if (out == shared_act || out == norm_out) return LMOE_ERR_INVALID_ARG;
+  if (!fits32(T, L, io_dtype) || !fits32(T, I, io_dtype) || !fits32(H, L, io_dtype) || !fits32(H, I, io_dtype))
+    return LMOE_ERR_UNSUPPORTED;
+  hipError_t err = launch_rmsnorm(T, L, latent, gamma, eps, elt_of(io_dtype), norm_out, stream);
+  if (err != hipSuccess) return LMOE_ERR_HIP;
+  StreamGemm g{};
+  g.a = shared_act;                  // phase 0: shared-expert FC2, rounded like a stored tensor
+  g.a_bytes = (uint32_t)((long)T * I * esize_of(io_dtype));
+  g.lda = I;
+  g.Kd = I;
+  g.a1 = norm_out;                   // phase 1: up projection of the normalized latent
+  g.a1_bytes = (uint32_t)((long)T * L * esize_of(io_dtype));
+  g.lda1 = L;
+  g.Kd1 = L;
+  g.w1 = w_up;
+  g.M = T;
+  g.topk = 1;
+  g.beta = 1.0f;
+  g.nseg = 1;
+  g.seg[0] = Seg{w_s2, H, H, Epi::ADD2, elt_of(io_dtype), out, H, 0, 0};
+  return hip_status(launch_stream_gemm(g, elt_of(io_dtype), (T + 15) / 16, stream));
 }
 
 lmoe_status lmoe_situ_masked(int E, int T_max, int d, lmoe_dtype dtype, const void* in,

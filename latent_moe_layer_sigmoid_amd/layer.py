@@ -46,9 +46,13 @@ class LatentMoELayer:
     W_s1 [2I,H], W_s2 [H,I], gamma [L], W_up [H,L]; the projections are packed on the
     device (lmoe_pack_weights) when the layer is built."""
 
-    def __init__(self, shape: LayerShape, weights: dict, device="cuda"):
+    def __init__(self, shape: LayerShape, weights: dict, device="cuda", fused=True):
         B.lib()   # fail loudly now if the library is missing
         self.s = shape
+        # fused: the hidden-input projections share one launch (lmoe_linear_multi) and the
+        # shared expert's FC2 is folded into the up projection (lmoe_tail_shared);
+        # otherwise every step is its own call.
+        self.fused = fused
         self.device = torch.device(device)
         self._bufs = {}
         # weights go to HBM in the packed MFMA-operand layout once, at construction
@@ -114,9 +118,16 @@ class LatentMoELayer:
         dt = _lmoe_dtype(s.dtype)
         rc = b["rows_cap"]
         mark = timer.mark if timer is not None else (lambda name: None)
-        # a1 router GEMM -> fp32 logits
-        mark("router")
-        B.lmoe_linear(T, s.E, s.H, dt, X, dt, w["W_r"], B.LMOE_F32, b["logits"], stream)
+        if self.fused:
+            # a1 router GEMM, a3 latent down projection, a10 shared FC1 + SituGLU: one launch
+            mark("front")
+            B.lmoe_linear_multi(T, s.H, dt, X, 3, [s.E, s.L, s.I], [w["W_r"], w["W_down"], w["W_s1"]],
+                                [B.LMOE_F32, dt, dt], [b["logits"], b["x"], b["act_s"]], [0, 0, 1], s.beta,
+                                s.linear_beta, stream)
+        else:
+            # a1 router GEMM -> fp32 logits
+            mark("router")
+            B.lmoe_linear(T, s.E, s.H, dt, X, dt, w["W_r"], B.LMOE_F32, b["logits"], stream)
         # a2 routing
         mark("route")
         B.lmoe_route(T, s.E, s.K, b["logits"], w["bias"], s.rsf, 1, b["ids"], b["weights"], stream)
@@ -125,9 +136,10 @@ class LatentMoELayer:
         B.lmoe_permute(T, s.E, s.K, s.tile_m, b["ids"], b["counts"], b["offsets"], b["tile_offsets"],
                        b["row_to_pair"], b["tile_expert"], b["pair_to_row"], rc, b["perm_ws"],
                        b["perm_ws_bytes"], stream)
-        # a3 latent down projection
-        mark("down")
-        B.lmoe_linear(T, s.L, s.H, dt, X, dt, w["W_down"], dt, b["x"], stream)
+        if not self.fused:
+            # a3 latent down projection
+            mark("down")
+            B.lmoe_linear(T, s.L, s.H, dt, X, dt, w["W_down"], dt, b["x"], stream)
         if s.experts == "mx":
             # a4 input quantization, a6-a8 FC1 + SituGLU + requant, a9 FC2 + combine
             mark("quant")
@@ -150,16 +162,22 @@ class LatentMoELayer:
             B.lmoe_fc2_combine(T, s.E, s.K, s.d, s.L, s.tile_m, dt, b["act"], None, b["row_to_pair"],
                                b["tile_expert"], dt, w["W2"], None, b["weights"], B.LMOE_F32, b["z"], rc,
                                b["fc2_ws"], b["fc2_ws_bytes"], stream)
-        # a10 shared expert (dense mode: E = K = 1)
-        mark("shared_fc1")
-        B.lmoe_fc1_situ(T, 1, 1, s.H, s.I, 16, dt, X, None, None, None, dt, w["W_s1"], None, s.beta,
-                        s.linear_beta, dt, b["act_s"], None, T, stream)
-        mark("shared_fc2")
-        B.lmoe_fc2_combine(T, 1, 1, s.I, s.H, 16, dt, b["act_s"], None, None, None, dt, w["W_s2"], None, None,
-                           dt, b["sh"], T, None, 0, stream)
-        # a11 + a12 latent RMSNorm, up projection with the shared add in its epilogue
-        mark("tail")
-        B.lmoe_tail(T, s.L, s.H, b["z"], w["gamma"], s.eps, w["W_up"], b["sh"], dt, b["out"], b["n"], stream)
+        if self.fused:
+            # a10 shared FC2 folded into a11 + a12: RMSNorm, then one GEMM over both K ranges
+            mark("tail")
+            B.lmoe_tail_shared(T, s.L, s.H, s.I, b["z"], w["gamma"], s.eps, w["W_up"], b["act_s"], w["W_s2"], dt,
+                               b["out"], b["n"], stream)
+        else:
+            # a10 shared expert (dense mode: E = K = 1)
+            mark("shared_fc1")
+            B.lmoe_fc1_situ(T, 1, 1, s.H, s.I, 16, dt, X, None, None, None, dt, w["W_s1"], None, s.beta,
+                            s.linear_beta, dt, b["act_s"], None, T, stream)
+            mark("shared_fc2")
+            B.lmoe_fc2_combine(T, 1, 1, s.I, s.H, 16, dt, b["act_s"], None, None, None, dt, w["W_s2"], None, None,
+                               dt, b["sh"], T, None, 0, stream)
+            # a11 + a12 latent RMSNorm, up projection with the shared add in its epilogue
+            mark("tail")
+            B.lmoe_tail(T, s.L, s.H, b["z"], w["gamma"], s.eps, w["W_up"], b["sh"], dt, b["out"], b["n"], stream)
         mark(None)
         return b["out"]
 

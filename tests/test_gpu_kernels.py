@@ -353,6 +353,49 @@ def test_dense_mode_shared_expert(B, dt):
     assert norm_err(f64(sh), ref) <= 1e-2
 
 
+@pytest.mark.parametrize("M,Kd,dt", [(8, 7168, "bf16"), (3, 256, "f32"), (37, 384, "bf16")])
+def test_linear_multi_matches_oracle(B, M, Kd, dt):
+    rng = np.random.default_rng(M + Kd)
+    td = torch.bfloat16 if dt == "bf16" else torch.float32
+    ldt = B.LMOE_BF16 if dt == "bf16" else B.LMOE_F32
+    N = [48, 128, 64]
+    x = torch.from_numpy(rng.standard_normal((M, Kd))).to(td)
+    ws = [torch.from_numpy(rng.standard_normal((n * (2 if i == 2 else 1), Kd)) / math.sqrt(Kd)).to(td)
+          for i, n in enumerate(N)]
+    ys = [torch.empty(M, N[0], device=DEV), torch.empty(M, N[1], dtype=td, device=DEV),
+          torch.empty(M, N[2], dtype=td, device=DEV)]
+    B.lmoe_linear_multi(M, Kd, ldt, x.to(DEV), 3, N, [B.packed(w.to(DEV)) for w in ws], [B.LMOE_F32, ldt, ldt], ys,
+                        [0, 0, 1], 1.0, 0.5)
+    torch.cuda.synchronize()
+    x64 = f64(x)
+    assert norm_err(f64(ys[0]), oracle.f32_round(oracle.linear(x64, f64(ws[0])))) <= 1e-5
+    assert norm_err(f64(ys[1]), oracle.round_to(oracle.linear(x64, f64(ws[1])), dt)) <= 8e-3
+    ref2 = oracle.round_to(oracle.situ_glu_rows(oracle.linear(x64, f64(ws[2])), 1.0, 0.5), dt)
+    assert norm_err(f64(ys[2]), ref2) <= 1e-2
+
+
+@pytest.mark.parametrize("T,L,H,I,dt", [(8, 2048, 7168, 4096, "bf16"), (4, 128, 256, 128, "f32"),
+                                        (21, 256, 512, 384, "bf16")])
+def test_tail_shared_matches_oracle(B, T, L, H, I, dt):
+    rng = np.random.default_rng(T + L + I)
+    td = torch.bfloat16 if dt == "bf16" else torch.float32
+    ldt = B.LMOE_BF16 if dt == "bf16" else B.LMOE_F32
+    z = torch.from_numpy(rng.standard_normal((T, L)) * 0.3).float()
+    gamma = torch.from_numpy(rng.uniform(0.9, 1.1, L)).to(td)
+    Wup = torch.from_numpy(rng.standard_normal((H, L)) / math.sqrt(L)).to(td)
+    a_s = torch.from_numpy(rng.standard_normal((T, I))).to(td)
+    Ws2 = torch.from_numpy(rng.standard_normal((H, I)) / math.sqrt(I)).to(td)
+    out = torch.empty(T, H, dtype=td, device=DEV)
+    n = torch.empty(T, L, dtype=td, device=DEV)
+    B.lmoe_tail_shared(T, L, H, I, z.to(DEV), gamma.to(DEV), 1e-6, B.packed(Wup.to(DEV)), a_s.to(DEV),
+                       B.packed(Ws2.to(DEV)), ldt, out, n)
+    torch.cuda.synchronize()
+    sh = oracle.round_to(oracle.linear(f64(a_s), f64(Ws2)), dt)
+    rn, rout = oracle.tail(f64(z), f64(gamma), 1e-6, f64(Wup), sh, dt)
+    assert norm_err(f64(n), rn) <= 1e-2
+    assert norm_err(f64(out), rout) <= 1e-2
+
+
 # ------------------------------------------------------------------------------- tail
 
 @pytest.mark.parametrize("T,L,H,dt,alias", [(8, 2048, 7168, "bf16", False), (4, 128, 256, "f32", True),

@@ -15,19 +15,19 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def build_layer(cfg, seed):
+def build_layer(cfg, seed, fused=True):
     from latent_moe_layer_sigmoid_amd import LatentMoELayer, LayerShape
     w_dev = LI.make_layer_weights(cfg, seed, device=DEV)
     shape = LayerShape(H=cfg.H, L=cfg.L, E=cfg.E, K=cfg.K, d=cfg.d, I=cfg.I, dtype=cfg.dtype, experts=cfg.experts,
                        beta=cfg.beta, linear_beta=cfg.linear_beta, rsf=cfg.rsf, eps=cfg.eps, tile_m=cfg.tile_m)
-    return LatentMoELayer(shape, w_dev), w_dev
+    return LatentMoELayer(shape, w_dev, fused=fused), w_dev
 
 
-def check_layer(cfg, seed, tokens=None, out_tol=1e-2):
+def check_layer(cfg, seed, tokens=None, out_tol=1e-2, fused=True):
     """Run the layer on the GPU for all T tokens; compare routing / permutation for all
     tokens and the float outputs for `tokens` (all when None) against the oracle."""
-    print(f"[layer parity] {cfg.name} T={cfg.T} seed={seed}", flush=True)
-    layer, w_dev = build_layer(cfg, seed)
+    print(f"[layer parity] {cfg.name} T={cfg.T} seed={seed} fused={fused}", flush=True)
+    layer, w_dev = build_layer(cfg, seed, fused)
     w_cpu = LI.make_layer_weights(cfg, seed, device="cpu", experts=False)
     o = oracle_weights(cfg, seed, w_cpu)
     X, _ = guarded_x(cfg, seed, o["W_r"], o["bias"])
@@ -62,7 +62,8 @@ def check_layer(cfg, seed, tokens=None, out_tol=1e-2):
         act = f64(b["act"])[p2r]                     # [len(sel), K, d]
         assert norm_err(act, ref["act"]) <= 1e-2
     assert norm_err(f64(b["z"])[sel], ref["z"]) <= 1e-2
-    assert norm_err(f64(b["sh"])[sel], ref["sh"]) <= 1e-2
+    if not fused:
+        assert norm_err(f64(b["sh"])[sel], ref["sh"]) <= 1e-2
     assert norm_err(f64(b["n"])[sel], ref["n"]) <= 1e-2
     err = norm_err(f64(out)[sel], ref["out"])
     print(f"[layer parity] {cfg.name}: out err {err:.3e}", flush=True)
@@ -70,9 +71,9 @@ def check_layer(cfg, seed, tokens=None, out_tol=1e-2):
     return layer, X
 
 
-@pytest.mark.parametrize("seed", [1, 101])
-def test_layer_tiny_fp32(seed):
-    check_layer(LI.TINY, seed)
+@pytest.mark.parametrize("seed,fused", [(1, True), (101, True), (1, False)])
+def test_layer_tiny_fp32(seed, fused):
+    check_layer(LI.TINY, seed, fused=fused)
 
 
 def test_layer_decode_bf16_full_size():
@@ -84,8 +85,8 @@ def test_layer_decode_bf16_full_size():
     assert torch.equal(first.view(torch.int16), layer.buffers(LI.DECODE.T)["out"].view(torch.int16))
 
 
-def test_layer_decode_second_seed():
-    check_layer(LI.DECODE, 102)
+def test_layer_decode_second_seed_unfused_path():
+    check_layer(LI.DECODE, 102, fused=False)
 
 
 def test_layer_prefill_reduced_dims_ragged_tiles():
