@@ -36,14 +36,19 @@ def layer_bytes(cfg, n_touched):
     once (bf16 = 2 bytes)."""
     e = 2
     dense = e * (cfg.E * cfg.H + cfg.L * cfg.H + 3 * cfg.H * cfg.I + cfg.H * cfg.L)
-    experts = n_touched * 3 * cfg.L * cfg.d * e
+    experts = n_touched * 3 * cfg.L * cfg.d * (e if cfg.experts != "mx" else 0.5 + 1 / 32)
     acts = e * cfg.T * cfg.H * 2
-    return dense + experts + acts
+    return int(dense + experts + acts)
 
 
 def fc1_bytes(cfg, n_touched, rows):
     """Algorithmic bytes of one grouped FC1 + SituGLU launch: W1 of each touched expert
-    (2d x L bf16) read once, the latent rows read once, the activation rows written once."""
+    (2d x L) read once, the latent rows read once, the activation rows written once.
+    bf16: 2 bytes per element; MX: 0.5 byte per e2m1 weight + 1/32 byte of scale, 1 byte
+    per e4m3 activation + 1/32 byte of scale."""
+    if cfg.experts == "mx":
+        w = n_touched * 2 * cfg.d * cfg.L * (0.5 + 1 / 32)
+        return int(w + cfg.T * cfg.L * (1 + 1 / 32) + rows * cfg.d * (1 + 1 / 32))
     return n_touched * 2 * cfg.d * cfg.L * 2 + cfg.T * cfg.L * 2 + rows * cfg.d * 2
 
 

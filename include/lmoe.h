@@ -78,6 +78,17 @@ const char* lmoe_status_string(lmoe_status s);
 lmoe_status lmoe_pack_weights(int batch, int N, int Kd, lmoe_dtype dtype, const void* src, void* dst,
                               hipStream_t stream);
 
+/* MXFP4 weight packing for the MX expert GEMMs. src: `batch` matrices [N, Kd] as codes
+ * [N, Kd/2] (two E2M1 per byte, element 2i in the low nibble) and E8M0 scales [N, Kd/32];
+ * dst: same sizes, packed. For 16-row group n16 and 512-wide K stage s (nst = Kd / 512):
+ * the codes' 4 KB block at byte (n16*nst + s)*4096 holds at byte q*1024 + g*256 + r*16 + j
+ * the source code byte (s*512 + q*128 + g*32)/2 + j of row 16*n16 + r (j < 16); the
+ * scales' 256-byte block at (n16*nst + s)*256 holds at byte (16g + r)*4 + q the scale of
+ * K block s*16 + q*4 + g of that row. Lane l = 16g + r then holds one 32-element MX block
+ * per scaled MFMA. N % 16 == 0 and Kd % 512 == 0, else LMOE_ERR_UNSUPPORTED. */
+lmoe_status lmoe_pack_mxfp4_weights(int batch, int N, int Kd, const uint8_t* codes_src, const uint8_t* scales_src,
+                                    uint8_t* codes_dst, uint8_t* scales_dst, hipStream_t stream);
+
 /* a1 / a3 -- dense projection y[M,N] = x[M,Kd] @ w[N,Kd]^T with fp32 accumulation.
  * Used for the router GEMM (y LMOE_F32: [P1] commit 4, DeepSeekV3 routing takes FP32
  * logits; [P2] "Description": the router GEMM runs first) and the latent down projection
@@ -159,10 +170,12 @@ lmoe_status lmoe_quant_mxfp8(int rows, int cols, lmoe_dtype in_dtype, const void
  * K == 1: row r = token r for r < T.
  * beta must be finite and > 0 ([P1] commit 3: beta is required); linear_beta <= 0 means
  * unset (passes up through). tile_m must be the tile the permutation was built with.
- * a_dtype/w_dtype: F32/F32, BF16/BF16, or MXFP8_E4M3/MXFP4_E2M1 (a_scale [T, in_dim/32],
- * w1_scale [E, 2d, in_dim/32]). act_dtype: F32 or BF16 (same as a_dtype for the dense
- * dtypes), or MXFP8_E4M3 with act_scale [rows_cap, d/32] (SituGLU in fp32, then
- * requantized per 32 outputs). */
+ * a_dtype/w_dtype: F32/F32 or BF16/BF16 with act_dtype == a_dtype; or MXFP8_E4M3 /
+ * MXFP4_E2M1 (grouped mode only; a_scale [T, in_dim/32] row-major, w1 and w1_scale
+ * packed by lmoe_pack_mxfp4_weights, in_dim % 512 == 0, d % 32 == 0) with act_dtype
+ * MXFP8_E4M3: SituGLU in fp32 on the dequantized accumulators, then each 32 consecutive
+ * outputs requantized as lmoe_quant_mxfp8 does (act codes [rows_cap, d], act_scale
+ * [rows_cap, d/32]). */
 lmoe_status lmoe_fc1_situ(int T, int E, int K, int in_dim, int d, int tile_m,
                           lmoe_dtype a_dtype, const void* a, const uint8_t* a_scale,
                           const int32_t* row_to_pair, const int32_t* tile_expert,
@@ -180,8 +193,9 @@ lmoe_status lmoe_fc1_situ(int T, int E, int K, int in_dim, int d, int tile_m,
  * With K > 1 the per-pair products go through `workspace` (>= lmoe_fc2_workspace_bytes
  * bytes) and are summed in fixed k order, so the result is bitwise reproducible.
  * Dense mode as in lmoe_fc1_situ (shared expert: E == 1, K == 1).
- * act_dtype/w_dtype: F32/F32, BF16/BF16 or MXFP8_E4M3/MXFP4_E2M1 (act_scale [rows_cap,
- * d/32], w2_scale [E, out_dim, d/32]). out_dtype F32 or BF16. */
+ * act_dtype/w_dtype: F32/F32, BF16/BF16, or MXFP8_E4M3/MXFP4_E2M1 (grouped mode only;
+ * act_scale [rows_cap, d/32] row-major; w2, w2_scale packed by lmoe_pack_mxfp4_weights;
+ * d % 512 == 0, out_dim % 64 == 0). out_dtype F32 or BF16. */
 size_t lmoe_fc2_workspace_bytes(int T, int K, int out_dim);
 lmoe_status lmoe_fc2_combine(int T, int E, int K, int d, int out_dim, int tile_m,
                              lmoe_dtype act_dtype, const void* act, const uint8_t* act_scale,

@@ -33,6 +33,7 @@ SIGNATURES = [
     ("lmoe_abi_version", _i, []),
     ("lmoe_status_string", ctypes.c_char_p, [_i]),
     ("lmoe_pack_weights", _i, [_i, _i, _i, _i, _p, _p, _p]),
+    ("lmoe_pack_mxfp4_weights", _i, [_i, _i, _i, _p, _p, _p, _p, _p]),
     ("lmoe_linear", _i, [_i, _i, _i, _i, _p, _i, _p, _i, _p, _p]),
     ("lmoe_linear_multi", _i, [_i, _i, _i, _p, _i, _p, _p, _p, _p, _p, _f, _f, _p]),
     ("lmoe_route", _i, [_i, _i, _i, _p, _p, _f, _i, _p, _p, _p]),
@@ -120,6 +121,21 @@ def packed(w, dtype=None, stream=None):
 def lmoe_linear(M, N, Kd, x_dtype, x, w_dtype, w, y_dtype, y, stream=None):
     _check("lmoe_linear", lib().lmoe_linear(M, N, Kd, x_dtype, _ptr(x), w_dtype, _ptr(w), y_dtype, _ptr(y),
                                             _stream(stream)))
+
+
+def lmoe_pack_mxfp4_weights(batch, N, Kd, codes_src, scales_src, codes_dst, scales_dst, stream=None):
+    _check("lmoe_pack_mxfp4_weights", lib().lmoe_pack_mxfp4_weights(batch, N, Kd, _ptr(codes_src), _ptr(scales_src),
+                                                                    _ptr(codes_dst), _ptr(scales_dst),
+                                                                    _stream(stream)))
+
+
+def packed_mxfp4(codes, scales, stream=None):
+    """Packed copies of MXFP4 weights: codes [(batch,) N, Kd/2] and scales [(batch,) N, Kd/32]."""
+    batch = codes.shape[0] if codes.dim() == 3 else 1
+    N, Kd = codes.shape[-2], codes.shape[-1] * 2
+    c, s = torch.empty_like(codes), torch.empty_like(scales)
+    lmoe_pack_mxfp4_weights(batch, N, Kd, codes, scales, c, s, stream)
+    return c, s
 
 
 def lmoe_linear_multi(M, Kd, x_dtype, x, n_proj, N, w, y_dtype, y, situ, beta, linear_beta, stream=None):

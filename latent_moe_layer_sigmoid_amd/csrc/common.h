@@ -69,6 +69,14 @@ LMOE_DEV int mx_e4m3_exponent(float amax) {
   return x < -127 ? -127 : (x > 127 ? 127 : x);
 }
 
+// Buffer resource: wave-uniform base address and byte size; the hardware range-checks
+// every access (reads past the end return zeros, writes past it are dropped).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+LMOE_DEV rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 template <typename T>
 LMOE_DEV T wave_max(T v) {
 #pragma unroll

@@ -222,4 +222,52 @@ hipError_t launch_pack_weights(int batch, int N, int Kd, int esize, const void* 
   return hipGetLastError();
 }
 
+// ---- MXFP4 weight packing. Per matrix [N, Kd] (codes [N, Kd/2] bytes, two e2m1 per byte,
+// scales [N, Kd/32] e8m0), 16-row group n16 and 512-wide K stage s (nst = Kd / 512):
+//   codes: 4 KB block at (n16 * nst + s) * 4096; byte q*1024 + g*256 + r*16 + j holds
+//          source byte (s*512 + q*128 + g*32) / 2 + j of row 16*n16 + r (j < 16);
+//   scales: 256 B block at (n16 * nst + s) * 256; byte (g*16 + r)*4 + q holds the scale
+//          of K block s*16 + q*4 + g of row 16*n16 + r.
+// Lane l = 16g + r then reads its MFMA q operand (32 e2m1 values) at q*1024 + 16l and its
+// four scales as one dword at 4l.
+__global__ __launch_bounds__(256) void pack_mxfp4_codes_kernel(long pieces, int N, int Kd,
+                                                               const uint4* __restrict__ src, uint4* __restrict__ dst) {
+  const long p = (long)blockIdx.x * 256 + threadIdx.x;
+  if (p >= pieces) return;
+  const int nst = Kd / 512;
+  const long per_matrix = (long)N * Kd / 32;        // 16-byte pieces per matrix
+  const long b = p / per_matrix, pm = p - b * per_matrix;
+  const long blk = pm >> 8;
+  const int w = (int)(pm & 255), q = w >> 6, l = w & 63, g = l >> 4, r = l & 15;
+  const long n16 = blk / nst, st = blk - n16 * nst;
+  const long row = n16 * 16 + r;
+  const long byte0 = (st * 512 + q * 128 + g * 32) / 2;
+  dst[p] = src[b * per_matrix + (row * (Kd / 2) + byte0) / 16];
+}
+
+__global__ __launch_bounds__(256) void pack_mxfp4_scales_kernel(long n, int N, int Kd, const uint8_t* __restrict__ src,
+                                                                uint8_t* __restrict__ dst) {
+  const long p = (long)blockIdx.x * 256 + threadIdx.x;
+  if (p >= n) return;
+  const int nst = Kd / 512;
+  const long per_matrix = (long)N * Kd / 32;
+  const long b = p / per_matrix, pm = p - b * per_matrix;
+  const long blk = pm >> 8;
+  const int w = (int)(pm & 255), l = w >> 2, q = w & 3, g = l >> 4, r = l & 15;
+  const long n16 = blk / nst, st = blk - n16 * nst;
+  const long row = n16 * 16 + r;
+  dst[p] = src[b * per_matrix + row * (Kd / 32) + st * 16 + q * 4 + g];
+}
+
+hipError_t launch_pack_mxfp4(int batch, int N, int Kd, const void* codes_src, const void* scales_src, void* codes_dst,
+                             void* scales_dst, hipStream_t stream) {
+  const long pieces = (long)batch * N * Kd / 32;
+  hipLaunchKernelGGL(pack_mxfp4_codes_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, stream, pieces, N,
+                     Kd, (const uint4*)codes_src, (uint4*)codes_dst);
+  const long ns = (long)batch * N * Kd / 32;
+  hipLaunchKernelGGL(pack_mxfp4_scales_kernel, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, stream, ns, N, Kd,
+                     (const uint8_t*)scales_src, (uint8_t*)scales_dst);
+  return hipGetLastError();
+}
+
 }  // namespace lmoe

@@ -30,11 +30,6 @@ struct Chunk {
 // size, range-checked by the hardware: reads past the end return zeros), a per-lane
 // 32-bit byte offset that never changes, and the chunk offset in a scalar register, so
 // the K loop carries no per-lane address arithmetic.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-LMOE_DEV rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
 
 // Activation rows are row-major: lane l's share of a 256-byte chunk row is the four
 // 16-byte pieces at 16 * (l / 16) + 64 * q, q = 0..3 (voff includes 16 * (l / 16)), so

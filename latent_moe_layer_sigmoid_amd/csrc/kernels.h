@@ -15,7 +15,8 @@ enum class Epi : int {
   PAIR = 2,     // ws[pair, n] = w[pair] * acc                         (fp32, combined afterwards)
   TOKEN = 3,    // out[token, n] = w[pair] * acc                       (out_elt; K == 1)
   ADD = 4,      // out[row, n] = add[row, n] + acc                     (out_elt)
-  ADD2 = 5      // out[row, n] = round(acc) + acc1 (second K phase)    (out_elt)
+  ADD2 = 5,     // out[row, n] = round(acc) + acc1 (second K phase)    (out_elt)
+  SITU_MX = 6   // SituGLU, then MXFP8 requant per 32 outputs (codes + e8m0 scales)
 };
 
 // One group of output columns with its own weight and epilogue. Several segments that
@@ -56,10 +57,17 @@ struct StreamGemm {
   const float* pair_w;       // PAIR / TOKEN weights (NULL = 1)
   const void* add;           // ADD
   float beta, lbeta;
+  // MX operands: e8m0 scales of A (row-major [*, Kd/32]) and of the packed weights
+  const uint8_t* a_scale;
+  uint32_t a_scale_bytes;
+  const uint8_t* w_scale;
+  uint8_t* out_scale;        // SITU_MX: [rows_cap, n_out/32]
 };
 
 // live_tiles: expected number of 16-row tiles that hold rows (sizes the split-K factor).
 hipError_t launch_stream_gemm(StreamGemm g, Elt elt, int live_tiles, hipStream_t stream);
+// MXFP8 x packed MXFP4 (grouped mode, one segment: SITU_MX or PAIR / TOKEN); Kd % 512 == 0.
+hipError_t launch_stream_gemm_mx(StreamGemm g, int live_tiles, hipStream_t stream);
 
 hipError_t launch_route(int T, int E, int K, const float* logits, const float* bias, float rsf, int renorm,
                         int32_t* ids, float* weights, hipStream_t stream);
@@ -75,6 +83,8 @@ hipError_t launch_quant_mxfp8(int rows, int cols, Elt elt, const void* in, uint8
                               hipStream_t stream);
 hipError_t launch_combine(int T, int K, int N, const float* ws, Elt out_elt, void* out, hipStream_t stream);
 hipError_t launch_pack_weights(int batch, int N, int Kd, int esize, const void* src, void* dst, hipStream_t stream);
+hipError_t launch_pack_mxfp4(int batch, int N, int Kd, const void* codes_src, const void* scales_src, void* codes_dst,
+                             void* scales_dst, hipStream_t stream);
 hipError_t launch_rmsnorm(int T, int L, const float* z, const void* gamma, float eps, Elt elt, void* out,
                           hipStream_t stream);
 

@@ -57,6 +57,16 @@ lmoe_status lmoe_pack_weights(int batch, int N, int Kd, lmoe_dtype dtype, const 
   return hip_status(launch_pack_weights(batch, N, Kd, (int)esize_of(dtype), src, dst, stream));
 }
 
+lmoe_status lmoe_pack_mxfp4_weights(int batch, int N, int Kd, const uint8_t* codes_src, const uint8_t* scales_src,
+                                    uint8_t* codes_dst, uint8_t* scales_dst, hipStream_t stream) {
+  if (batch < 0 || N < 0 || Kd < 0) return LMOE_ERR_INVALID_ARG;
+  if (N % 16 != 0 || Kd % 512 != 0) return LMOE_ERR_UNSUPPORTED;
+  if (batch == 0 || N == 0 || Kd == 0) return LMOE_OK;
+  if (!codes_src || !scales_src || !codes_dst || !scales_dst || codes_src == codes_dst || scales_src == scales_dst)
+    return LMOE_ERR_INVALID_ARG;
+  return hip_status(launch_pack_mxfp4(batch, N, Kd, codes_src, scales_src, codes_dst, scales_dst, stream));
+}
+
 lmoe_status lmoe_linear(int M, int N, int Kd, lmoe_dtype x_dtype, const void* x, lmoe_dtype w_dtype,
                         const void* w, lmoe_dtype y_dtype, void* y, hipStream_t stream) {
   if (M < 0 || N <= 0 || Kd <= 0) return LMOE_ERR_INVALID_ARG;
@@ -190,8 +200,32 @@ lmoe_status lmoe_fc1_situ(int T, int E, int K, int in_dim, int d, int tile_m, lm
   if (!(beta > 0.0f) || !isfinite(beta) || isnan(linear_beta) || isinf(linear_beta)) return LMOE_ERR_INVALID_ARG;
   const bool mx = a_dtype == LMOE_MXFP8_E4M3 || w_dtype == LMOE_MXFP4_E2M1;
   if (mx) {
-    if (a_dtype != LMOE_MXFP8_E4M3 || w_dtype != LMOE_MXFP4_E2M1) return LMOE_ERR_INVALID_ARG;
-    return LMOE_ERR_UNSUPPORTED;
+    if (a_dtype != LMOE_MXFP8_E4M3 || w_dtype != LMOE_MXFP4_E2M1 || act_dtype != LMOE_MXFP8_E4M3)
+      return LMOE_ERR_INVALID_ARG;
+    if (dense || in_dim % 512 != 0 || d % 32 != 0) return LMOE_ERR_UNSUPPORTED;
+    if (T == 0) return LMOE_OK;
+    if (!a || !a_scale || !w1 || !w1_scale || !act || !act_scale) return LMOE_ERR_INVALID_ARG;
+    if ((long)T * in_dim >= 0xFFFFFFFFL || 2L * d * in_dim / 2 >= 0xFFFFFFFFL) return LMOE_ERR_UNSUPPORTED;
+    StreamGemm g{};
+    g.a = a;
+    g.a_bytes = (uint32_t)((long)T * in_dim);
+    g.a_scale = a_scale;
+    g.a_scale_bytes = (uint32_t)((long)T * in_dim / 32);
+    g.lda = in_dim;
+    g.Kd = in_dim;
+    g.M = rows_cap;
+    g.row_to_pair = row_to_pair;
+    g.tile_expert = tile_expert;
+    g.tile_m = tile_m;
+    g.topk = K;
+    g.a_by_row = 0;
+    g.beta = beta;
+    g.lbeta = linear_beta;
+    g.w_scale = w1_scale;
+    g.out_scale = act_scale;
+    g.nseg = 1;
+    g.seg[0] = Seg{w1, 2 * d, d, Epi::SITU_MX, Elt::F32, act, d, 0, 0};
+    return hip_status(launch_stream_gemm_mx(g, live_tiles((long)T * K, E), stream));
   }
   if (!dense_elt(a_dtype) || a_dtype != w_dtype || act_dtype != a_dtype) return LMOE_ERR_INVALID_ARG;
   if (in_dim % kchunk_of(a_dtype) != 0 || d % 16 != 0) return LMOE_ERR_UNSUPPORTED;
@@ -234,7 +268,36 @@ lmoe_status lmoe_fc2_combine(int T, int E, int K, int d, int out_dim, int tile_m
   const bool mx = act_dtype == LMOE_MXFP8_E4M3 || w_dtype == LMOE_MXFP4_E2M1;
   if (mx) {
     if (act_dtype != LMOE_MXFP8_E4M3 || w_dtype != LMOE_MXFP4_E2M1) return LMOE_ERR_INVALID_ARG;
-    return LMOE_ERR_UNSUPPORTED;
+    if (dense || d % 512 != 0 || out_dim % 64 != 0) return LMOE_ERR_UNSUPPORTED;
+    if (T == 0) return LMOE_OK;
+    if (!act || !act_scale || !w2 || !w2_scale || !out) return LMOE_ERR_INVALID_ARG;
+    if (K > 1 && (!workspace || workspace_bytes < lmoe_fc2_workspace_bytes(T, K, out_dim))) return LMOE_ERR_WORKSPACE;
+    if ((long)rows_cap * d >= 0xFFFFFFFFL || (long)out_dim * d / 2 >= 0xFFFFFFFFL) return LMOE_ERR_UNSUPPORTED;
+    StreamGemm g{};
+    g.a = act;
+    g.a_bytes = (uint32_t)((long)rows_cap * d);
+    g.a_scale = act_scale;
+    g.a_scale_bytes = (uint32_t)((long)rows_cap * d / 32);
+    g.lda = d;
+    g.Kd = d;
+    g.M = rows_cap;
+    g.row_to_pair = row_to_pair;
+    g.tile_expert = tile_expert;
+    g.tile_m = tile_m;
+    g.topk = K;
+    g.a_by_row = 1;
+    g.pair_w = topk_weights;
+    g.beta = 1.0f;
+    g.w_scale = w2_scale;
+    g.nseg = 1;
+    if (K == 1)
+      g.seg[0] = Seg{w2, out_dim, out_dim, Epi::TOKEN, elt_of(out_dtype), out, out_dim, 0, 0};
+    else
+      g.seg[0] = Seg{w2, out_dim, out_dim, Epi::PAIR, Elt::F32, workspace, out_dim, 0, 0};
+    hipError_t err = launch_stream_gemm_mx(g, live_tiles((long)T * K, E), stream);
+    if (err != hipSuccess) return LMOE_ERR_HIP;
+    if (K > 1) err = launch_combine(T, K, out_dim, (const float*)workspace, elt_of(out_dtype), out, stream);
+    return hip_status(err);
   }
   if (!dense_elt(act_dtype) || act_dtype != w_dtype) return LMOE_ERR_INVALID_ARG;
   if (d % kchunk_of(act_dtype) != 0 || out_dim % 16 != 0) return LMOE_ERR_UNSUPPORTED;

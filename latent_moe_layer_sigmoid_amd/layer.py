@@ -60,7 +60,10 @@ class LatentMoELayer:
         for k, v in weights.items():
             if k in ("W_r", "W_down", "W1", "W2", "W_s1", "W_s2", "W_up"):
                 self.w[k] = B.packed(v)
-            else:
+            elif k in ("W1_codes", "W2_codes"):
+                name = k[:2]
+                self.w[k], self.w[name + "_scales"] = B.packed_mxfp4(v, weights[name + "_scales"])
+            elif k not in ("W1_scales", "W2_scales"):
                 self.w[k] = v
         torch.cuda.synchronize(self.device)
 

@@ -316,20 +316,124 @@ def test_fc1_fc2_grouped_match_oracle(B, T, E, K, L, d, tile_m, dt):
     assert norm_err(act64[:len(r2p)][valid], ref_act[valid]) <= 1e-2
     assert np.all(act64[:len(r2p)][~valid] == sentinel)        # pad rows never written
     assert np.all(act64[len(r2p):] == sentinel)
-    # FC2 + combine on the GPU's own activations (isolates FC2)
+    # FC2 + combine on independently generated activation rows (pad rows left as garbage)
+    rng = np.random.default_rng(T + 3)
+    act_in = torch.from_numpy(rng.standard_normal((rc, d))).to(c["td"])
     z = torch.full((T, L), float("nan"), device=DEV)
     wsb = B.lmoe_fc2_workspace_bytes(T, K, L)
     ws = torch.empty(max(wsb // 4, 1), device=DEV)
-    B.lmoe_fc2_combine(T, E, K, d, L, tile_m, ldt, act, None, c["r2p"], c["te"], ldt, B.packed(c["W2"].to(DEV)), None,
-                       torch.from_numpy(c["w"]).to(DEV), B.LMOE_F32, z, rc, ws, wsb)
+    B.lmoe_fc2_combine(T, E, K, d, L, tile_m, ldt, act_in.to(DEV), None, c["r2p"], c["te"], ldt,
+                       B.packed(c["W2"].to(DEV)), None, torch.from_numpy(c["w"]).to(DEV), B.LMOE_F32, z, rc, ws, wsb)
     torch.cuda.synchronize()
+    a64 = f64(act_in)
     ref_z = np.zeros((T, L))
     p2r = c["perm"]["pair_to_row"]
     for t in range(T):
         for k in range(K):
             e = c["ids"][t, k]
-            y = oracle.linear(act64[p2r[t * K + k]][None, :], W2_64[e])[0]
+            y = oracle.linear(a64[p2r[t * K + k]][None, :], W2_64[e])[0]
             ref_z[t] += c["w"][t, k].astype(np.float64) * y
+    assert norm_err(f64(z), oracle.f32_round(ref_z)) <= 1e-4
+
+
+# ------------------------------------------------------------------ MX (MXFP8 x MXFP4) experts
+
+def _pack_mxfp4_reference(codes, scales):
+    """Packed MXFP4 layout from its definition (include/lmoe.h, lmoe_pack_mxfp4_weights)."""
+    N, half_k = codes.shape
+    Kd = half_k * 2
+    nst = Kd // 512
+    pc = np.empty(N * Kd // 2, dtype=np.uint8)
+    ps = np.empty(N * Kd // 32, dtype=np.uint8)
+    for n16 in range(N // 16):
+        for st in range(nst):
+            blk = n16 * nst + st
+            for q in range(4):
+                for g in range(4):
+                    for r in range(16):
+                        b0 = (st * 512 + q * 128 + g * 32) // 2
+                        dst = blk * 4096 + q * 1024 + g * 256 + r * 16
+                        pc[dst:dst + 16] = codes[n16 * 16 + r, b0:b0 + 16]
+                        ps[blk * 256 + (16 * g + r) * 4 + q] = scales[n16 * 16 + r, st * 16 + q * 4 + g]
+    return pc.reshape(N, half_k), ps.reshape(N, Kd // 32)
+
+
+def test_pack_mxfp4_layout(B):
+    rng = np.random.default_rng(3)
+    N, Kd = 32, 1024
+    codes = rng.integers(0, 256, (2, N, Kd // 2)).astype(np.uint8)
+    scales = rng.integers(0, 255, (2, N, Kd // 32)).astype(np.uint8)
+    pc, ps = B.packed_mxfp4(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV))
+    torch.cuda.synchronize()
+    for b in range(2):
+        rc, rs = _pack_mxfp4_reference(codes[b], scales[b])
+        assert np.array_equal(pc[b].cpu().numpy(), rc)
+        assert np.array_equal(ps[b].cpu().numpy(), rs)
+
+
+def _mx_weights(rng, E, N, Kd):
+    codes = rng.integers(0, 256, (E, N, Kd // 2)).astype(np.uint8)
+    scales = rng.integers(118, 123, (E, N, Kd // 32)).astype(np.uint8)
+    return codes, scales
+
+
+@pytest.mark.parametrize("T,E,K,L,d,tile_m", [(24, 8, 4, 1024, 512, 16), (40, 16, 8, 512, 512, 32)])
+def test_fc1_fc2_mx_match_oracle(B, T, E, K, L, d, tile_m):
+    rng = np.random.default_rng(T + E)
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    wts = (rng.random((T, K)) + 0.1).astype(np.float32)
+    perm = oracle.permute(ids, E, tile_m)
+    rc = B.lmoe_permute_rows_cap(T, E, K, tile_m)
+    r2p = torch.from_numpy(np.concatenate([perm["row_to_pair"], np.full(rc - len(perm["row_to_pair"]), -1)])
+                           .astype(np.int32)).to(DEV)
+    te = torch.from_numpy(tile_expert_from_offsets(perm["tile_offsets"], tile_m, rc // tile_m).astype(np.int32)).to(DEV)
+    # activations quantized by the oracle's codec (inputs never come from the GPU path)
+    xq, xs = oracle.mxfp8_quantize(oracle.bf16_round(rng.standard_normal((T, L))))
+    W1c, W1s = _mx_weights(rng, E, 2 * d, L)
+    W2c, W2s = _mx_weights(rng, E, L, d)
+    p1c, p1s = B.packed_mxfp4(torch.from_numpy(W1c).to(DEV), torch.from_numpy(W1s).to(DEV))
+    p2c, p2s = B.packed_mxfp4(torch.from_numpy(W2c).to(DEV), torch.from_numpy(W2s).to(DEV))
+    act = torch.full((rc, d), 0x55, dtype=torch.uint8, device=DEV)
+    act_s = torch.full((rc, d // 32), 0x55, dtype=torch.uint8, device=DEV)
+    B.lmoe_fc1_situ(T, E, K, L, d, tile_m, B.LMOE_MXFP8_E4M3, torch.from_numpy(xq).to(DEV),
+                    torch.from_numpy(xs).to(DEV), r2p, te, B.LMOE_MXFP4_E2M1, p1c, p1s, 1.0, 0.0,
+                    B.LMOE_MXFP8_E4M3, act, act_s, rc)
+    torch.cuda.synchronize()
+    x_hat = oracle.mxfp8_dequant(xq, xs)
+    flat = ids.reshape(-1)
+    r2p_np = perm["row_to_pair"]
+    rows = np.nonzero(r2p_np >= 0)[0]
+    got_c, got_s = act.cpu().numpy(), act_s.cpu().numpy()
+    ref_c = np.zeros((len(rows), d), np.uint8)
+    ref_s = np.zeros((len(rows), d // 32), np.uint8)
+    for i, r in enumerate(rows):
+        p = r2p_np[r]
+        h = oracle.linear(x_hat[p // K][None, :], oracle.mxfp4_dequant(W1c[flat[p]], W1s[flat[p]]))
+        a32 = oracle.f32_round(oracle.situ_glu_rows(h, 1.0, 0.0))
+        ref_c[i], ref_s[i] = [v[0] for v in oracle.mxfp8_quantize(a32)]
+    assert np.mean(got_c[rows] == ref_c) >= 0.99 and np.mean(got_s[rows] == ref_s) >= 0.99
+    deq_g = oracle.mxfp8_dequant(got_c[rows], got_s[rows])
+    deq_r = oracle.mxfp8_dequant(ref_c, ref_s)
+    assert norm_err(deq_g, deq_r) <= 0.07                       # at most about one e4m3 step
+    pad = np.nonzero(r2p_np < 0)[0]
+    assert np.all(got_c[pad] == 0x55) and np.all(got_s[pad] == 0x55)   # pad rows never written
+    # FC2 + combine on independently quantized activation rows
+    aq, as_ = oracle.mxfp8_quantize(oracle.bf16_round(rng.standard_normal((rc, d))))
+    z = torch.full((T, L), float("nan"), device=DEV)
+    wsb = B.lmoe_fc2_workspace_bytes(T, K, L)
+    ws = torch.empty(max(wsb // 4, 1), device=DEV)
+    B.lmoe_fc2_combine(T, E, K, d, L, tile_m, B.LMOE_MXFP8_E4M3, torch.from_numpy(aq).to(DEV),
+                       torch.from_numpy(as_).to(DEV), r2p, te, B.LMOE_MXFP4_E2M1, p2c, p2s,
+                       torch.from_numpy(wts).to(DEV), B.LMOE_F32, z, rc, ws, wsb)
+    torch.cuda.synchronize()
+    a_hat = oracle.mxfp8_dequant(aq, as_)
+    p2r = perm["pair_to_row"]
+    ref_z = np.zeros((T, L))
+    for t in range(T):
+        for k in range(K):
+            e = ids[t, k]
+            y = oracle.linear(a_hat[p2r[t * K + k]][None, :], oracle.mxfp4_dequant(W2c[e], W2s[e]))[0]
+            ref_z[t] += wts[t, k].astype(np.float64) * y
     assert norm_err(f64(z), oracle.f32_round(ref_z)) <= 1e-4
 
 

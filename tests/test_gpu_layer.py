@@ -61,10 +61,12 @@ def check_layer(cfg, seed, tokens=None, out_tol=1e-2, fused=True):
     if cfg.experts != "mx":
         act = f64(b["act"])[p2r]                     # [len(sel), K, d]
         assert norm_err(act, ref["act"]) <= 1e-2
-    assert norm_err(f64(b["z"])[sel], ref["z"]) <= 1e-2
+    # MX requantization amplifies one-ulp differences of the latent upstream: the MX bar
+    # (3e-2) applies to the tensors downstream of the expert GEMMs as well
+    assert norm_err(f64(b["z"])[sel], ref["z"]) <= out_tol
     if not fused:
         assert norm_err(f64(b["sh"])[sel], ref["sh"]) <= 1e-2
-    assert norm_err(f64(b["n"])[sel], ref["n"]) <= 1e-2
+    assert norm_err(f64(b["n"])[sel], ref["n"]) <= out_tol
     err = norm_err(f64(out)[sel], ref["out"])
     print(f"[layer parity] {cfg.name}: out err {err:.3e}", flush=True)
     assert err <= out_tol
@@ -93,6 +95,15 @@ def test_layer_prefill_reduced_dims_ragged_tiles():
     # prefill structure (tile 128, skewed load) at dimensions the oracle finishes in seconds
     cfg = LI.scaled(LI.PREFILL, name="prefill_reduced", T=300, H=1024, L=512, E=64, K=8, d=128, I=256)
     check_layer(cfg, 4)
+
+
+def test_layer_mx_reduced_dims():
+    cfg = LI.scaled(LI.MX, name="mx_reduced", T=64, H=1024, L=1024, E=32, K=4, d=512, I=256)
+    check_layer(cfg, 5, out_tol=3e-2)
+
+
+def test_layer_mx_full_size_sampled_tokens():
+    check_layer(LI.MX, 5, tokens=[0, 1, 511, 1023], out_tol=3e-2)
 
 
 def test_layer_prefill_full_size_sampled_tokens():
