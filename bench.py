@@ -96,6 +96,18 @@ def cpu_baseline(torch, LI, cfg, seed, X_cpu, n_tokens):
     return reps * n_tokens / dt, dt, reps
 
 
+def blas_threads():
+    """Threads numpy's BLAS runs the oracle's matrix products on (the host threads it uses)."""
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"]
+        if n:
+            return max(n)
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,7 +209,7 @@ def main():
         n = min(args.cpu_tokens, cfg.T)
         log(f"cpu baseline: oracle on {n} tokens")
         v, dt, reps = cpu_baseline(torch, LI, cfg, args.seed, X_cpu, n)
-        res["cpu_baseline"] = {"value": round(v, 4), "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
+        res["cpu_baseline"] = {"value": round(v, 4), "unit": "tokens/s", "cores": blas_threads(),
                                "kind": "oracle",
                                "sample": f"{n} of the {cfg.T} tokens of one step ({n * cfg.K} expert pairs), "
                                          f"repeated {reps}x, numpy float64, {dt:.1f} s"}

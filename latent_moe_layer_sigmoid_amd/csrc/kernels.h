@@ -66,6 +66,8 @@ struct StreamGemm {
 
 // live_tiles: expected number of 16-row tiles that hold rows (sizes the split-K factor).
 hipError_t launch_stream_gemm(StreamGemm g, Elt elt, int live_tiles, hipStream_t stream);
+// LDS-tiled bf16 GEMM: 128-row tiles (dense rows, or grouped tiles with tile_m == 128); Kd % 128 == 0.
+hipError_t launch_tiled_gemm(StreamGemm g, hipStream_t stream);
 // MXFP8 x packed MXFP4 (grouped mode, one segment: SITU_MX or PAIR / TOKEN); Kd % 512 == 0.
 hipError_t launch_stream_gemm_mx(StreamGemm g, int live_tiles, hipStream_t stream);
 

@@ -24,6 +24,13 @@ long rows_bound(long pairs, int E, int tile_m) {
   const long cap = pairs + nonempty * (tile_m - 1);
   return (cap + tile_m - 1) / tile_m * tile_m;
 }
+// Token-heavy bf16 calls go to the LDS-tiled kernel (128-row tiles); the rest stream the
+// weights over 16-row tiles.
+bool use_tiled_dense(long M, lmoe_dtype t) { return t == LMOE_BF16 && M >= 256; }
+bool use_tiled_grouped(int tile_m, lmoe_dtype t) { return t == LMOE_BF16 && tile_m == 128; }
+hipError_t run_gemm(const StreamGemm& g, lmoe_dtype t, bool tiled, int live, hipStream_t stream) {
+  return tiled ? launch_tiled_gemm(g, stream) : launch_stream_gemm(g, elt_of(t), live, stream);
+}
 // expected 16-row tiles holding rows: pairs / 16 plus one partial tile per touched expert
 int live_tiles(long pairs, int E) {
   const long nonempty = pairs < E ? pairs : E;
@@ -85,7 +92,7 @@ lmoe_status lmoe_linear(int M, int N, int Kd, lmoe_dtype x_dtype, const void* x,
   g.beta = 1.0f;
   g.nseg = 1;
   g.seg[0] = Seg{w, N, N, Epi::STORE, elt_of(y_dtype), y, N, 0, 0};
-  return hip_status(launch_stream_gemm(g, elt_of(x_dtype), (M + 15) / 16, stream));
+  return hip_status(run_gemm(g, x_dtype, use_tiled_dense(M, x_dtype), (M + 15) / 16, stream));
 }
 
 lmoe_status lmoe_linear_multi(int M, int Kd, lmoe_dtype x_dtype, const void* x, int n_proj, const int* N,
@@ -122,7 +129,7 @@ lmoe_status lmoe_linear_multi(int M, int Kd, lmoe_dtype x_dtype, const void* x, 
     g.seg[i] = Seg{w[i], si ? 2 * N[i] : N[i], N[i], si ? Epi::SITU : Epi::STORE, elt_of(y_dtype[i]), y[i], N[i], 0,
                    0};
   }
-  return hip_status(launch_stream_gemm(g, elt_of(x_dtype), (M + 15) / 16, stream));
+  return hip_status(run_gemm(g, x_dtype, use_tiled_dense(M, x_dtype), (M + 15) / 16, stream));
 }
 
 lmoe_status lmoe_route(int T, int E, int K, const float* logits, const float* bias, float rsf, int renormalize,
@@ -248,7 +255,8 @@ lmoe_status lmoe_fc1_situ(int T, int E, int K, int in_dim, int d, int tile_m, lm
   g.nseg = 1;
   g.seg[0] = Seg{w1, 2 * d, d, Epi::SITU, elt_of(act_dtype), act, d, 0, 0};
   const int live = dense ? (T + 15) / 16 : live_tiles((long)T * K, E);
-  return hip_status(launch_stream_gemm(g, elt_of(a_dtype), live, stream));
+  const bool tiled = dense ? use_tiled_dense(T, a_dtype) : use_tiled_grouped(tile_m, a_dtype);
+  return hip_status(run_gemm(g, a_dtype, tiled, live, stream));
 }
 
 size_t lmoe_fc2_workspace_bytes(int T, int K, int out_dim) {
@@ -325,7 +333,8 @@ lmoe_status lmoe_fc2_combine(int T, int E, int K, int d, int out_dim, int tile_m
   else
     g.seg[0] = Seg{w2, out_dim, out_dim, Epi::PAIR, Elt::F32, workspace, out_dim, 0, 0};
   const int live = dense ? (T + 15) / 16 : live_tiles((long)T * K, E);
-  hipError_t err = launch_stream_gemm(g, elt_of(act_dtype), live, stream);
+  const bool tiled = dense ? use_tiled_dense(T, act_dtype) : use_tiled_grouped(tile_m, act_dtype);
+  hipError_t err = run_gemm(g, act_dtype, tiled, live, stream);
   if (err != hipSuccess) return LMOE_ERR_HIP;
   if (K > 1) err = launch_combine(T, K, out_dim, (const float*)workspace, elt_of(out_dtype), out, stream);
   return hip_status(err);
@@ -352,7 +361,7 @@ lmoe_status lmoe_tail(int T, int L, int H, const float* latent, const void* gamm
   g.beta = 1.0f;
   g.nseg = 1;
   g.seg[0] = Seg{w_up, H, H, Epi::ADD, elt_of(io_dtype), out, H, 0, 0};
-  return hip_status(launch_stream_gemm(g, elt_of(io_dtype), (T + 15) / 16, stream));
+  return hip_status(run_gemm(g, io_dtype, use_tiled_dense(T, io_dtype), (T + 15) / 16, stream));
 }
 
 lmoe_status lmoe_tail_shared(int T, int L, int H, int I, const float* latent, const void* gamma, float eps,
@@ -368,6 +377,28 @@ lmoe_status lmoe_tail_shared(int T, int L, int H, int I, const float* latent, co
     return LMOE_ERR_UNSUPPORTED;
   hipError_t err = launch_rmsnorm(T, L, latent, gamma, eps, elt_of(io_dtype), norm_out, stream);
   if (err != hipSuccess) return LMOE_ERR_HIP;
+  if (use_tiled_dense(T, io_dtype)) {
+    // token-heavy: out = shared-expert FC2 (stored, rounded), then out += up projection in place
+    StreamGemm g{};
+    g.a = shared_act;
+    g.a_bytes = (uint32_t)((long)T * I * esize_of(io_dtype));
+    g.lda = I;
+    g.Kd = I;
+    g.M = T;
+    g.topk = 1;
+    g.beta = 1.0f;
+    g.nseg = 1;
+    g.seg[0] = Seg{w_s2, H, H, Epi::STORE, elt_of(io_dtype), out, H, 0, 0};
+    err = launch_tiled_gemm(g, stream);
+    if (err != hipSuccess) return LMOE_ERR_HIP;
+    g.a = norm_out;
+    g.a_bytes = (uint32_t)((long)T * L * esize_of(io_dtype));
+    g.lda = L;
+    g.Kd = L;
+    g.add = out;
+    g.seg[0] = Seg{w_up, H, H, Epi::ADD, elt_of(io_dtype), out, H, 0, 0};
+    return hip_status(launch_tiled_gemm(g, stream));
+  }
   StreamGemm g{};
   g.a = shared_act;                  // phase 0: shared-expert FC2, rounded like a stored tensor
   g.a_bytes = (uint32_t)((long)T * I * esize_of(io_dtype));

@@ -258,7 +258,8 @@ def test_pack_weights_layout(B, N, Kd, dt):
 @pytest.mark.parametrize("M,N,Kd,dt,yt", [(1, 16, 128, "bf16", "f32"), (8, 896, 7168, "bf16", "f32"),
                                           (8, 2048, 7168, "bf16", "bf16"), (17, 48, 256, "bf16", "bf16"),
                                           (4, 16, 256, "f32", "f32"), (33, 128, 192, "f32", "f32"),
-                                          (200, 64, 384, "bf16", "f32")])
+                                          (200, 64, 384, "bf16", "f32"), (300, 400, 640, "bf16", "bf16"),
+                                          (256, 128, 128, "bf16", "f32")])
 def test_linear_matches_oracle(B, M, N, Kd, dt, yt):
     rng = np.random.default_rng(M + N + Kd)
     td = torch.bfloat16 if dt == "bf16" else torch.float32
@@ -293,7 +294,8 @@ def _expert_case(B, T, E, K, L, d, tile_m, dt, seed):
 
 @pytest.mark.parametrize("T,E,K,L,d,tile_m,dt", [(4, 16, 4, 128, 64, 16, "f32"), (8, 64, 16, 2048, 512, 16, "bf16"),
                                                  (50, 32, 4, 256, 128, 32, "bf16"),
-                                                 (300, 16, 2, 256, 128, 128, "bf16")])
+                                                 (300, 16, 2, 256, 128, 128, "bf16"),
+                                                 (600, 64, 8, 1024, 256, 128, "bf16")])
 def test_fc1_fc2_grouped_match_oracle(B, T, E, K, L, d, tile_m, dt):
     c = _expert_case(B, T, E, K, L, d, tile_m, dt, seed=T + E)
     ldt = B.LMOE_BF16 if dt == "bf16" else B.LMOE_F32
@@ -457,7 +459,7 @@ def test_dense_mode_shared_expert(B, dt):
     assert norm_err(f64(sh), ref) <= 1e-2
 
 
-@pytest.mark.parametrize("M,Kd,dt", [(8, 7168, "bf16"), (3, 256, "f32"), (37, 384, "bf16")])
+@pytest.mark.parametrize("M,Kd,dt", [(8, 7168, "bf16"), (3, 256, "f32"), (37, 384, "bf16"), (260, 512, "bf16")])
 def test_linear_multi_matches_oracle(B, M, Kd, dt):
     rng = np.random.default_rng(M + Kd)
     td = torch.bfloat16 if dt == "bf16" else torch.float32
@@ -479,7 +481,7 @@ def test_linear_multi_matches_oracle(B, M, Kd, dt):
 
 
 @pytest.mark.parametrize("T,L,H,I,dt", [(8, 2048, 7168, 4096, "bf16"), (4, 128, 256, 128, "f32"),
-                                        (21, 256, 512, 384, "bf16")])
+                                        (21, 256, 512, 384, "bf16"), (300, 256, 400, 384, "bf16")])
 def test_tail_shared_matches_oracle(B, T, L, H, I, dt):
     rng = np.random.default_rng(T + L + I)
     td = torch.bfloat16 if dt == "bf16" else torch.float32
@@ -503,7 +505,7 @@ def test_tail_shared_matches_oracle(B, T, L, H, I, dt):
 # ------------------------------------------------------------------------------- tail
 
 @pytest.mark.parametrize("T,L,H,dt,alias", [(8, 2048, 7168, "bf16", False), (4, 128, 256, "f32", True),
-                                            (33, 256, 512, "bf16", True)])
+                                            (33, 256, 512, "bf16", True), (260, 384, 272, "bf16", True)])
 def test_tail_matches_oracle(B, T, L, H, dt, alias):
     rng = np.random.default_rng(T + L)
     td = torch.bfloat16 if dt == "bf16" else torch.float32
