@@ -117,6 +117,8 @@ def main():
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=8)
+    ap.add_argument("--schedule", choices=["one_stream", "shared_stream"], default="shared_stream",
+                    help="shared_stream: the shared expert runs on a second stream")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no multi-GPU path)",
@@ -136,7 +138,7 @@ def main():
     w = LI.make_layer_weights(cfg, args.seed, device="cuda")
     shape = LayerShape(H=cfg.H, L=cfg.L, E=cfg.E, K=cfg.K, d=cfg.d, I=cfg.I, dtype=cfg.dtype, experts=cfg.experts,
                        beta=cfg.beta, linear_beta=cfg.linear_beta, rsf=cfg.rsf, eps=cfg.eps, tile_m=cfg.tile_m)
-    layer = LatentMoELayer(shape, w)
+    layer = LatentMoELayer(shape, w, shared_stream=args.schedule == "shared_stream")
     X_cpu = LI.make_x(cfg, args.seed)
     X = X_cpu.to("cuda")
     stream = torch.cuda.current_stream()
@@ -194,7 +196,7 @@ def main():
         "data": "synthetic (seeded counter-based generator; random-init weights)",
         "config": {"workload": f"{cfg.name}: T={cfg.T} H={cfg.H} L={cfg.L} E={cfg.E} top-{cfg.K} d={cfg.d} "
                                f"shared I={cfg.I} experts={cfg.experts} tile_m={cfg.tile_m}",
-                   "tokens_per_step": cfg.T, "seed": args.seed},
+                   "tokens_per_step": cfg.T, "seed": args.seed, "schedule": args.schedule},
         "roofline": {"kernel": "grouped FC1 + SituGLU (stream_gemm_kernel, SituGLU epilogue)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,

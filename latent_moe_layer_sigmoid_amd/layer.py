@@ -46,14 +46,20 @@ class LatentMoELayer:
     W_s1 [2I,H], W_s2 [H,I], gamma [L], W_up [H,L]; the projections are packed on the
     device (lmoe_pack_weights) when the layer is built."""
 
-    def __init__(self, shape: LayerShape, weights: dict, device="cuda", fused=True):
+    def __init__(self, shape: LayerShape, weights: dict, device="cuda", fused=True, shared_stream=False):
         B.lib()   # fail loudly now if the library is missing
         self.s = shape
         # fused: the hidden-input projections share one launch (lmoe_linear_multi) and the
         # shared expert's FC2 is folded into the up projection (lmoe_tail_shared);
         # otherwise every step is its own call.
         self.fused = fused
+        # shared_stream: the shared expert runs on a second stream, concurrently with the
+        # router GEMM, routing, permutation and the routed experts, and the tail waits for
+        # it (TensorRT-LLM PR 20541, "Commit 2": shared experts on their own stream, joined
+        # by an event before the routed reduction). Same kernels, same results.
+        self.shared_stream = shared_stream
         self.device = torch.device(device)
+        self._side = torch.cuda.Stream(self.device) if shared_stream else None   # default priority
         self._bufs = {}
         # weights go to HBM in the packed MFMA-operand layout once, at construction
         self.w = {}
@@ -119,8 +125,9 @@ class LatentMoELayer:
         T = X.shape[0]
         b = self.buffers(T)
         dt = _lmoe_dtype(s.dtype)
-        rc = b["rows_cap"]
         mark = timer.mark if timer is not None else (lambda name: None)
+        if self.shared_stream:
+            return self._forward_two_streams(X, b, stream, mark)
         if self.fused:
             # a1 router GEMM, a3 latent down projection, a10 shared FC1 + SituGLU: one launch
             mark("front")
@@ -128,43 +135,13 @@ class LatentMoELayer:
                                 [B.LMOE_F32, dt, dt], [b["logits"], b["x"], b["act_s"]], [0, 0, 1], s.beta,
                                 s.linear_beta, stream)
         else:
-            # a1 router GEMM -> fp32 logits
+            # a1 router GEMM -> fp32 logits, a3 latent down projection
             mark("router")
             B.lmoe_linear(T, s.E, s.H, dt, X, dt, w["W_r"], B.LMOE_F32, b["logits"], stream)
-        # a2 routing
-        mark("route")
-        B.lmoe_route(T, s.E, s.K, b["logits"], w["bias"], s.rsf, 1, b["ids"], b["weights"], stream)
-        # a5 expert-sorted permutation
-        mark("permute")
-        B.lmoe_permute(T, s.E, s.K, s.tile_m, b["ids"], b["counts"], b["offsets"], b["tile_offsets"],
-                       b["row_to_pair"], b["tile_expert"], b["pair_to_row"], rc, b["perm_ws"],
-                       b["perm_ws_bytes"], stream)
-        if not self.fused:
-            # a3 latent down projection
             mark("down")
             B.lmoe_linear(T, s.L, s.H, dt, X, dt, w["W_down"], dt, b["x"], stream)
-        if s.experts == "mx":
-            # a4 input quantization, a6-a8 FC1 + SituGLU + requant, a9 FC2 + combine
-            mark("quant")
-            B.lmoe_quant_mxfp8(T, s.L, dt, b["x"], b["xq"], b["xs"], stream)
-            mark("fc1")
-            B.lmoe_fc1_situ(T, s.E, s.K, s.L, s.d, s.tile_m, B.LMOE_MXFP8_E4M3, b["xq"], b["xs"], b["row_to_pair"],
-                            b["tile_expert"], B.LMOE_MXFP4_E2M1, w["W1_codes"], w["W1_scales"], s.beta,
-                            s.linear_beta, B.LMOE_MXFP8_E4M3, b["act"], b["act_scale"], rc, stream)
-            mark("fc2")
-            B.lmoe_fc2_combine(T, s.E, s.K, s.d, s.L, s.tile_m, B.LMOE_MXFP8_E4M3, b["act"], b["act_scale"],
-                               b["row_to_pair"], b["tile_expert"], B.LMOE_MXFP4_E2M1, w["W2_codes"],
-                               w["W2_scales"], b["weights"], B.LMOE_F32, b["z"], rc, b["fc2_ws"],
-                               b["fc2_ws_bytes"], stream)
-        else:
-            # a6 + a7 FC1 with the SituGLU epilogue, a9 FC2 + weighted combine
-            mark("fc1")
-            B.lmoe_fc1_situ(T, s.E, s.K, s.L, s.d, s.tile_m, dt, b["x"], None, b["row_to_pair"], b["tile_expert"],
-                            dt, w["W1"], None, s.beta, s.linear_beta, dt, b["act"], None, rc, stream)
-            mark("fc2")
-            B.lmoe_fc2_combine(T, s.E, s.K, s.d, s.L, s.tile_m, dt, b["act"], None, b["row_to_pair"],
-                               b["tile_expert"], dt, w["W2"], None, b["weights"], B.LMOE_F32, b["z"], rc,
-                               b["fc2_ws"], b["fc2_ws_bytes"], stream)
+        # a2 routing, a5 permutation, (a4) a6-a9 routed experts
+        self._routed(X, b, stream, mark)
         if self.fused:
             # a10 shared FC2 folded into a11 + a12: RMSNorm, then one GEMM over both K ranges
             mark("tail")
@@ -181,6 +158,69 @@ class LatentMoELayer:
             # a11 + a12 latent RMSNorm, up projection with the shared add in its epilogue
             mark("tail")
             B.lmoe_tail(T, s.L, s.H, b["z"], w["gamma"], s.eps, w["W_up"], b["sh"], dt, b["out"], b["n"], stream)
+        mark(None)
+        return b["out"]
+
+    def _routed(self, X, b, stream, mark):
+        """Routing, permutation and the routed experts (a2, a4-a9) on `stream`."""
+        s, w = self.s, self.w
+        T = X.shape[0]
+        dt = _lmoe_dtype(s.dtype)
+        rc = b["rows_cap"]
+        mark("route")
+        B.lmoe_route(T, s.E, s.K, b["logits"], w["bias"], s.rsf, 1, b["ids"], b["weights"], stream)
+        mark("permute")
+        B.lmoe_permute(T, s.E, s.K, s.tile_m, b["ids"], b["counts"], b["offsets"], b["tile_offsets"],
+                       b["row_to_pair"], b["tile_expert"], b["pair_to_row"], rc, b["perm_ws"],
+                       b["perm_ws_bytes"], stream)
+        if s.experts == "mx":
+            mark("quant")
+            B.lmoe_quant_mxfp8(T, s.L, dt, b["x"], b["xq"], b["xs"], stream)
+            mark("fc1")
+            B.lmoe_fc1_situ(T, s.E, s.K, s.L, s.d, s.tile_m, B.LMOE_MXFP8_E4M3, b["xq"], b["xs"], b["row_to_pair"],
+                            b["tile_expert"], B.LMOE_MXFP4_E2M1, w["W1_codes"], w["W1_scales"], s.beta,
+                            s.linear_beta, B.LMOE_MXFP8_E4M3, b["act"], b["act_scale"], rc, stream)
+            mark("fc2")
+            B.lmoe_fc2_combine(T, s.E, s.K, s.d, s.L, s.tile_m, B.LMOE_MXFP8_E4M3, b["act"], b["act_scale"],
+                               b["row_to_pair"], b["tile_expert"], B.LMOE_MXFP4_E2M1, w["W2_codes"],
+                               w["W2_scales"], b["weights"], B.LMOE_F32, b["z"], rc, b["fc2_ws"],
+                               b["fc2_ws_bytes"], stream)
+        else:
+            mark("fc1")
+            B.lmoe_fc1_situ(T, s.E, s.K, s.L, s.d, s.tile_m, dt, b["x"], None, b["row_to_pair"], b["tile_expert"],
+                            dt, w["W1"], None, s.beta, s.linear_beta, dt, b["act"], None, rc, stream)
+            mark("fc2")
+            B.lmoe_fc2_combine(T, s.E, s.K, s.d, s.L, s.tile_m, dt, b["act"], None, b["row_to_pair"],
+                               b["tile_expert"], dt, w["W2"], None, b["weights"], B.LMOE_F32, b["z"], rc,
+                               b["fc2_ws"], b["fc2_ws_bytes"], stream)
+
+    def _forward_two_streams(self, X, b, stream, mark):
+        """Main stream: router GEMM + down projection (one launch), routing, permutation,
+        experts, then RMSNorm + up projection with the shared add. Side stream: the shared
+        expert (FC1 + SituGLU, FC2), started once the main stream reaches this call and
+        joined by an event before the tail."""
+        s, w = self.s, self.w
+        T = X.shape[0]
+        dt = _lmoe_dtype(s.dtype)
+        main = torch.cuda.current_stream(self.device) if stream is None else stream
+        side = self._side
+        start = torch.cuda.Event()
+        start.record(main)
+        side.wait_event(start)            # X is ready and the previous call's tail has read sh
+        X.record_stream(side)
+        B.lmoe_fc1_situ(T, 1, 1, s.H, s.I, 16, dt, X, None, None, None, dt, w["W_s1"], None, s.beta,
+                        s.linear_beta, dt, b["act_s"], None, T, side)
+        B.lmoe_fc2_combine(T, 1, 1, s.I, s.H, 16, dt, b["act_s"], None, None, None, dt, w["W_s2"], None, None,
+                           dt, b["sh"], T, None, 0, side)
+        shared_done = torch.cuda.Event()
+        shared_done.record(side)
+        mark("front")
+        B.lmoe_linear_multi(T, s.H, dt, X, 2, [s.E, s.L], [w["W_r"], w["W_down"]], [B.LMOE_F32, dt],
+                            [b["logits"], b["x"]], None, s.beta, s.linear_beta, main)
+        self._routed(X, b, main, mark)
+        main.wait_event(shared_done)
+        mark("tail")
+        B.lmoe_tail(T, s.L, s.H, b["z"], w["gamma"], s.eps, w["W_up"], b["sh"], dt, b["out"], b["n"], main)
         mark(None)
         return b["out"]
 

@@ -15,19 +15,19 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def build_layer(cfg, seed, fused=True):
+def build_layer(cfg, seed, fused=True, shared_stream=False):
     from latent_moe_layer_sigmoid_amd import LatentMoELayer, LayerShape
     w_dev = LI.make_layer_weights(cfg, seed, device=DEV)
     shape = LayerShape(H=cfg.H, L=cfg.L, E=cfg.E, K=cfg.K, d=cfg.d, I=cfg.I, dtype=cfg.dtype, experts=cfg.experts,
                        beta=cfg.beta, linear_beta=cfg.linear_beta, rsf=cfg.rsf, eps=cfg.eps, tile_m=cfg.tile_m)
-    return LatentMoELayer(shape, w_dev, fused=fused), w_dev
+    return LatentMoELayer(shape, w_dev, fused=fused, shared_stream=shared_stream), w_dev
 
 
-def check_layer(cfg, seed, tokens=None, out_tol=1e-2, fused=True):
+def check_layer(cfg, seed, tokens=None, out_tol=1e-2, fused=True, shared_stream=False):
     """Run the layer on the GPU for all T tokens; compare routing / permutation for all
     tokens and the float outputs for `tokens` (all when None) against the oracle."""
-    print(f"[layer parity] {cfg.name} T={cfg.T} seed={seed} fused={fused}", flush=True)
-    layer, w_dev = build_layer(cfg, seed, fused)
+    print(f"[layer parity] {cfg.name} T={cfg.T} seed={seed} fused={fused} shared_stream={shared_stream}", flush=True)
+    layer, w_dev = build_layer(cfg, seed, fused, shared_stream)
     w_cpu = LI.make_layer_weights(cfg, seed, device="cpu", experts=False)
     o = oracle_weights(cfg, seed, w_cpu)
     X, _ = guarded_x(cfg, seed, o["W_r"], o["bias"])
@@ -64,7 +64,7 @@ def check_layer(cfg, seed, tokens=None, out_tol=1e-2, fused=True):
     # MX requantization amplifies one-ulp differences of the latent upstream: the MX bar
     # (3e-2) applies to the tensors downstream of the expert GEMMs as well
     assert norm_err(f64(b["z"])[sel], ref["z"]) <= out_tol
-    if not fused:
+    if not fused or shared_stream:
         assert norm_err(f64(b["sh"])[sel], ref["sh"]) <= 1e-2
     assert norm_err(f64(b["n"])[sel], ref["n"]) <= out_tol
     err = norm_err(f64(out)[sel], ref["out"])
@@ -89,6 +89,17 @@ def test_layer_decode_bf16_full_size():
 
 def test_layer_decode_second_seed_unfused_path():
     check_layer(LI.DECODE, 102, fused=False)
+
+
+def test_layer_tiny_and_decode_shared_expert_stream():
+    check_layer(LI.TINY, 3, shared_stream=True)
+    layer, X = check_layer(LI.DECODE, 2, shared_stream=True)
+    # repeated calls: the side stream never overtakes the main stream's tail
+    first = layer.buffers(LI.DECODE.T)["out"].clone()
+    for _ in range(3):
+        layer.forward(X.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), layer.buffers(LI.DECODE.T)["out"].view(torch.int16))
 
 
 def test_layer_prefill_reduced_dims_ragged_tiles():
