@@ -2,33 +2,45 @@
 // the prefill-sized projections of the hidden input, the tail, and the grouped expert
 // FC1 / FC2 over tiles of 128 expert rows.
 //
-// Workgroup tile 128 rows x 128 weight rows (a SituGLU block takes 64 gate rows and the
-// matching 64 up rows), K stage of 128, 256 threads = 4 wavefronts in a 2 x 2 grid, each
-// owning 64 x 64 outputs as 4 x 4 v_mfma_f32_16x16x32_bf16 tiles. Both operands reach LDS
-// by direct buffer-to-LDS loads (buffer_load_dwordx4 ... lds), arranged in the packed MFMA
-// order the weights already have in HBM: for each 16-row group and 32-wide K slice q, a
-// 1 KB block holding lane l = 16g + r's 16 bytes (row r, K 8g .. 8g + 7) at 16 l. Every
-// MFMA operand is then one conflict-free 1 KB ds_read_b128, and the weights are copied
-// block by block. Two LDS stages (2 x 64 KB): stage c + 1 is requested before stage c is
-// computed. Workgroups are remapped so that consecutive tiles share an XCD (and its L2).
-// Epilogues as in the weight-streaming kernel: plain store, SituGLU (vLLM PR 50088,
-// commit 2), weighted per-pair store for the combine (TensorRT-LLM PR 20541, "Commit 1":
-// finalize), and the in-place add of the up projection (vLLM latent_moe_runner page,
-// _shard_up_proj_tail).
+// Workgroup tile: 128 rows x 512 weight rows, 256 threads = 4 wavefronts side by side,
+// each owning all 128 rows x its own 128 weight rows as 8 x 8 v_mfma_f32_16x16x32_bf16
+// tiles (256 fp32 accumulators per lane; one wavefront per SIMD). A SituGLU wavefront
+// takes 64 gate rows and the matching 64 up rows. Per 32-wide K step the workgroup needs
+// 8 KB of activations and 32 KB of weights for 1024 MFMA cycles per SIMD (about 40 bytes
+// per clock per CU), and each wavefront reads 16 KB of operands from LDS.
+//
+// Operands reach LDS by direct buffer-to-LDS loads (buffer_load_dwordx4 ... lds) in the
+// packed MFMA order the weights already have in HBM: for each 16-row group and 32-wide K
+// step, a 1 KB block holding lane l = 16g + r's 16 bytes (row r, K 8g .. 8g + 7) at 16 l.
+// Every MFMA operand is then one conflict-free ds_read_b128, and the weights are copied
+// block for block. LDS is a ring of NSLOT 40 KB K steps, NSLOT - 1 of them in flight
+// while one is computed; the operands of step c + 1 are read from LDS into registers
+// while the MFMAs of step c run. Workgroups are ordered so that the 32 running on one XCD
+// cover 8 row tiles x 4 weight blocks, which share operands in that XCD's L2.
+//
+// Epilogues: plain store, SituGLU (vLLM PR 50088, commit 2), weighted per-pair store for
+// the combine (TensorRT-LLM PR 20541, "Commit 1": finalize), and the in-place add of the
+// up projection (vLLM latent_moe_runner page, _shard_up_proj_tail).
 #include "common.h"
 #include "kernels.h"
+
+#include <utility>
 
 namespace lmoe {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int TILE_M = 128;
-constexpr int STAGE = 65536;      // bytes per LDS stage: A 32 KB + B 32 KB
-constexpr int B_OFF = 32768;
+constexpr int TILE_N = 512;           // weight rows per workgroup (SituGLU: 256 gate + 256 up)
+constexpr int NSLOT = 4;              // LDS ring of K steps
+constexpr int SLOT = 40960;           // bytes per K step: A 8 x 1 KB + B 32 x 1 KB
+constexpr int B_OFF = 8192;
+constexpr int LOADS_PER_STEP = 10;    // per wavefront: 2 A blocks + 8 B blocks
+constexpr int GROUP_M = 8;            // row tiles per swizzle group
 
-// s_waitcnt immediates (gfx9 encoding): wait until at most n vector-memory operations of
-// this wave are outstanding; expcnt and lgkmcnt unconstrained.
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// s_waitcnt immediates (gfx9 encoding): vm = vector-memory count (6 bits), lgkm = LDS
+// count (4 bits); expcnt unconstrained.
+constexpr int waitcnt(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8); }
 
 LMOE_DEV void to_lds(rsrc_t r, char* lds, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
@@ -41,21 +53,72 @@ LMOE_DEV void store_out(Elt elt, void* base, size_t idx, float v) {
     reinterpret_cast<uint16_t*>(base)[idx] = f32_to_bf16(v);
 }
 
-__global__ __launch_bounds__(256) void tiled_gemm_kernel(const StreamGemm g, int blocks_total, int nch) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
-  constexpr int NACC = 16;
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1, so that register
+// arrays indexed by I stay in registers.
+template <typename F, int... I>
+LMOE_DEV void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+LMOE_DEV void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// A wave-uniform copy of a pointer / value (kept in scalar registers, so that buffer
+// descriptors built from it need no per-lane waterfall).
+LMOE_DEV const char* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
+// 16-byte LDS read at byte address addr + OFF. Issued as inline assembly: the compiler
+// would otherwise wait for every outstanding buffer-to-LDS load before any LDS read (it
+// cannot tell which LDS bytes they write). The caller waits (lgkmcnt) before using the
+// result; in this kernel every step starts with s_waitcnt lgkmcnt(0) and a barrier, and
+// fragments are used one step after they are read.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+template <int OFF>
+LMOE_DEV bf16x8_t lds_read16(uint32_t addr) {
+  u32x4_t r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
+// Workgroup barrier without the release/acquire fences of __syncthreads(): the fence would
+// make every wavefront wait for all of its buffer-to-LDS loads, including the ones meant
+// to stay in flight. The kernel orders LDS itself: s_waitcnt on its own loads, then this.
+LMOE_DEV void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+struct Frag {
+  bf16x8_t a[8], b[8];
+};
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void tiled_gemm_kernel(
+    const StreamGemm g, int blocks_total, int m_tiles, int nch) {
+  __shared__ __attribute__((aligned(1024))) char smem[NSLOT * SLOT];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
   const int m = lane & 15, g4 = lane >> 4;
 
-  // consecutive logical tiles on one XCD (workgroups are dealt to the 8 XCDs in turn)
-  const int G = gridDim.x;
-  const int bid = (G & 7) == 0 ? (int)(blockIdx.x & 7) * (G >> 3) + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
-  const int mt = bid / blocks_total;
-  const int nb_all = bid - mt * blocks_total;
+  // ---- tile of this workgroup: XCD-contiguous logical ids, then row-tile groups of 8
+  const int G = m_tiles * blocks_total;
+  const int G8 = (G + 7) & ~7;
+  const int lid = (int)(blockIdx.x & 7) * (G8 >> 3) + (int)(blockIdx.x >> 3);
+  if (lid >= G) return;
+  const int per_group = GROUP_M * blocks_total;
+  const int grp = lid / per_group;
+  const int first_m = grp * GROUP_M;
+  const int gm = min(GROUP_M, m_tiles - first_m);
+  const int within = lid - grp * per_group;
+  const int mt = first_m + within % gm;
+  const int nb_all = within / gm;
   const int row0 = mt * TILE_M;
-  if (row0 >= g.M) return;
 
   int s = 0;
 #pragma unroll
@@ -67,154 +130,201 @@ __global__ __launch_bounds__(256) void tiled_gemm_kernel(const StreamGemm g, int
   const bool grouped = g.row_to_pair != nullptr;
   int e = 0;
   if (grouped) {
-    e = g.tile_expert[row0 / g.tile_m];
+    e = __builtin_amdgcn_readfirstlane(g.tile_expert[row0 / g.tile_m]);
     if (e < 0) return;
   }
 
-  // ---- rows this wave loads into LDS (groups 2*wave, 2*wave+1) and their byte offsets
-  int arow[2];
+  // ---- activation rows this wavefront copies (row groups 2*wave, 2*wave + 1)
+  const rsrc_t a_rs = make_rsrc(uniform_ptr(g.a), __builtin_amdgcn_readfirstlane(g.a_bytes));
+  uint32_t a_off[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int row = row0 + 16 * (2 * wave + h) + m;
+    int arow;
     if (grouped) {
       int p = g.row_to_pair[row];
       const bool real = p >= 0;
       if (!real) p = g.row_to_pair[row0];               // the tile's first row is always a real pair
-      arow[h] = g.a_by_row ? (real ? row : row0) : p / g.topk;
+      arow = g.a_by_row ? (real ? row : row0) : p / g.topk;
     } else {
-      arow[h] = min(row, g.M - 1);
+      arow = min(row, g.M - 1);
     }
-  }
-  const rsrc_t a_rs = make_rsrc(g.a, g.a_bytes);
-  uint32_t a_off[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) a_off[h] = (uint32_t)arow[h] * (uint32_t)(g.lda * 2) + g4 * 16;
-
-  // ---- weight row groups this wave loads (LDS groups 2*wave, 2*wave+1)
-  const uint32_t w_bytes = (uint32_t)sg.n_total * (uint32_t)(g.Kd * 2);
-  const rsrc_t w_rs = make_rsrc(reinterpret_cast<const char*>(sg.w) + (size_t)e * w_bytes, w_bytes);
-  uint32_t b_off[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int jj = 2 * wave + h;
-    const int n16 = situ ? (jj < 4 ? nb * 4 + jj : sg.n_out / 16 + nb * 4 + (jj - 4)) : nb * 8 + jj;
-    b_off[h] = (uint32_t)n16 * (uint32_t)nch * 4096u + lane * 16;   // past the matrix: zeros
+    a_off[h] = (uint32_t)arow * (uint32_t)(g.lda * 2) + g4 * 16;
   }
 
-  auto issue = [&](int c, int st) {
-    char* base = smem + st * STAGE;
+  // ---- weight row groups of this wavefront (its own 8 groups; SituGLU: 4 gate + 4 up)
+  const uint32_t w_bytes = __builtin_amdgcn_readfirstlane((uint32_t)sg.n_total * (uint32_t)(g.Kd * 2));
+  const rsrc_t w_rs = make_rsrc(uniform_ptr(reinterpret_cast<const char*>(sg.w) + (size_t)e * w_bytes), w_bytes);
+  uint32_t b_off[8];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+  for (int j = 0; j < 8; ++j) {
+    const int n16 = situ ? (j < 4 ? nb * 16 + 4 * wave + j : sg.n_out / 16 + nb * 16 + 4 * wave + (j - 4))
+                         : nb * 32 + 8 * wave + j;
+    b_off[j] = (uint32_t)n16 * (uint32_t)(g.Kd * 32) + lane * 16;   // past the matrix: zeros
+  }
+
+  auto issue = [&](int c) {
+    char* base = smem + (c % NSLOT) * SLOT;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        to_lds(a_rs, base + ((2 * wave + h) * 4 + q) * 1024, a_off[h], (uint32_t)c * 256u + q * 64u);
+    for (int h = 0; h < 2; ++h) to_lds(a_rs, base + (2 * wave + h) * 1024, a_off[h], (uint32_t)c * 64u);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        to_lds(w_rs, base + B_OFF + ((2 * wave + h) * 4 + q) * 1024, b_off[h], (uint32_t)c * 4096u + q * 1024u);
+    for (int j = 0; j < 8; ++j) to_lds(w_rs, base + B_OFF + (8 * wave + j) * 1024, b_off[j], (uint32_t)c * 1024u);
+  };
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)smem + lane * 16;
+  auto read = [&](int c, Frag& f) {
+    const uint32_t base = lds0 + (uint32_t)(c % NSLOT) * SLOT;
+    const uint32_t bbase = base + B_OFF + wave * 8192;
+    static_for<8>([&](auto i) { f.a[i] = lds_read16<int(i) * 1024>(base); });
+    static_for<8>([&](auto j) { f.b[j] = lds_read16<int(j) * 1024>(bbase); });
   };
 
-  floatx4 acc[NACC];
+  floatx4 acc[8][8];
 #pragma unroll
-  for (int j = 0; j < NACC; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  int bgrp[4];   // LDS weight groups of this wave's four column tiles
+  auto mma = [&](const Frag& f) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) bgrp[j] = situ ? (j < 2 ? 2 * wn + j : 4 + 2 * wn + (j - 2)) : 4 * wn + j;
-
-  auto compute = [&](int st) {
-    const char* base = smem + st * STAGE;
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      bf16x8_t a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const bf16x8_t*>(base + ((4 * wm + i) * 4 + q) * 1024 + lane * 16);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const bf16x8_t*>(base + B_OFF + (bgrp[j] * 4 + q) * 1024 + lane * 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i * 4 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i * 4 + j], 0, 0, 0);
-    }
+      for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
   };
 
-  issue(0, 0);
-  for (int c = 0; c < nch; ++c) {
-    if (c + 1 < nch) {
-      issue(c + 1, (c + 1) & 1);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(16));   // this wave's stage-c requests have landed
-    } else {
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    }
-    __syncthreads();                                 // ... and every other wave's
-    compute(c & 1);
-    __syncthreads();                                 // stage c & 1 is free for stage c + 2
-  }
+  // ---- prologue: steps 0 .. NSLOT-1 in flight; step 0 in registers
+#pragma unroll
+  for (int c = 0; c < NSLOT; ++c)
+    if (c < nch) issue(c);
+  // wait until at most `ahead` later steps of this wavefront are still in flight
+  auto wait_steps = [&](int ahead) {
+    if (ahead >= 3)
+      __builtin_amdgcn_s_waitcnt(waitcnt(3 * LOADS_PER_STEP, 0));
+    else if (ahead == 2)
+      __builtin_amdgcn_s_waitcnt(waitcnt(2 * LOADS_PER_STEP, 0));
+    else if (ahead == 1)
+      __builtin_amdgcn_s_waitcnt(waitcnt(LOADS_PER_STEP, 0));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt(0, 0));
+  };
+  wait_steps(min(nch, NSLOT) - 1);
+  lds_barrier();
+  Frag f0, f1;
+  read(0, f0);
 
-  // ---- epilogue: tile (i, j): rows row0 + 64 wm + 16 i + 4 g4 + rr, column lane m
+  // ---- main loop, two steps per trip so that the register fragments alternate.
+  // Step c: wait until step c + 1 has landed (this wavefront's loads, then the barrier for
+  // the others) and this wavefront's reads of step c (slot c % NSLOT) are done; after the
+  // barrier every wavefront is done with that slot, and step c + NSLOT goes into it. Then
+  // read step c + 1 into registers while the MFMAs of step c run.
+  auto step = [&](int c, Frag& cur, Frag& nxt) {
+    // issued so far: steps up to min(c + NSLOT - 1, nch - 1)
+    wait_steps(min(c + NSLOT - 1, nch - 1) - (c + 1));
+    lds_barrier();                        // nothing moves across the waits and the barrier
+    if (c + NSLOT < nch) issue(c + NSLOT);
+    if (c + 1 < nch) read(c + 1, nxt);
+    mma(cur);
+  };
+  int c = 0;
+  for (; c + 1 < nch; c += 2) {
+    step(c, f0, f1);
+    step(c + 1, f1, f0);
+  }
+  if (c < nch) step(c, f0, f1);
+
+  // ---- epilogue, 64 rows at a time through this wavefront's own LDS region (every
+  // wavefront is past its last LDS read and every buffer-to-LDS load has landed).
+  // Accumulator tile (i, j) element rr is row 16 i + 4 g4 + rr, column 16 j + m of the
+  // wavefront's 128 x 128 block; it is written to LDS as fp32 [64][RS], then read back as
+  // 4 consecutive columns per lane so that the outputs leave as contiguous row segments.
+  constexpr int RS = 132;                          // row stride (floats), padded against bank conflicts
+  float* red = reinterpret_cast<float*>(smem) + wave * (64 * RS);
   const float inv_b = 1.0f / g.beta;
   const float inv_lb = g.lbeta > 0.0f ? 1.0f / g.lbeta : 0.0f;
+  static_for<2>([&](auto h) {
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<4>([&](auto ii) {
+      static_for<8>([&](auto j) {
+        static_for<4>([&](auto rr) {
+          red[(16 * ii + 4 * g4 + rr) * RS + 16 * j + m] = acc[4 * int(h) + int(ii)][int(j)][int(rr)];
+        });
+      });
+    });
+    __builtin_amdgcn_sched_barrier(0);
+    const int rbase = row0 + 64 * h;
+    if (situ) {
+      // 16 lanes per row (4 outputs each): gate columns c .. c + 3, up columns 64 + c ..
+      const int q = lane & 15;
+      const int col = 256 * nb + 64 * wave + 4 * q;
+      for (int r = lane >> 4; r < 64; r += 4) {
+        const int row = rbase + r;
+        const int pair = grouped ? g.row_to_pair[row] : (row < g.M ? row : -1);
+        const floatx4 gv = *reinterpret_cast<const floatx4*>(red + r * RS + 4 * q);
+        const floatx4 uv = *reinterpret_cast<const floatx4*>(red + r * RS + 64 + 4 * q);
+        if (pair < 0 || col >= sg.n_out) continue;
+        float v[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int row = row0 + 64 * wm + 16 * i + 4 * g4 + rr;
-      int pair = row;
-      if (grouped) {
-        pair = g.row_to_pair[row];
-        if (pair < 0) continue;
-      } else if (row >= g.M) {
-        continue;
-      }
-      if (situ) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = 64 * nb + 32 * wn + 16 * j + m;
-          if (col >= sg.n_out) continue;
-          const float v = situ_f(acc[i * 4 + j][rr], acc[i * 4 + j + 2][rr], g.beta, inv_b, g.lbeta, inv_lb);
-          store_out(sg.out_elt, sg.out, (size_t)row * sg.ldo + col, v);
+        for (int k = 0; k < 4; ++k) v[k] = situ_f(gv[k], uv[k], g.beta, inv_b, g.lbeta, inv_lb);
+        const size_t idx = (size_t)row * sg.ldo + col;
+        if (sg.out_elt == Elt::F32) {
+          *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(sg.out) + idx) = floatx4{v[0], v[1], v[2], v[3]};
+        } else {
+          const uint32_t lo = f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+          const uint32_t hi = f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(sg.out) + idx) = make_uint2(lo, hi);
         }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = 128 * nb + 64 * wn + 16 * j + m;
-          if (col >= sg.n_out) continue;
-          float v = acc[i * 4 + j][rr];
-          if (sg.epi == Epi::STORE) {
-            store_out(sg.out_elt, sg.out, (size_t)row * sg.ldo + col, v);
-          } else if (sg.epi == Epi::PAIR) {
-            const float wgt = g.pair_w ? g.pair_w[pair] : 1.0f;
-            reinterpret_cast<float*>(sg.out)[(size_t)pair * sg.ldo + col] = wgt * v;
-          } else if (sg.epi == Epi::TOKEN) {
-            const float wgt = g.pair_w ? g.pair_w[pair] : 1.0f;
-            store_out(sg.out_elt, sg.out, (size_t)(pair / g.topk) * sg.ldo + col, wgt * v);
-          } else if (sg.epi == Epi::ADD) {
-            const size_t idx = (size_t)row * sg.ldo + col;
-            const float add = g.add ? (sg.out_elt == Elt::F32 ? reinterpret_cast<const float*>(g.add)[idx]
-                                                               : bf16_to_f32(reinterpret_cast<const uint16_t*>(g.add)[idx]))
-                                    : 0.0f;
-            store_out(sg.out_elt, sg.out, idx, add + v);
+      }
+    } else {
+      // 32 lanes per row (4 columns each)
+      const int q = lane & 31;
+      const int col = TILE_N * nb + 128 * wave + 4 * q;
+      for (int r = lane >> 5; r < 64; r += 2) {
+        const int row = rbase + r;
+        const int pair = grouped ? g.row_to_pair[row] : (row < g.M ? row : -1);
+        floatx4 v = *reinterpret_cast<const floatx4*>(red + r * RS + 4 * q);
+        if (pair < 0 || col >= sg.n_out) continue;
+        size_t idx = (size_t)row * sg.ldo + col;
+        if (sg.epi == Epi::PAIR || sg.epi == Epi::TOKEN) {
+          const float wgt = g.pair_w ? g.pair_w[pair] : 1.0f;
+          v *= wgt;
+          if (sg.epi == Epi::PAIR) {
+            *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(sg.out) + (size_t)pair * sg.ldo + col) = v;
+            continue;
           }
+          idx = (size_t)(pair / g.topk) * sg.ldo + col;
+        } else if (sg.epi == Epi::ADD && g.add != nullptr) {
+          if (sg.out_elt == Elt::F32) {
+            v += *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(g.add) + idx);
+          } else {
+            const uint2 a = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(g.add) + idx);
+            v += floatx4{bf16_to_f32((uint16_t)a.x), bf16_to_f32((uint16_t)(a.x >> 16)), bf16_to_f32((uint16_t)a.y),
+                         bf16_to_f32((uint16_t)(a.y >> 16))};
+          }
+        }
+        if (sg.out_elt == Elt::F32) {
+          *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(sg.out) + idx) = v;
+        } else {
+          const uint32_t lo = f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+          const uint32_t hi = f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(sg.out) + idx) = make_uint2(lo, hi);
         }
       }
     }
+  });
 }
 
 hipError_t launch_tiled_gemm(StreamGemm g, hipStream_t stream) {
-  const int nch = g.Kd / 128;
+  const int nch = g.Kd / 32;
   int b0 = 0;
   for (int i = 0; i < g.nseg; ++i) {
-    const int per = g.seg[i].epi == Epi::SITU ? 64 : 128;
+    const int per = g.seg[i].epi == Epi::SITU ? TILE_N / 2 : TILE_N;
     g.seg[i].blocks = (g.seg[i].n_out + per - 1) / per;
     g.seg[i].block0 = b0;
     b0 += g.seg[i].blocks;
   }
   const int m_tiles = (g.M + TILE_M - 1) / TILE_M;
-  hipLaunchKernelGGL(tiled_gemm_kernel, dim3((unsigned)(m_tiles * b0)), dim3(256), 0, stream, g, b0, nch);
+  const int G = m_tiles * b0;
+  const unsigned G8 = (unsigned)((G + 7) & ~7);
+  hipLaunchKernelGGL(tiled_gemm_kernel, dim3(G8), dim3(256), 0, stream, g, b0, m_tiles, nch);
   return hipGetLastError();
 }
 
