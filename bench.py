@@ -52,6 +52,31 @@ def fc1_bytes(cfg, n_touched, rows):
     return n_touched * 2 * cfg.d * cfg.L * 2 + cfg.T * cfg.L * 2 + rows * cfg.d * 2
 
 
+def fc1_traffic(cfg, seed):
+    """HBM bytes per FC1 launch from the committed counter profile (FETCH_SIZE + WRITE_SIZE,
+    scaled by a plain copy of known size), for the workload it was taken on; None when
+    the workload differs or the kernel sources changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "fc1_decode_bf16_pmc.md")
+    if cfg.name != "decode_bf16" or seed != 2 or not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("|", " ", "#", "`")):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    try:
+        h = hashlib.sha256()
+        for f in kv["kernel_sources"].split():
+            with open(os.path.join(ROOT, f), "rb") as fh:
+                h.update(fh.read())
+        if h.hexdigest() != kv["kernel_sources_sha256"]:
+            return None
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
+
+
 def route_microbench(torch, B, LI, reps=200):
     cfg = LI.ROUTE_MASKED
     logits = LI.make_route_logits(cfg, 3, device="cuda")
@@ -117,6 +142,9 @@ def main():
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=8)
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="run one plain device copy of this many MiB (fp32 multiply by one) before the "
+                         "layer, as the reference kernel for HBM byte counters")
     ap.add_argument("--schedule", choices=["one_stream", "shared_stream"], default="shared_stream",
                     help="shared_stream: the shared expert runs on a second stream")
     args = ap.parse_args()
@@ -142,6 +170,16 @@ def main():
     X_cpu = LI.make_x(cfg, args.seed)
     X = X_cpu.to("cuda")
     stream = torch.cuda.current_stream()
+
+    if args.calibrate_copy_mb > 0:
+        n = args.calibrate_copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)      # reads and writes n * 4 bytes
+        torch.cuda.synchronize()
+        log(f"calibration copy: {n * 4} bytes read, {n * 4} bytes written")
+        del src, dst
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -199,7 +237,7 @@ def main():
                    "tokens_per_step": cfg.T, "seed": args.seed, "schedule": args.schedule},
         "roofline": {"kernel": "grouped FC1 + SituGLU (stream_gemm_kernel, SituGLU epilogue)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": fc1_traffic(cfg, args.seed),
                      "algorithmic_bytes": fb, "avg_ms": round(fc1_ms, 5), "n_touched_experts": n_touched},
         "layer_hbm": {"algorithmic_bytes": lb, "achieved_GBs": round(lb / (ms_per_step * 1e-3) / 1e9, 1),
                       "frac": round(lb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
