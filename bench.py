@@ -145,6 +145,8 @@ def main():
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB (fp32 multiply by one) before the "
                          "layer, as the reference kernel for HBM byte counters")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of a HIP graph of the layer step instead of eager launches")
     ap.add_argument("--schedule", choices=["one_stream", "shared_stream"], default="shared_stream",
                     help="shared_stream: the shared expert runs on a second stream")
     args = ap.parse_args()
@@ -186,12 +188,20 @@ def main():
         layer.forward(X)
     torch.cuda.synchronize()
 
+    step = (lambda: layer.forward(X))
+    if args.graph:
+        graph = layer.capture(X)
+        step = graph.replay
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+
     # timed region: K whole-layer steps, back to back
-    log(f"timing {args.steps} steps")
+    log(f"timing {args.steps} steps ({'graph replays' if args.graph else 'eager launches'})")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        layer.forward(X)
+        step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1000.0 / args.steps
@@ -234,7 +244,8 @@ def main():
         "data": "synthetic (seeded counter-based generator; random-init weights)",
         "config": {"workload": f"{cfg.name}: T={cfg.T} H={cfg.H} L={cfg.L} E={cfg.E} top-{cfg.K} d={cfg.d} "
                                f"shared I={cfg.I} experts={cfg.experts} tile_m={cfg.tile_m}",
-                   "tokens_per_step": cfg.T, "seed": args.seed, "schedule": args.schedule},
+                   "tokens_per_step": cfg.T, "seed": args.seed, "schedule": args.schedule,
+                   "launch": "hip_graph" if args.graph else "eager"},
         "roofline": {"kernel": "grouped FC1 + SituGLU (stream_gemm_kernel, SituGLU epilogue)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": fc1_traffic(cfg, args.seed),

@@ -147,6 +147,20 @@ lmoe_status lmoe_permute(int T, int E, int K, int tile_m, const int32_t* topk_id
                          int32_t* row_to_pair, int32_t* tile_expert, int32_t* pair_to_row,
                          int rows_cap, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Routing followed by the permutation, in one launch for decode-sized batches
+ * (T <= 16 and T*K <= 1024: one workgroup routes each token with one wavefront, keeps the
+ * ids on chip and builds the permutation from them; [P2] "Commit 1": routing writes the
+ * workspace that FC1 / FC2 / finalize read). Larger batches run lmoe_route then
+ * lmoe_permute. Arguments, outputs, checks and error codes are exactly those of the two
+ * calls (topk_ids and topk_weights are written as by lmoe_route; workspace as for
+ * lmoe_permute); results are identical to the two calls made in sequence. */
+lmoe_status lmoe_route_permute(int T, int E, int K, const float* logits, const float* bias,
+                               float routed_scaling_factor, int renormalize,
+                               int32_t* topk_ids, float* topk_weights, int tile_m,
+                               int32_t* expert_counts, int32_t* expert_offsets, int32_t* tile_offsets,
+                               int32_t* row_to_pair, int32_t* tile_expert, int32_t* pair_to_row,
+                               int rows_cap, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* a4 / a8 -- MXFP8 (E4M3) quantization along rows ([OCP-MX]; [P2] "Description": input
  * quantization before the MXE4M3 x MXE2M1 experts; [P1] commit 3: the general gated
  * activations apply the activation, then requantize). Per 32 consecutive elements:
@@ -205,6 +219,22 @@ lmoe_status lmoe_fc2_combine(int T, int E, int K, int d, int out_dim, int tile_m
                              int rows_cap, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/* FC2 + combine + latent RMSNorm, the FC2 half of the layer ending in the normalized
+ * latent that the up projection reads: exactly lmoe_fc2_combine with out_dtype F32 and
+ * out = z, followed by the RMSNorm of lmoe_tail (norm_out = z / sqrt(mean(z^2) + eps) *
+ * gamma, in fp32; gamma [out_dim] and norm_out [T, out_dim] in norm_dtype, F32 or BF16).
+ * With K > 1 one kernel sums each token's K products (fixed k order) and normalizes the
+ * sum, which it also stores in z; results are bit-identical to the two separate calls.
+ * Pass latent = NULL to lmoe_tail / lmoe_tail_shared afterwards. Extra checks: eps >= 0
+ * and finite, out_dim % 4 == 0, norm_out != NULL and != z (when T > 0). */
+lmoe_status lmoe_fc2_combine_norm(int T, int E, int K, int d, int out_dim, int tile_m,
+                                  lmoe_dtype act_dtype, const void* act, const uint8_t* act_scale,
+                                  const int32_t* row_to_pair, const int32_t* tile_expert,
+                                  lmoe_dtype w_dtype, const void* w2, const uint8_t* w2_scale,
+                                  const float* topk_weights, float* z, int rows_cap,
+                                  void* workspace, size_t workspace_bytes, const void* gamma, float eps,
+                                  lmoe_dtype norm_dtype, void* norm_out, hipStream_t stream);
+
 /* a11 + a12 -- latent tail ([P1] commit 7: the routed output is summed before the
  * output transform because it contains an RMSNorm; [P3] _shard_up_proj_tail: norm of
  * the reduced latent, then shared += latent @ up_proj^T in the GEMM's epilogue; [P1]
@@ -214,7 +244,8 @@ lmoe_status lmoe_fc2_combine(int T, int E, int K, int d, int out_dim, int tile_m
  * latent fp32 [T, L]; gamma [L] in io_dtype (NULL = ones); w_up [H, L] in io_dtype;
  * shared, out [T, H] in io_dtype (shared NULL = no add; out may alias shared);
  * norm_out [T, L] in io_dtype (caller-owned, also returned). io_dtype F32 or BF16.
- * eps >= 0. L % 128 == 0 (BF16) / 64 (F32), H % 16 == 0. */
+ * latent NULL: norm_out already holds the normalized latent (from lmoe_fc2_combine_norm)
+ * and only the projection runs. eps >= 0. L % 128 == 0 (BF16) / 64 (F32), H % 16 == 0. */
 lmoe_status lmoe_tail(int T, int L, int H, const float* latent, const void* gamma, float eps,
                       const void* w_up, const void* shared, lmoe_dtype io_dtype, void* out,
                       void* norm_out, hipStream_t stream);
@@ -228,7 +259,8 @@ lmoe_status lmoe_tail(int T, int L, int H, const float* latent, const void* gamm
  * where round() rounds to io_dtype: the shared-expert output is rounded exactly as if
  * it had been stored, then added in fp32. shared_act [T, I] is the shared expert's
  * SituGLU activation, w_s2 [H, I] and w_up [H, L] packed weights. out must not alias
- * shared_act or norm_out. L % 128 and I % 128 == 0 (BF16; 64 for F32), H % 16 == 0. */
+ * shared_act or norm_out. latent NULL: norm_out already holds the normalized latent.
+ * L % 128 and I % 128 == 0 (BF16; 64 for F32), H % 16 == 0. */
 lmoe_status lmoe_tail_shared(int T, int L, int H, int I, const float* latent, const void* gamma, float eps,
                              const void* w_up, const void* shared_act, const void* w_s2, lmoe_dtype io_dtype,
                              void* out, void* norm_out, hipStream_t stream);

@@ -40,12 +40,15 @@ SIGNATURES = [
     ("lmoe_permute_workspace_bytes", _z, [_i, _i, _i]),
     ("lmoe_permute_rows_cap", _i, [_i, _i, _i, _i]),
     ("lmoe_permute", _i, [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _i, _p, _z, _p]),
+    ("lmoe_route_permute", _i, [_i, _i, _i, _p, _p, _f, _i, _p, _p, _i, _p, _p, _p, _p, _p, _p, _i, _p, _z, _p]),
     ("lmoe_quant_mxfp8", _i, [_i, _i, _i, _p, _p, _p, _p]),
     ("lmoe_fc1_situ", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _i, _p, _p, _f, _f, _i, _p, _p, _i,
                            _p]),
     ("lmoe_fc2_workspace_bytes", _z, [_i, _i, _i]),
     ("lmoe_fc2_combine", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _i, _p, _p, _p, _i, _p, _i, _p,
                               _z, _p]),
+    ("lmoe_fc2_combine_norm", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _i, _p, _p, _p, _p, _i, _p, _z, _p, _f,
+                                   _i, _p, _p]),
     ("lmoe_tail", _i, [_i, _i, _i, _p, _p, _f, _p, _p, _i, _p, _p, _p]),
     ("lmoe_tail_shared", _i, [_i, _i, _i, _i, _p, _p, _f, _p, _p, _p, _i, _p, _p, _p]),
     ("lmoe_situ_masked", _i, [_i, _i, _i, _i, _p, _p, _f, _f, _p, _p]),
@@ -171,6 +174,15 @@ def lmoe_permute(T, E, K, tile_m, topk_ids, expert_counts, expert_offsets, tile_
                                               int(workspace_bytes), _stream(stream)))
 
 
+def lmoe_route_permute(T, E, K, logits, bias, routed_scaling_factor, renormalize, topk_ids, topk_weights, tile_m,
+                       expert_counts, expert_offsets, tile_offsets, row_to_pair, tile_expert, pair_to_row, rows_cap,
+                       workspace, workspace_bytes, stream=None):
+    _check("lmoe_route_permute", lib().lmoe_route_permute(
+        T, E, K, _ptr(logits), _ptr(bias), float(routed_scaling_factor), int(renormalize), _ptr(topk_ids),
+        _ptr(topk_weights), tile_m, _ptr(expert_counts), _ptr(expert_offsets), _ptr(tile_offsets), _ptr(row_to_pair),
+        _ptr(tile_expert), _ptr(pair_to_row), rows_cap, _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
 def lmoe_quant_mxfp8(rows, cols, in_dtype, inp, codes, scales, stream=None):
     _check("lmoe_quant_mxfp8", lib().lmoe_quant_mxfp8(rows, cols, in_dtype, _ptr(inp), _ptr(codes), _ptr(scales),
                                                       _stream(stream)))
@@ -195,6 +207,15 @@ def lmoe_fc2_combine(T, E, K, d, out_dim, tile_m, act_dtype, act, act_scale, row
                                                       w_dtype, _ptr(w2), _ptr(w2_scale), _ptr(topk_weights),
                                                       out_dtype, _ptr(out), rows_cap, _ptr(workspace),
                                                       int(workspace_bytes), _stream(stream)))
+
+
+def lmoe_fc2_combine_norm(T, E, K, d, out_dim, tile_m, act_dtype, act, act_scale, row_to_pair, tile_expert, w_dtype,
+                          w2, w2_scale, topk_weights, z, rows_cap, workspace, workspace_bytes, gamma, eps, norm_dtype,
+                          norm_out, stream=None):
+    _check("lmoe_fc2_combine_norm", lib().lmoe_fc2_combine_norm(
+        T, E, K, d, out_dim, tile_m, act_dtype, _ptr(act), _ptr(act_scale), _ptr(row_to_pair), _ptr(tile_expert),
+        w_dtype, _ptr(w2), _ptr(w2_scale), _ptr(topk_weights), _ptr(z), rows_cap, _ptr(workspace),
+        int(workspace_bytes), _ptr(gamma), float(eps), norm_dtype, _ptr(norm_out), _stream(stream)))
 
 
 def lmoe_tail(T, L, H, latent, gamma, eps, w_up, shared, io_dtype, out, norm_out, stream=None):

@@ -188,6 +188,61 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(int L, const float* __rest
   }
 }
 
+// ---- combine + latent RMSNorm in one pass per token: z[t, :] = sum_{k ascending} ws[t*K + k, :]
+// (stored fp32), then n = z / sqrt(mean(z^2) + eps) * gamma with the summation order of
+// rmsnorm_kernel, so both routes give the same bits. Each thread reads back only the z
+// values it wrote itself.
+__global__ __launch_bounds__(256) void combine_norm_kernel(int K, int L, const float* __restrict__ ws,
+                                                           float* __restrict__ z, const void* __restrict__ gamma,
+                                                           int gamma_bf16, float eps, int out_bf16,
+                                                           void* __restrict__ out) {
+  __shared__ float s_part[4];
+  const int t = blockIdx.x;
+  float* zrow = z + (size_t)t * L;
+  const float* src = ws + (size_t)t * K * L;
+  float ss = 0.0f;
+  for (int i = threadIdx.x * 4; i < L; i += 256 * 4) {
+    float4 v = *reinterpret_cast<const float4*>(src + i);
+    for (int k = 1; k < K; ++k) {
+      const float4 u = *reinterpret_cast<const float4*>(src + (size_t)k * L + i);
+      v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+    }
+    *reinterpret_cast<float4*>(zrow + i) = v;
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+  const float r = 1.0f / sqrtf(tot / (float)L + eps);
+  for (int i = threadIdx.x * 4; i < L; i += 256 * 4) {
+    const float4 v = *reinterpret_cast<const float4*>(zrow + i);
+    float o[4] = {v.x * r, v.y * r, v.z * r, v.w * r};
+    if (gamma) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] *= gamma_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(gamma)[i + q])
+                           : reinterpret_cast<const float*>(gamma)[i + q];
+    }
+    if (out_bf16) {
+      uint2 p;
+      p.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+      p.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + (size_t)t * L + i) = p;
+    } else {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + (size_t)t * L + i) =
+          make_float4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
+hipError_t launch_combine_norm(int T, int K, int L, const float* ws, float* z, const void* gamma, float eps, Elt elt,
+                               void* out, hipStream_t stream) {
+  const int bf = elt == Elt::BF16 ? 1 : 0;
+  hipLaunchKernelGGL(combine_norm_kernel, dim3(T), dim3(256), 0, stream, K, L, ws, z, gamma, bf, eps, bf, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_rmsnorm(int T, int L, const float* z, const void* gamma, float eps, Elt elt, void* out,
                           hipStream_t stream) {
   const int bf = elt == Elt::BF16 ? 1 : 0;

@@ -79,6 +79,13 @@ hipError_t launch_permute(int npairs, int E, int tile_m, int max_tiles, const in
                           int32_t* offsets, int32_t* tile_offsets, int32_t* row_to_pair, int32_t* tile_expert,
                           int32_t* pair_to_row, void* workspace, hipStream_t stream);
 
+// Routing then permutation (one workgroup when route_permute_fusable(T, K)).
+bool route_permute_fusable(int T, int K);
+hipError_t launch_route_permute(int T, int E, int K, const float* logits, const float* bias, float rsf,
+                                int renorm, int32_t* ids, float* weights, int tile_m, int max_tiles,
+                                int32_t* counts, int32_t* offsets, int32_t* tile_offsets, int32_t* row_to_pair,
+                                int32_t* tile_expert, int32_t* pair_to_row, void* workspace, hipStream_t stream);
+
 hipError_t launch_situ_masked(int E, int T_max, int d, Elt elt, const void* in, const int32_t* counts,
                               float beta, float lbeta, void* out, hipStream_t stream);
 hipError_t launch_quant_mxfp8(int rows, int cols, Elt elt, const void* in, uint8_t* codes, uint8_t* scales,
@@ -87,6 +94,9 @@ hipError_t launch_combine(int T, int K, int N, const float* ws, Elt out_elt, voi
 hipError_t launch_pack_weights(int batch, int N, int Kd, int esize, const void* src, void* dst, hipStream_t stream);
 hipError_t launch_pack_mxfp4(int batch, int N, int Kd, const void* codes_src, const void* scales_src, void* codes_dst,
                              void* scales_dst, hipStream_t stream);
+// Combine (fixed k order) into fp32 z and RMSNorm of z into out, one workgroup per token.
+hipError_t launch_combine_norm(int T, int K, int L, const float* ws, float* z, const void* gamma, float eps, Elt elt,
+                               void* out, hipStream_t stream);
 hipError_t launch_rmsnorm(int T, int L, const float* z, const void* gamma, float eps, Elt elt, void* out,
                           hipStream_t stream);
 

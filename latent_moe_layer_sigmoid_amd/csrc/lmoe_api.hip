@@ -172,6 +172,28 @@ lmoe_status lmoe_permute(int T, int E, int K, int tile_m, const int32_t* topk_id
                                    stream));
 }
 
+lmoe_status lmoe_route_permute(int T, int E, int K, const float* logits, const float* bias, float rsf,
+                               int renormalize, int32_t* topk_ids, float* topk_weights, int tile_m,
+                               int32_t* expert_counts, int32_t* expert_offsets, int32_t* tile_offsets,
+                               int32_t* row_to_pair, int32_t* tile_expert, int32_t* pair_to_row, int rows_cap,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  // the checks of lmoe_route, then those of lmoe_permute
+  if (T < 0 || E < 1 || K < 1 || K > E || K > 64 || !isfinite(rsf) || !tile_ok(tile_m)) return LMOE_ERR_INVALID_ARG;
+  if (E > 1024) return LMOE_ERR_UNSUPPORTED;
+  if ((long)T * K > 0x3FFFFFFFL) return LMOE_ERR_UNSUPPORTED;
+  if (T == 0) return LMOE_OK;
+  if (!logits || !topk_ids || !topk_weights || !expert_counts || !expert_offsets || !tile_offsets ||
+      !row_to_pair || !tile_expert || !pair_to_row)
+    return LMOE_ERR_INVALID_ARG;
+  const long npairs = (long)T * K;
+  if (rows_cap < rows_bound(npairs, E, tile_m) || rows_cap % tile_m != 0) return LMOE_ERR_WORKSPACE;
+  const size_t need = permute_workspace_bytes((int)npairs, E);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return LMOE_ERR_WORKSPACE;
+  return hip_status(launch_route_permute(T, E, K, logits, bias, rsf, renormalize, topk_ids, topk_weights, tile_m,
+                                         rows_cap / tile_m, expert_counts, expert_offsets, tile_offsets,
+                                         row_to_pair, tile_expert, pair_to_row, workspace, stream));
+}
+
 lmoe_status lmoe_quant_mxfp8(int rows, int cols, lmoe_dtype in_dtype, const void* in, uint8_t* codes,
                              uint8_t* scales, hipStream_t stream) {
   if (rows < 0 || cols <= 0 || !dense_elt(in_dtype)) return LMOE_ERR_INVALID_ARG;
@@ -264,11 +286,27 @@ size_t lmoe_fc2_workspace_bytes(int T, int K, int out_dim) {
   return (size_t)T * K * out_dim * sizeof(float);
 }
 
-lmoe_status lmoe_fc2_combine(int T, int E, int K, int d, int out_dim, int tile_m, lmoe_dtype act_dtype,
-                             const void* act, const uint8_t* act_scale, const int32_t* row_to_pair,
-                             const int32_t* tile_expert, lmoe_dtype w_dtype, const void* w2,
-                             const uint8_t* w2_scale, const float* topk_weights, lmoe_dtype out_dtype, void* out,
-                             int rows_cap, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// FC2 + combine; with norm_out != NULL the combined fp32 rows are also RMS-normalized into
+// norm_out (norm_dtype, with gamma of that dtype) by the same kernel that sums them.
+static lmoe_status fc2_combine_impl(int T, int E, int K, int d, int out_dim, int tile_m, lmoe_dtype act_dtype,
+                                    const void* act, const uint8_t* act_scale, const int32_t* row_to_pair,
+                                    const int32_t* tile_expert, lmoe_dtype w_dtype, const void* w2,
+                                    const uint8_t* w2_scale, const float* topk_weights, lmoe_dtype out_dtype,
+                                    void* out, int rows_cap, void* workspace, size_t workspace_bytes,
+                                    const void* gamma, float eps, lmoe_dtype norm_dtype, void* norm_out,
+                                    hipStream_t stream) {
+  const bool norm = norm_out != nullptr;
+  auto finish = [&](hipError_t err) -> lmoe_status {   // combine (K > 1) and / or RMSNorm
+    if (err != hipSuccess) return LMOE_ERR_HIP;
+    if (K > 1 && norm)
+      err = launch_combine_norm(T, K, out_dim, (const float*)workspace, (float*)out, gamma, eps, elt_of(norm_dtype),
+                                norm_out, stream);
+    else if (K > 1)
+      err = launch_combine(T, K, out_dim, (const float*)workspace, elt_of(out_dtype), out, stream);
+    else if (norm)
+      err = launch_rmsnorm(T, out_dim, (const float*)out, gamma, eps, elt_of(norm_dtype), norm_out, stream);
+    return hip_status(err);
+  };
   bool dense = false;
   lmoe_status st = check_grouped(T, E, K, tile_m, row_to_pair, tile_expert, rows_cap, &dense);
   if (st != LMOE_OK) return st;
@@ -302,10 +340,7 @@ lmoe_status lmoe_fc2_combine(int T, int E, int K, int d, int out_dim, int tile_m
       g.seg[0] = Seg{w2, out_dim, out_dim, Epi::TOKEN, elt_of(out_dtype), out, out_dim, 0, 0};
     else
       g.seg[0] = Seg{w2, out_dim, out_dim, Epi::PAIR, Elt::F32, workspace, out_dim, 0, 0};
-    hipError_t err = launch_stream_gemm_mx(g, live_tiles((long)T * K, E), stream);
-    if (err != hipSuccess) return LMOE_ERR_HIP;
-    if (K > 1) err = launch_combine(T, K, out_dim, (const float*)workspace, elt_of(out_dtype), out, stream);
-    return hip_status(err);
+    return finish(launch_stream_gemm_mx(g, live_tiles((long)T * K, E), stream));
   }
   if (!dense_elt(act_dtype) || act_dtype != w_dtype) return LMOE_ERR_INVALID_ARG;
   if (d % kchunk_of(act_dtype) != 0 || out_dim % 16 != 0) return LMOE_ERR_UNSUPPORTED;
@@ -334,10 +369,32 @@ lmoe_status lmoe_fc2_combine(int T, int E, int K, int d, int out_dim, int tile_m
     g.seg[0] = Seg{w2, out_dim, out_dim, Epi::PAIR, Elt::F32, workspace, out_dim, 0, 0};
   const int live = dense ? (T + 15) / 16 : live_tiles((long)T * K, E);
   const bool tiled = dense ? use_tiled_dense(T, act_dtype) : use_tiled_grouped(tile_m, act_dtype);
-  hipError_t err = run_gemm(g, act_dtype, tiled, live, stream);
-  if (err != hipSuccess) return LMOE_ERR_HIP;
-  if (K > 1) err = launch_combine(T, K, out_dim, (const float*)workspace, elt_of(out_dtype), out, stream);
-  return hip_status(err);
+  return finish(run_gemm(g, act_dtype, tiled, live, stream));
+}
+
+lmoe_status lmoe_fc2_combine(int T, int E, int K, int d, int out_dim, int tile_m, lmoe_dtype act_dtype,
+                             const void* act, const uint8_t* act_scale, const int32_t* row_to_pair,
+                             const int32_t* tile_expert, lmoe_dtype w_dtype, const void* w2,
+                             const uint8_t* w2_scale, const float* topk_weights, lmoe_dtype out_dtype, void* out,
+                             int rows_cap, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return fc2_combine_impl(T, E, K, d, out_dim, tile_m, act_dtype, act, act_scale, row_to_pair, tile_expert, w_dtype,
+                          w2, w2_scale, topk_weights, out_dtype, out, rows_cap, workspace, workspace_bytes, nullptr,
+                          0.0f, LMOE_F32, nullptr, stream);
+}
+
+lmoe_status lmoe_fc2_combine_norm(int T, int E, int K, int d, int out_dim, int tile_m, lmoe_dtype act_dtype,
+                                  const void* act, const uint8_t* act_scale, const int32_t* row_to_pair,
+                                  const int32_t* tile_expert, lmoe_dtype w_dtype, const void* w2,
+                                  const uint8_t* w2_scale, const float* topk_weights, float* z, int rows_cap,
+                                  void* workspace, size_t workspace_bytes, const void* gamma, float eps,
+                                  lmoe_dtype norm_dtype, void* norm_out, hipStream_t stream) {
+  if (!dense_elt(norm_dtype) || !(eps >= 0.0f) || !isfinite(eps)) return LMOE_ERR_INVALID_ARG;
+  if (out_dim % 4 != 0) return LMOE_ERR_UNSUPPORTED;
+  if (T > 0 && !norm_out) return LMOE_ERR_INVALID_ARG;
+  if (T > 0 && (void*)z == norm_out) return LMOE_ERR_INVALID_ARG;
+  return fc2_combine_impl(T, E, K, d, out_dim, tile_m, act_dtype, act, act_scale, row_to_pair, tile_expert, w_dtype,
+                          w2, w2_scale, topk_weights, LMOE_F32, z, rows_cap, workspace, workspace_bytes, gamma, eps,
+                          norm_dtype, T > 0 ? norm_out : nullptr, stream);
 }
 
 lmoe_status lmoe_tail(int T, int L, int H, const float* latent, const void* gamma, float eps, const void* w_up,
@@ -346,10 +403,12 @@ lmoe_status lmoe_tail(int T, int L, int H, const float* latent, const void* gamm
   if (!dense_elt(io_dtype) || !(eps >= 0.0f) || !isfinite(eps)) return LMOE_ERR_INVALID_ARG;
   if (L % kchunk_of(io_dtype) != 0 || H % 16 != 0) return LMOE_ERR_UNSUPPORTED;
   if (T == 0) return LMOE_OK;
-  if (!latent || !w_up || !out || !norm_out) return LMOE_ERR_INVALID_ARG;
+  if (!w_up || !out || !norm_out) return LMOE_ERR_INVALID_ARG;
   if (!fits32(T, L, io_dtype) || !fits32(H, L, io_dtype)) return LMOE_ERR_UNSUPPORTED;
-  hipError_t err = launch_rmsnorm(T, L, latent, gamma, eps, elt_of(io_dtype), norm_out, stream);
-  if (err != hipSuccess) return LMOE_ERR_HIP;
+  if (latent) {   // NULL: norm_out already holds the normalized latent
+    hipError_t err = launch_rmsnorm(T, L, latent, gamma, eps, elt_of(io_dtype), norm_out, stream);
+    if (err != hipSuccess) return LMOE_ERR_HIP;
+  }
   StreamGemm g{};
   g.a = norm_out;
   g.a_bytes = (uint32_t)((long)T * L * esize_of(io_dtype));
@@ -371,12 +430,15 @@ lmoe_status lmoe_tail_shared(int T, int L, int H, int I, const float* latent, co
   if (!dense_elt(io_dtype) || !(eps >= 0.0f) || !isfinite(eps)) return LMOE_ERR_INVALID_ARG;
   if (L % kchunk_of(io_dtype) != 0 || I % kchunk_of(io_dtype) != 0 || H % 16 != 0) return LMOE_ERR_UNSUPPORTED;
   if (T == 0) return LMOE_OK;
-  if (!latent || !w_up || !shared_act || !w_s2 || !out || !norm_out) return LMOE_ERR_INVALID_ARG;
+  if (!w_up || !shared_act || !w_s2 || !out || !norm_out) return LMOE_ERR_INVALID_ARG;
   if (out == shared_act || out == norm_out) return LMOE_ERR_INVALID_ARG;
   if (!fits32(T, L, io_dtype) || !fits32(T, I, io_dtype) || !fits32(H, L, io_dtype) || !fits32(H, I, io_dtype))
     return LMOE_ERR_UNSUPPORTED;
-  hipError_t err = launch_rmsnorm(T, L, latent, gamma, eps, elt_of(io_dtype), norm_out, stream);
-  if (err != hipSuccess) return LMOE_ERR_HIP;
+  hipError_t err = hipSuccess;
+  if (latent) {   // NULL: norm_out already holds the normalized latent
+    err = launch_rmsnorm(T, L, latent, gamma, eps, elt_of(io_dtype), norm_out, stream);
+    if (err != hipSuccess) return LMOE_ERR_HIP;
+  }
   if (use_tiled_dense(T, io_dtype)) {
     // token-heavy: out = shared-expert FC2 (stored, rounded), then out += up projection in place
     StreamGemm g{};

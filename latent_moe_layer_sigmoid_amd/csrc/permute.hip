@@ -9,8 +9,13 @@
 // lanes, and the per-wave counts in LDS give the offset of each earlier wave.
 //   1 block  : one fused kernel (count, scan, rank, scatter).
 //   >1 blocks: count per block -> one-block scan over (expert, block) -> rank + scatter.
+// Decode-sized batches (T <= 16 tokens, T*K <= 1024 pairs) can also run routing and the
+// permutation as one workgroup: wavefront t routes token t (TensorRT-LLM PR 20541,
+// "Commit 1": the routing kernel writes the workspace FC1 / FC2 read), the ids stay in LDS
+// and the single-block permutation follows after a barrier.
 #include "common.h"
 #include "kernels.h"
+#include "route_dev.h"
 
 namespace lmoe {
 
@@ -144,6 +149,71 @@ __global__ __launch_bounds__(PB) void permute_fused_kernel(int npairs, int E, in
   __syncthreads();
   rank_scatter(ids, npairs, E, id_bits(E), 0, s_wcnt, [&](int e) { return s_toff[e]; }, row_to_pair,
                pair_to_row);
+}
+
+// ---- routing + permutation in one workgroup ------------------------------------------------
+template <int KPL, int NP>
+__global__ __launch_bounds__(PB) void route_permute_kernel(int T, int E, int K, const float* __restrict__ logits,
+                                                           const float* __restrict__ bias, float rsf, int renorm,
+                                                           int32_t* ids, float* weights, int tile_m, int max_tiles,
+                                                           int32_t* counts, int32_t* offsets, int32_t* tile_offsets,
+                                                           int32_t* row_to_pair, int32_t* tile_expert,
+                                                           int32_t* pair_to_row) {
+  extern __shared__ int smem[];
+  const int npairs = T * K;
+  int* s_cnt = smem;                      // [E]
+  int* s_toff = s_cnt + E;                // [E]
+  int* s_scr = s_toff + E;                // [PW]
+  int* s_ids = s_scr + PW;                // [T * K]
+  unsigned short* s_wcnt = (unsigned short*)(s_ids + npairs);   // [PW * E]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < E; e += PB) s_cnt[e] = 0;
+  if (w < T) {                            // whole wavefronts: token w
+    int e;
+    float wt;
+    route_token<KPL, NP>(w, E, K, logits, bias, rsf, renorm, &e, &wt);
+    if (lane < K) {
+      ids[(size_t)w * K + lane] = e;
+      weights[(size_t)w * K + lane] = wt;
+      s_ids[w * K + lane] = e;
+    }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < npairs) atomicAdd(&s_cnt[s_ids[threadIdx.x]], 1);
+  __syncthreads();
+  scan_experts(s_cnt, E, tile_m, max_tiles, counts, offsets, tile_offsets, row_to_pair, tile_expert,
+               s_scr, s_toff);
+  __syncthreads();
+  rank_scatter(s_ids, npairs, E, id_bits(E), 0, s_wcnt, [&](int e) { return s_toff[e]; }, row_to_pair,
+               pair_to_row);
+}
+
+bool route_permute_fusable(int T, int K) { return T <= PW && T * K <= PB; }
+
+hipError_t launch_route_permute(int T, int E, int K, const float* logits, const float* bias, float rsf,
+                                int renorm, int32_t* ids, float* weights, int tile_m, int max_tiles,
+                                int32_t* counts, int32_t* offsets, int32_t* tile_offsets, int32_t* row_to_pair,
+                                int32_t* tile_expert, int32_t* pair_to_row, void* workspace,
+                                hipStream_t stream) {
+  if (!route_permute_fusable(T, K)) {
+    hipError_t err = launch_route(T, E, K, logits, bias, rsf, renorm, ids, weights, stream);
+    if (err != hipSuccess) return err;
+    return launch_permute(T * K, E, tile_m, max_tiles, ids, counts, offsets, tile_offsets, row_to_pair,
+                          tile_expert, pair_to_row, workspace, stream);
+  }
+  const size_t sm = (size_t)(2 * E + PW + T * K) * sizeof(int) + (size_t)PW * E * sizeof(unsigned short);
+#define LMOE_RP(KPL, NP)                                                                                    \
+  hipLaunchKernelGGL((route_permute_kernel<KPL, NP>), dim3(1), dim3(PB), sm, stream, T, E, K, logits, bias, \
+                     rsf, renorm, ids, weights, tile_m, max_tiles, counts, offsets, tile_offsets, row_to_pair, \
+                     tile_expert, pair_to_row)
+  if (E <= 64) LMOE_RP(1, 1);
+  else if (E <= 128) LMOE_RP(2, 2);
+  else if (E <= 256) LMOE_RP(4, 4);
+  else if (E <= 512) LMOE_RP(8, 8);
+  else if (E <= 896) LMOE_RP(14, 16);
+  else LMOE_RP(16, 16);
+#undef LMOE_RP
+  return hipGetLastError();
 }
 
 // ---- several blocks ------------------------------------------------------------------------

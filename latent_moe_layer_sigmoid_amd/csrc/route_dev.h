@@ -1,0 +1,113 @@
+// Device routine of single-group sigmoid top-k routing for gfx950, shared by the routing
+// kernel and the fused routing + permutation kernel. The method and the data layout are
+// described in route.hip.
+#pragma once
+#include "common.h"
+
+namespace lmoe {
+
+LMOE_DEV uint32_t orderable(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Maximum of x over the 64 lanes, returned as a wave-uniform value.
+// Row shifts 1, 2, 4, 8 leave each row's maximum in its lane 15; two row broadcasts
+// carry it to lane 63. Lanes reading outside their row see 0, the identity here.
+LMOE_DEV uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true));   // row_shr:1
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true));   // row_shr:2
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true));   // row_shr:4
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true));   // row_shr:8
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+LMOE_DEV void cas_desc(uint64_t& a, uint64_t& b) {
+  const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+  a = hi;
+  b = lo;
+}
+
+// Batcher's odd-even merge sort of N (a power of two) keys, descending; fully unrolled.
+template <int N>
+LMOE_DEV void sort_desc(uint64_t* k) {
+#pragma unroll
+  for (int p = 1; p < N; p <<= 1)
+#pragma unroll
+    for (int q = p; q >= 1; q >>= 1)
+#pragma unroll
+      for (int j = q % p; j + q < N; j += 2 * q)
+#pragma unroll
+        for (int i = 0; i < q; ++i)
+          if (i + j + q < N && (i + j) / (2 * p) == (i + j + q) / (2 * p)) cas_desc(k[i + j], k[i + j + q]);
+}
+
+LMOE_DEV float score_of(float logit) { return __builtin_amdgcn_rcpf(1.0f + __expf(-logit)); }
+
+// Routes token t with the calling wavefront: lane k < K returns expert *e and weight *w of
+// slot k (other lanes return e = -1). Every lane of the wavefront must call it.
+template <int KPL, int NP>   // keys per lane, padded to the power of two NP
+LMOE_DEV void route_token(int t, int E, int K, const float* __restrict__ logits, const float* __restrict__ bias,
+                          float rsf, int renorm, int* e_out, float* w_out) {
+  const int lane = threadIdx.x & 63;
+  const float* row = logits + (size_t)t * E;
+
+  // issue every load before the first use (clamped, in-bounds indices), then build keys
+  float lg[KPL], bs[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int e = min(lane + 64 * j, E - 1);
+    lg[j] = row[e];
+    bs[j] = bias ? bias[e] : 0.0f;
+  }
+  uint64_t key[NP];
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int e = lane + 64 * j;
+    key[j] = 0;   // below every real key; never selected since K <= E
+    if (j < KPL && e < E) {
+      const float kap = score_of(lg[j]) + bs[j];
+      key[j] = ((uint64_t)orderable(kap) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+    }
+  }
+  sort_desc<NP>(key);
+
+  uint32_t my_lo = 0;
+  float my_lg = 0.0f;
+  for (int k = 0; k < K; ++k) {
+    const uint32_t hh = (uint32_t)(key[0] >> 32), ll = (uint32_t)key[0];
+    const uint32_t mh = wave_max_u32(hh);
+    const uint32_t ml = wave_max_u32(hh == mh ? ll : 0u);
+    if (hh == mh && ll == ml) {   // the unique winning lane pops its head
+#pragma unroll
+      for (int j = 0; j + 1 < NP; ++j) key[j] = key[j + 1];
+      key[NP - 1] = 0;
+    }
+    // the winner's logit, from the registers of lane (e % 64), slot e / 64 (e is uniform)
+    const uint32_t ew = 0xFFFFFFFFu - ml;
+    const int jw = (int)(ew >> 6);
+    float pick = lg[0];
+#pragma unroll
+    for (int j = 1; j < KPL; ++j) pick = (j == jw) ? lg[j] : pick;
+    const float lw = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pick), (int)(ew & 63)));
+    if (lane == k) {
+      my_lo = ml;
+      my_lg = lw;
+    }
+  }
+  int e = -1;
+  float s = 0.0f;
+  if (lane < K) {
+    e = (int)(0xFFFFFFFFu - my_lo);
+    s = score_of(my_lg);   // same expression as at selection time
+  }
+  float sum = s;            // butterfly: every lane ends with the same total
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) sum += __shfl_xor(sum, off, WAVE);
+  *e_out = e;
+  *w_out = renorm ? rsf * s / sum : rsf * s;
+}
+
+}  // namespace lmoe

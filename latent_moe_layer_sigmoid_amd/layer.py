@@ -129,50 +129,65 @@ class LatentMoELayer:
         if self.shared_stream:
             return self._forward_two_streams(X, b, stream, mark)
         if self.fused:
-            # a1 router GEMM, a3 latent down projection, a10 shared FC1 + SituGLU: one launch
+            # router GEMM, latent down projection, shared FC1 + SituGLU: one launch
             mark("front")
             B.lmoe_linear_multi(T, s.H, dt, X, 3, [s.E, s.L, s.I], [w["W_r"], w["W_down"], w["W_s1"]],
                                 [B.LMOE_F32, dt, dt], [b["logits"], b["x"], b["act_s"]], [0, 0, 1], s.beta,
                                 s.linear_beta, stream)
         else:
-            # a1 router GEMM -> fp32 logits, a3 latent down projection
+            # router GEMM -> fp32 logits, latent down projection
             mark("router")
             B.lmoe_linear(T, s.E, s.H, dt, X, dt, w["W_r"], B.LMOE_F32, b["logits"], stream)
             mark("down")
             B.lmoe_linear(T, s.L, s.H, dt, X, dt, w["W_down"], dt, b["x"], stream)
-        # a2 routing, a5 permutation, (a4) a6-a9 routed experts
-        self._routed(X, b, stream, mark)
+        # routing, permutation, routed experts (fused: FC2 also leaves the normalized latent)
+        self._routed(X, b, stream, mark, norm=self.fused)
         if self.fused:
-            # a10 shared FC2 folded into a11 + a12: RMSNorm, then one GEMM over both K ranges
+            # shared expert's FC2 folded into the up projection: one GEMM over both K ranges
             mark("tail")
-            B.lmoe_tail_shared(T, s.L, s.H, s.I, b["z"], w["gamma"], s.eps, w["W_up"], b["act_s"], w["W_s2"], dt,
+            B.lmoe_tail_shared(T, s.L, s.H, s.I, None, w["gamma"], s.eps, w["W_up"], b["act_s"], w["W_s2"], dt,
                                b["out"], b["n"], stream)
         else:
-            # a10 shared expert (dense mode: E = K = 1)
+            # shared expert (dense mode: E = K = 1)
             mark("shared_fc1")
             B.lmoe_fc1_situ(T, 1, 1, s.H, s.I, 16, dt, X, None, None, None, dt, w["W_s1"], None, s.beta,
                             s.linear_beta, dt, b["act_s"], None, T, stream)
             mark("shared_fc2")
             B.lmoe_fc2_combine(T, 1, 1, s.I, s.H, 16, dt, b["act_s"], None, None, None, dt, w["W_s2"], None, None,
                                dt, b["sh"], T, None, 0, stream)
-            # a11 + a12 latent RMSNorm, up projection with the shared add in its epilogue
+            # latent RMSNorm, up projection with the shared add in its epilogue
             mark("tail")
             B.lmoe_tail(T, s.L, s.H, b["z"], w["gamma"], s.eps, w["W_up"], b["sh"], dt, b["out"], b["n"], stream)
         mark(None)
         return b["out"]
 
-    def _routed(self, X, b, stream, mark):
-        """Routing, permutation and the routed experts (a2, a4-a9) on `stream`."""
+    def capture(self, X):
+        """A HIP graph of one forward pass on the static input X (same buffers as
+        forward(X)); graph.replay() reruns the whole layer, reading X's current contents.
+        The library records no memset and allocates nothing, so every launch is a kernel
+        node; the shared-expert stream, if used, is forked and joined inside the graph."""
+        cur = torch.cuda.current_stream(self.device)
+        warm = torch.cuda.Stream(self.device)
+        warm.wait_stream(cur)
+        with torch.cuda.stream(warm):
+            self.forward(X)               # buffers exist before capture
+        cur.wait_stream(warm)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.forward(X)
+        return graph
+
+    def _routed(self, X, b, stream, mark, norm=False):
+        """Routing, permutation and the routed experts on `stream`; with norm, the FC2 call
+        also leaves the RMS-normalized latent in b["n"] (combine and RMSNorm in one kernel)."""
         s, w = self.s, self.w
         T = X.shape[0]
         dt = _lmoe_dtype(s.dtype)
         rc = b["rows_cap"]
-        mark("route")
-        B.lmoe_route(T, s.E, s.K, b["logits"], w["bias"], s.rsf, 1, b["ids"], b["weights"], stream)
-        mark("permute")
-        B.lmoe_permute(T, s.E, s.K, s.tile_m, b["ids"], b["counts"], b["offsets"], b["tile_offsets"],
-                       b["row_to_pair"], b["tile_expert"], b["pair_to_row"], rc, b["perm_ws"],
-                       b["perm_ws_bytes"], stream)
+        mark("route_permute")
+        B.lmoe_route_permute(T, s.E, s.K, b["logits"], w["bias"], s.rsf, 1, b["ids"], b["weights"], s.tile_m,
+                             b["counts"], b["offsets"], b["tile_offsets"], b["row_to_pair"], b["tile_expert"],
+                             b["pair_to_row"], rc, b["perm_ws"], b["perm_ws_bytes"], stream)
         if s.experts == "mx":
             mark("quant")
             B.lmoe_quant_mxfp8(T, s.L, dt, b["x"], b["xq"], b["xs"], stream)
@@ -180,19 +195,22 @@ class LatentMoELayer:
             B.lmoe_fc1_situ(T, s.E, s.K, s.L, s.d, s.tile_m, B.LMOE_MXFP8_E4M3, b["xq"], b["xs"], b["row_to_pair"],
                             b["tile_expert"], B.LMOE_MXFP4_E2M1, w["W1_codes"], w["W1_scales"], s.beta,
                             s.linear_beta, B.LMOE_MXFP8_E4M3, b["act"], b["act_scale"], rc, stream)
-            mark("fc2")
-            B.lmoe_fc2_combine(T, s.E, s.K, s.d, s.L, s.tile_m, B.LMOE_MXFP8_E4M3, b["act"], b["act_scale"],
-                               b["row_to_pair"], b["tile_expert"], B.LMOE_MXFP4_E2M1, w["W2_codes"],
-                               w["W2_scales"], b["weights"], B.LMOE_F32, b["z"], rc, b["fc2_ws"],
-                               b["fc2_ws_bytes"], stream)
+            a_dt, a, a_s, w2_dt, w2, w2_s = (B.LMOE_MXFP8_E4M3, b["act"], b["act_scale"], B.LMOE_MXFP4_E2M1,
+                                             w["W2_codes"], w["W2_scales"])
         else:
             mark("fc1")
             B.lmoe_fc1_situ(T, s.E, s.K, s.L, s.d, s.tile_m, dt, b["x"], None, b["row_to_pair"], b["tile_expert"],
                             dt, w["W1"], None, s.beta, s.linear_beta, dt, b["act"], None, rc, stream)
-            mark("fc2")
-            B.lmoe_fc2_combine(T, s.E, s.K, s.d, s.L, s.tile_m, dt, b["act"], None, b["row_to_pair"],
-                               b["tile_expert"], dt, w["W2"], None, b["weights"], B.LMOE_F32, b["z"], rc,
-                               b["fc2_ws"], b["fc2_ws_bytes"], stream)
+            a_dt, a, a_s, w2_dt, w2, w2_s = dt, b["act"], None, dt, w["W2"], None
+        mark("fc2")
+        if norm:
+            B.lmoe_fc2_combine_norm(T, s.E, s.K, s.d, s.L, s.tile_m, a_dt, a, a_s, b["row_to_pair"], b["tile_expert"],
+                                    w2_dt, w2, w2_s, b["weights"], b["z"], rc, b["fc2_ws"], b["fc2_ws_bytes"],
+                                    w["gamma"], s.eps, dt, b["n"], stream)
+        else:
+            B.lmoe_fc2_combine(T, s.E, s.K, s.d, s.L, s.tile_m, a_dt, a, a_s, b["row_to_pair"], b["tile_expert"],
+                               w2_dt, w2, w2_s, b["weights"], B.LMOE_F32, b["z"], rc, b["fc2_ws"], b["fc2_ws_bytes"],
+                               stream)
 
     def _forward_two_streams(self, X, b, stream, mark):
         """Main stream: router GEMM + down projection (one launch), routing, permutation,
@@ -207,7 +225,8 @@ class LatentMoELayer:
         start = torch.cuda.Event()
         start.record(main)
         side.wait_event(start)            # X is ready and the previous call's tail has read sh
-        X.record_stream(side)
+        if not torch.cuda.is_current_stream_capturing():
+            X.record_stream(side)
         B.lmoe_fc1_situ(T, 1, 1, s.H, s.I, 16, dt, X, None, None, None, dt, w["W_s1"], None, s.beta,
                         s.linear_beta, dt, b["act_s"], None, T, side)
         B.lmoe_fc2_combine(T, 1, 1, s.I, s.H, 16, dt, b["act_s"], None, None, None, dt, w["W_s2"], None, None,
@@ -217,10 +236,10 @@ class LatentMoELayer:
         mark("front")
         B.lmoe_linear_multi(T, s.H, dt, X, 2, [s.E, s.L], [w["W_r"], w["W_down"]], [B.LMOE_F32, dt],
                             [b["logits"], b["x"]], None, s.beta, s.linear_beta, main)
-        self._routed(X, b, main, mark)
+        self._routed(X, b, main, mark, norm=True)
         main.wait_event(shared_done)
         mark("tail")
-        B.lmoe_tail(T, s.L, s.H, b["z"], w["gamma"], s.eps, w["W_up"], b["sh"], dt, b["out"], b["n"], main)
+        B.lmoe_tail(T, s.L, s.H, None, w["gamma"], s.eps, w["W_up"], b["sh"], dt, b["out"], b["n"], main)
         mark(None)
         return b["out"]
 

@@ -137,6 +137,53 @@ def test_permute_matches_oracle(B, T, E, K, tile_m, skew):
     assert np.array_equal(got["row_to_pair"][got["pair_to_row"]], np.arange(T * K))
 
 
+@pytest.mark.parametrize("T,E,K,tile_m", [(4, 16, 4, 16), (8, 896, 16, 16), (16, 896, 16, 16), (17, 896, 16, 16),
+                                           (1, 8, 8, 16), (8, 1024, 64, 32), (64, 256, 16, 128), (300, 896, 16, 128)])
+def test_route_permute_matches_oracle(B, T, E, K, tile_m):
+    """One call = routing then permutation: fused into one workgroup for T <= 16 and
+    T*K <= 1024, two kernels otherwise; both bit-exact against the oracle."""
+    cfg = LI.scaled(LI.ROUTE_MASKED, T=T, E=E, K=K)
+    if K == 64:
+        cfg = LI.scaled(cfg, logit_var=0.25)
+    logits, bias, _ = guarded_route_logits(cfg, seed=2000 + T + E + K, max_rounds=400)
+    rc = B.lmoe_permute_rows_cap(T, E, K, tile_m)
+    wsb = B.lmoe_permute_workspace_bytes(T, E, K)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    ids = torch.full((T, K), -7, **i32)
+    w = torch.full((T, K), float("nan"), dtype=torch.float32, device=DEV)
+    o = dict(counts=torch.full((E,), -9, **i32), offsets=torch.full((E + 1,), -9, **i32),
+             tile_offsets=torch.full((E + 1,), -9, **i32), row_to_pair=torch.full((rc,), -9, **i32),
+             tile_expert=torch.full((rc // tile_m,), -9, **i32), pair_to_row=torch.full((T * K,), -9, **i32))
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=DEV)
+    B.lmoe_route_permute(T, E, K, logits.to(DEV), bias.to(DEV), cfg.rsf, 1, ids, w, tile_m, o["counts"], o["offsets"],
+                         o["tile_offsets"], o["row_to_pair"], o["tile_expert"], o["pair_to_row"], rc, ws, wsb)
+    torch.cuda.synchronize()
+    rid, rw, _ = oracle.route(logits.double().numpy(), bias.double().numpy(), K, cfg.rsf)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=1e-5, atol=0)
+    ref = oracle.permute(rid, E, tile_m)
+    got = {k: v.cpu().numpy() for k, v in o.items()}
+    nrows = int(ref["tile_offsets"][E])
+    for k in ("counts", "offsets", "tile_offsets", "pair_to_row"):
+        assert np.array_equal(got[k], ref[k]), k
+    assert np.array_equal(got["row_to_pair"][:nrows], ref["row_to_pair"])
+    assert np.array_equal(got["tile_expert"], tile_expert_from_offsets(ref["tile_offsets"], tile_m, rc // tile_m))
+
+
+def test_route_permute_empty_and_checks(B):
+    i32 = dict(dtype=torch.int32, device=DEV)
+    z = torch.zeros(64, **i32)
+    f = torch.zeros(64, dtype=torch.float32, device=DEV)
+    # T == 0: success, nothing written, pointers not needed
+    B.lmoe_route_permute(0, 16, 4, None, None, 1.0, 1, None, None, 16, None, None, None, None, None, None, 0, None, 0)
+    with pytest.raises(B.LmoeError) as ei:   # rows_cap too small
+        B.lmoe_route_permute(2, 16, 4, f, None, 1.0, 1, z, f, 16, z, z, z, z, z, z, 16, None, 0)
+    assert ei.value.status == B.LMOE_ERR_WORKSPACE
+    with pytest.raises(B.LmoeError) as ei:   # K > E
+        B.lmoe_route_permute(2, 4, 8, f, None, 1.0, 1, z, f, 16, z, z, z, z, z, z, 256, None, 0)
+    assert ei.value.status == B.LMOE_ERR_INVALID_ARG
+
+
 def test_permute_capacity_checks(B):
     ids = torch.zeros(4, 2, dtype=torch.int32, device=DEV)
     z = torch.zeros(64, dtype=torch.int32, device=DEV)
@@ -336,6 +383,54 @@ def test_fc1_fc2_grouped_match_oracle(B, T, E, K, L, d, tile_m, dt):
             y = oracle.linear(a64[p2r[t * K + k]][None, :], W2_64[e])[0]
             ref_z[t] += c["w"][t, k].astype(np.float64) * y
     assert norm_err(f64(z), oracle.f32_round(ref_z)) <= 1e-4
+
+
+@pytest.mark.parametrize("T,E,K,L,d,tile_m,dt", [(8, 64, 16, 2048, 512, 16, "bf16"), (4, 16, 4, 128, 64, 16, "f32"),
+                                                 (300, 16, 2, 256, 128, 128, "bf16"), (5, 1, 1, 256, 128, 16, "bf16")])
+def test_fc2_combine_norm_matches_two_calls_and_oracle(B, T, E, K, L, d, tile_m, dt):
+    """FC2 + combine + RMSNorm in one call: z and the normalized latent are bit-identical
+    to lmoe_fc2_combine followed by lmoe_tail's RMSNorm, and within tolerance of the
+    oracle's combine and RMSNorm."""
+    c = _expert_case(B, T, E, K, L, d, tile_m, dt, seed=T + E + 11)
+    ldt = B.LMOE_BF16 if dt == "bf16" else B.LMOE_F32
+    rc = c["rc"]
+    dense = E == 1 and K == 1
+    r2p, te = (None, None) if dense else (c["r2p"], c["te"])
+    rcap = T if dense else rc
+    rng = np.random.default_rng(T + 5)
+    act_in = torch.from_numpy(rng.standard_normal((rcap, d))).to(c["td"]).to(DEV)
+    W2p = B.packed(c["W2"].to(DEV))
+    wts = torch.from_numpy(c["w"]).to(DEV)
+    gamma = torch.from_numpy(rng.uniform(0.9, 1.1, L)).to(c["td"]).to(DEV)
+    wsb = B.lmoe_fc2_workspace_bytes(T, K, L)
+    ws = torch.empty(max(wsb // 4, 1), device=DEV)
+    z1 = torch.full((T, L), float("nan"), device=DEV)
+    B.lmoe_fc2_combine(T, E, K, d, L, tile_m, ldt, act_in, None, r2p, te, ldt, W2p, None, wts, B.LMOE_F32, z1, rcap,
+                       ws, wsb)
+    n1 = torch.empty(T, L, dtype=c["td"], device=DEV)
+    out = torch.empty(T, 16, dtype=c["td"], device=DEV)
+    w_up = B.packed(torch.zeros(16, L, dtype=c["td"], device=DEV))
+    B.lmoe_tail(T, L, 16, z1, gamma, 1e-6, w_up, None, ldt, out, n1)
+    z2 = torch.full((T, L), float("nan"), device=DEV)
+    n2 = torch.full((T, L), float("nan"), dtype=c["td"], device=DEV)
+    B.lmoe_fc2_combine_norm(T, E, K, d, L, tile_m, ldt, act_in, None, r2p, te, ldt, W2p, None, wts, z2, rcap, ws, wsb,
+                            gamma, 1e-6, ldt, n2)
+    torch.cuda.synchronize()
+    assert torch.equal(z1.view(torch.int32), z2.view(torch.int32))
+    assert torch.equal(n1.view(torch.int16) if dt == "bf16" else n1.view(torch.int32),
+                       n2.view(torch.int16) if dt == "bf16" else n2.view(torch.int32))
+    # oracle: combine of the expert products, then RMSNorm
+    a64, W2_64 = f64(act_in), f64(c["W2"])
+    p2r = np.arange(T) if dense else c["perm"]["pair_to_row"]
+    ref_z = np.zeros((T, L))
+    for t in range(T):
+        for k in range(K):
+            e = 0 if dense else c["ids"][t, k]
+            y = oracle.linear(a64[p2r[t * K + k]][None, :], W2_64[e])[0]
+            ref_z[t] += c["w"][t, k].astype(np.float64) * y
+    ref_z = oracle.f32_round(ref_z)
+    assert norm_err(f64(z2), ref_z) <= 1e-4
+    assert norm_err(f64(n2), oracle.round_to(oracle.rmsnorm(ref_z, f64(gamma), 1e-6), dt)) <= 1e-2
 
 
 # ------------------------------------------------------------------ MX (MXFP8 x MXFP4) experts

@@ -120,3 +120,28 @@ def test_layer_mx_full_size_sampled_tokens():
 def test_layer_prefill_full_size_sampled_tokens():
     cfg = LI.PREFILL
     check_layer(cfg, 4, tokens=[0, 1, 2, 4095, 8190, 8191])
+
+
+@pytest.mark.parametrize("shared_stream", [False, True])
+def test_layer_decode_graph_replays_match_eager(shared_stream):
+    """A captured graph of the decode layer, replayed several times with eager work and
+    synchronizations in between, reproduces the eager output bit for bit every time."""
+    cfg = LI.DECODE
+    layer, _ = build_layer(cfg, 2, shared_stream=shared_stream)
+    w_cpu = LI.make_layer_weights(cfg, 2, device="cpu", experts=False)
+    o = oracle_weights(cfg, 2, w_cpu)
+    X, _ = guarded_x(cfg, 2, o["W_r"], o["bias"])
+    X2 = LI.make_x(cfg, 77)
+    Xs = X.to(DEV).clone()
+    eager = layer.forward(Xs).clone()
+    eager2 = layer.forward(X2.to(DEV)).clone()
+    torch.cuda.synchronize()
+    graph = layer.capture(Xs)
+    for r in range(4):
+        Xs.copy_(X.to(DEV) if r % 2 == 0 else X2.to(DEV))
+        graph.replay()
+        torch.cuda.synchronize()
+        want = eager if r % 2 == 0 else eager2
+        assert torch.equal(layer.buffers(cfg.T)["out"].view(torch.int16), want.view(torch.int16)), f"replay {r}"
+        layer.forward(X2.to(DEV))           # eager work between replays
+        torch.cuda.synchronize()
