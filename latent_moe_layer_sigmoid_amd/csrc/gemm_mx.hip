@@ -11,12 +11,13 @@
 // B) covers K block [32g, 32g + 32). Loading A that way makes the hardware K order the
 // natural one, so the MX blocks of the data line up with the scales.
 //
-// Grouped expert tiles of 16 rows, one wavefront per (tile, column block), NT tiles of
-// 16 columns per wave. A pipeline step is 256 K elements = two scaled MFMAs: per lane
-// 2 x 32 fp8 bytes of its activation row (row-major) and, per weight tile, 2 x 16 bytes
-// of packed e2m1 codes (one contiguous 1 KB per wave-wide load; layout written by
-// lmoe_pack_mxfp4_weights) plus one dword holding the lane's four weight scales of the
-// 512-wide stage.
+// Grouped expert tiles of 16 rows (or 32 when the permutation's tile is a multiple of 32:
+// two row groups then share every weight fragment, halving weight traffic per row), one
+// wavefront per (tile, column block), NT tiles of 16 columns per wave. A pipeline step is
+// 256 K elements = two scaled MFMAs per row group: per lane 2 x 32 fp8 bytes of each
+// activation row (row-major) and, per weight tile, 2 x 16 bytes of packed e2m1 codes (one
+// contiguous 1 KB per wave-wide load; layout written by lmoe_pack_mxfp4_weights) plus one
+// dword holding the lane's four weight scales of the 512-wide stage.
 // Epilogues: SituGLU on the fp32 accumulators followed by MXFP8 requantization of each
 // 32 consecutive outputs (2 gate tiles x 16 lanes share one block: amax by butterfly
 // over the 16 lanes), or the weighted per-pair store of FC2.
@@ -25,20 +26,20 @@
 
 namespace lmoe {
 
-template <int NT>
+template <int NT, int R>
 struct MxStep {
-  uint4 a[4];        // A codes: MFMA u uses a[2u] (K 16g..) and a[2u+1] (K 64+16g..)
-  uint32_t sa[2];    // A scales (byte in bits 0..7)
+  uint4 a[R][4];     // A codes of row group r: MFMA u uses a[r][2u] (K 16g..) and a[r][2u+1] (K 64+16g..)
+  uint32_t sa[R][2]; // A scales (byte in bits 0..7)
   uint4 b[NT][2];    // B codes: MFMA u uses b[j][u] (16 bytes = 32 e2m1)
   uint32_t sb[NT];   // B scales of the stage: byte q = 2h + u
 };
 
-template <int NT>
+template <int NT, int R>
 __global__ __launch_bounds__(64) void stream_gemm_mx_kernel(const StreamGemm g, int blocks_total, int nsteps) {
   const int lane = threadIdx.x & 63;
   const int mt = blockIdx.x / blocks_total;
   const int nb = blockIdx.x - mt * blocks_total;
-  const int row0 = mt * 16;
+  const int row0 = mt * 16 * R;   // R row groups of 16 share every weight fragment
   if (row0 >= g.M) return;
   const Seg sg = g.seg[0];
   const bool situ = sg.epi == Epi::SITU_MX;
@@ -49,10 +50,11 @@ __global__ __launch_bounds__(64) void stream_gemm_mx_kernel(const StreamGemm g, 
   const int Kd = g.Kd;
   const int nst = Kd / 512;
 
-  int pair_a = g.row_to_pair[row0 + m];
-  int pair_o[4];
+  int pair_o[R][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) pair_o[i] = g.row_to_pair[row0 + 4 * g4 + i];
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pair_o[r][i] = g.row_to_pair[row0 + 16 * r + 4 * g4 + i];
 
   // weight tiles (packed codes and scales of expert e)
   const int half = NT / 2;
@@ -68,27 +70,35 @@ __global__ __launch_bounds__(64) void stream_gemm_mx_kernel(const StreamGemm g, 
     n16[j] = (uint32_t)(n0 / 16);
   }
 
-  const uint64_t valid = __ballot(pair_a >= 0);
-  if (valid == 0) return;
-  const int src = __ffsll((unsigned long long)valid) - 1;
-  const int fill = __shfl(pair_a, src, WAVE);
-  const int p = pair_a >= 0 ? pair_a : fill;
-  const int r = pair_a >= 0 ? row0 + m : row0 + src;
-  const int arow = g.a_by_row ? r : p / g.topk;
+  // activation rows: a pad row reads the tile's first row; a tile whose first row is a pad
+  // holds only pads (pads close each expert's segment)
+  const int first = g.row_to_pair[row0];
+  if (first < 0) return;
   const rsrc_t ac_rs = make_rsrc(g.a, g.a_bytes);
   const rsrc_t as_rs = make_rsrc(g.a_scale, g.a_scale_bytes);
-  const uint32_t ac_off = (uint32_t)arow * (uint32_t)Kd + g4 * 16;
-  const uint32_t as_off = (uint32_t)arow * (uint32_t)(Kd / 32) + g4;
+  uint32_t ac_off[R], as_off[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int pa = g.row_to_pair[row0 + 16 * r + m];
+    const bool real = pa >= 0;
+    const int arow = g.a_by_row ? (real ? row0 + 16 * r + m : row0) : (real ? pa : first) / g.topk;
+    ac_off[r] = (uint32_t)arow * (uint32_t)Kd + g4 * 16;
+    as_off[r] = (uint32_t)arow * (uint32_t)(Kd / 32) + g4;
+  }
 
-  auto issue = [&](int t, MxStep<NT>& st) {
+  auto issue = [&](int t, MxStep<NT, R>& st) {
     const int s = t >> 1, h = t & 1;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int q = 2 * h + u;
       const uint32_t ko = (uint32_t)(s * 512 + q * 128);
-      st.a[2 * u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ac_rs, ac_off, ko, 0));
-      st.a[2 * u + 1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ac_rs, ac_off + 64, ko, 0));
-      st.sa[u] = __builtin_amdgcn_raw_buffer_load_b8(as_rs, as_off, (uint32_t)(s * 16 + q * 4), 0);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        st.a[r][2 * u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ac_rs, ac_off[r], ko, 0));
+        st.a[r][2 * u + 1] =
+            __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ac_rs, ac_off[r] + 64, ko, 0));
+        st.sa[r][u] = __builtin_amdgcn_raw_buffer_load_b8(as_rs, as_off[r], (uint32_t)(s * 16 + q * 4), 0);
+      }
 #pragma unroll
       for (int j = 0; j < NT; ++j)
         st.b[j][u] = __builtin_bit_cast(
@@ -99,29 +109,34 @@ __global__ __launch_bounds__(64) void stream_gemm_mx_kernel(const StreamGemm g, 
       st.sb[j] = __builtin_amdgcn_raw_buffer_load_b32(ws_rs, lane * 4, (n16[j] * nst + s) * 256u, 0);
   };
 
-  floatx4 acc[NT];
+  floatx4 acc[R][NT];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[r][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  auto consume = [&](int t, const MxStep<NT>& st) {
+  auto consume = [&](int t, const MxStep<NT, R>& st) {
     const int h = t & 1;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const intx8 av = {(int)st.a[2 * u].x,     (int)st.a[2 * u].y,     (int)st.a[2 * u].z,
-                        (int)st.a[2 * u].w,     (int)st.a[2 * u + 1].x, (int)st.a[2 * u + 1].y,
-                        (int)st.a[2 * u + 1].z, (int)st.a[2 * u + 1].w};
-      const int sa = (int)(st.sa[u] & 0xFFu);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const intx8 bv = {(int)st.b[j][u].x, (int)st.b[j][u].y, (int)st.b[j][u].z, (int)st.b[j][u].w, 0, 0, 0, 0};
-        const int sb = (int)((st.sb[j] >> (8 * (2 * h + u))) & 0xFFu);
-        acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[j], 0, 4, 0, sa, 0, sb);
+      for (int r = 0; r < R; ++r) {
+        const intx8 av = {(int)st.a[r][2 * u].x,     (int)st.a[r][2 * u].y,     (int)st.a[r][2 * u].z,
+                          (int)st.a[r][2 * u].w,     (int)st.a[r][2 * u + 1].x, (int)st.a[r][2 * u + 1].y,
+                          (int)st.a[r][2 * u + 1].z, (int)st.a[r][2 * u + 1].w};
+        const int sa = (int)(st.sa[r][u] & 0xFFu);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const intx8 bv = {(int)st.b[j][u].x, (int)st.b[j][u].y, (int)st.b[j][u].z, (int)st.b[j][u].w, 0, 0, 0, 0};
+          const int sb = (int)((st.sb[j] >> (8 * (2 * h + u))) & 0xFFu);
+          acc[r][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[r][j], 0, 4, 0, sa, 0, sb);
+        }
       }
     }
   };
 
   {
-    MxStep<NT> s0, s1;
+    MxStep<NT, R> s0, s1;
     issue(0, s0);
     int t = 0;
     while (true) {
@@ -138,46 +153,50 @@ __global__ __launch_bounds__(64) void stream_gemm_mx_kernel(const StreamGemm g, 
     }
   }
 
-  // ---- epilogue: lane holds rows row0 + 4*g4 + i, column (tile j) ... + m
-  if (situ) {
-    const float inv_b = 1.0f / g.beta;
-    const float inv_lb = g.lbeta > 0.0f ? 1.0f / g.lbeta : 0.0f;
-    const int nblk = sg.n_out / 32;
+  // ---- epilogue: row group r, lane holds rows row0 + 16 r + 4*g4 + i, column (tile j) ... + m
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int orow = row0 + 4 * g4 + i;
-      float v[half];
-      float amax = 0.0f;
+  for (int r = 0; r < R; ++r) {
+    if (situ) {
+      const float inv_b = 1.0f / g.beta;
+      const float inv_lb = g.lbeta > 0.0f ? 1.0f / g.lbeta : 0.0f;
+      const int nblk = sg.n_out / 32;
 #pragma unroll
-      for (int j = 0; j < half; ++j) {
-        v[j] = situ_f(acc[j][i], acc[j + half][i], g.beta, inv_b, g.lbeta, inv_lb);
-        amax = fmaxf(amax, fabsf(v[j]));
+      for (int i = 0; i < 4; ++i) {
+        const int orow = row0 + 16 * r + 4 * g4 + i;
+        float v[half];
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < half; ++j) {
+          v[j] = situ_f(acc[r][j][i], acc[r][j + half][i], g.beta, inv_b, g.lbeta, inv_lb);
+          amax = fmaxf(amax, fabsf(v[j]));
+        }
+        // one MX block = the 32 columns of this wave (NT/2 == 2 gate tiles x 16 lanes)
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, WAVE));
+        const int X = mx_e4m3_exponent(amax);
+        if (pair_o[r][i] < 0) continue;
+        uint8_t* act = reinterpret_cast<uint8_t*>(sg.out) + (size_t)orow * sg.ldo;
+#pragma unroll
+        for (int j = 0; j < half; ++j)
+          act[nb * half * 16 + j * 16 + m] = (uint8_t)e4m3_encode(__builtin_ldexpf(v[j], -X));
+        if (m == 0) g.out_scale[(size_t)orow * nblk + nb] = (uint8_t)(X + 127);
       }
-      // one MX block = the 32 columns of this wave (NT/2 == 2 gate tiles x 16 lanes)
+    } else {
 #pragma unroll
-      for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, WAVE));
-      const int X = mx_e4m3_exponent(amax);
-      if (pair_o[i] < 0) continue;
-      uint8_t* act = reinterpret_cast<uint8_t*>(sg.out) + (size_t)orow * sg.ldo;
+      for (int i = 0; i < 4; ++i) {
+        const int pair = pair_o[r][i];
+        if (pair < 0) continue;
+        const float wgt = g.pair_w ? g.pair_w[pair] : 1.0f;
 #pragma unroll
-      for (int j = 0; j < half; ++j) act[nb * half * 16 + j * 16 + m] = (uint8_t)e4m3_encode(__builtin_ldexpf(v[j], -X));
-      if (m == 0) g.out_scale[(size_t)orow * nblk + nb] = (uint8_t)(X + 127);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int pair = pair_o[i];
-      if (pair < 0) continue;
-      const float wgt = g.pair_w ? g.pair_w[pair] : 1.0f;
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const int col = nb * NT * 16 + j * 16 + m;
-        if (sg.epi == Epi::PAIR)
-          reinterpret_cast<float*>(sg.out)[(size_t)pair * sg.ldo + col] = wgt * acc[j][i];
-        else if (sg.out_elt == Elt::F32)   // TOKEN (K == 1)
-          reinterpret_cast<float*>(sg.out)[(size_t)(pair / g.topk) * sg.ldo + col] = wgt * acc[j][i];
-        else
-          reinterpret_cast<uint16_t*>(sg.out)[(size_t)(pair / g.topk) * sg.ldo + col] = f32_to_bf16(wgt * acc[j][i]);
+        for (int j = 0; j < NT; ++j) {
+          const int col = nb * NT * 16 + j * 16 + m;
+          if (sg.epi == Epi::PAIR)
+            reinterpret_cast<float*>(sg.out)[(size_t)pair * sg.ldo + col] = wgt * acc[r][j][i];
+          else if (sg.out_elt == Elt::F32)   // TOKEN (K == 1)
+            reinterpret_cast<float*>(sg.out)[(size_t)(pair / g.topk) * sg.ldo + col] = wgt * acc[r][j][i];
+          else
+            reinterpret_cast<uint16_t*>(sg.out)[(size_t)(pair / g.topk) * sg.ldo + col] = f32_to_bf16(wgt * acc[r][j][i]);
+        }
       }
     }
   }
@@ -186,7 +205,10 @@ __global__ __launch_bounds__(64) void stream_gemm_mx_kernel(const StreamGemm g, 
 hipError_t launch_stream_gemm_mx(StreamGemm g, int live, hipStream_t stream) {
   (void)live;
   const int nsteps = g.Kd / 256;
-  const int m_tiles = (g.M + 15) / 16;
+  // 32 rows per wavefront when expert tiles are a multiple of 32 rows (each weight fragment
+  // then feeds two scaled MFMAs), else 16
+  const int R = g.tile_m % 32 == 0 ? 2 : 1;
+  const int m_tiles = (g.M + 16 * R - 1) / (16 * R);
   // SituGLU + requant needs 32 gate columns per wave (one MX block): 2 gate + 2 up tiles.
   constexpr int NT = 4;
   const int tiles = g.seg[0].n_out / 16;
@@ -194,8 +216,12 @@ hipError_t launch_stream_gemm_mx(StreamGemm g, int live, hipStream_t stream) {
   g.seg[0].blocks = blocks;
   g.seg[0].block0 = 0;
   g.nseg = 1;
-  hipLaunchKernelGGL((stream_gemm_mx_kernel<NT>), dim3((unsigned)(m_tiles * blocks)), dim3(64), 0, stream, g, blocks,
-                     nsteps);
+  if (R == 2)
+    hipLaunchKernelGGL((stream_gemm_mx_kernel<NT, 2>), dim3((unsigned)(m_tiles * blocks)), dim3(64), 0, stream, g,
+                       blocks, nsteps);
+  else
+    hipLaunchKernelGGL((stream_gemm_mx_kernel<NT, 1>), dim3((unsigned)(m_tiles * blocks)), dim3(64), 0, stream, g,
+                       blocks, nsteps);
   return hipGetLastError();
 }
 

@@ -58,7 +58,7 @@ PREFILL = LayerConfig(
 MX = LayerConfig(
     name="mx_experts", T=1024, H=7168, L=2048, E=896, K=16, d=512, I=4096, dtype="bf16",
     experts="mx", beta=1.0, linear_beta=0.0, rsf=2.5, bias_range=0.05,
-    logit_var=2.0, tile_m=16,
+    logit_var=2.0, tile_m=32,
     notes="expert weights MXFP4 (e2m1 + e8m0 per 32 along K); activations MXFP8 e4m3")
 
 CONFIGS = {c.name: c for c in (TINY, DECODE, ROUTE_MASKED, PREFILL, MX)}

@@ -385,6 +385,35 @@ def test_fc1_fc2_grouped_match_oracle(B, T, E, K, L, d, tile_m, dt):
     assert norm_err(f64(z), oracle.f32_round(ref_z)) <= 1e-4
 
 
+def test_fc2_combine_wide_short_k(B):
+    """FC2 with many short-K work items (the decode regime) over 33 column blocks of 64,
+    the last one partial, against the oracle's weighted combine."""
+    T, E, K, d, out_dim, tile_m = 256, 32, 8, 128, 2064, 16
+    rng = np.random.default_rng(9)
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    wts = rng.random((T, K)).astype(np.float32) + 0.1
+    perm = oracle.permute(ids, E, tile_m)
+    rc = B.lmoe_permute_rows_cap(T, E, K, tile_m)
+    r2p = torch.from_numpy(np.concatenate([perm["row_to_pair"], np.full(rc - len(perm["row_to_pair"]), -1)])
+                           .astype(np.int32)).to(DEV)
+    te = torch.from_numpy(tile_expert_from_offsets(perm["tile_offsets"], tile_m, rc // tile_m).astype(np.int32)).to(DEV)
+    act = torch.from_numpy(rng.standard_normal((rc, d))).to(torch.bfloat16)
+    W2 = torch.from_numpy(rng.standard_normal((E, out_dim, d)) / math.sqrt(d)).to(torch.bfloat16)
+    z = torch.full((T, out_dim), float("nan"), device=DEV)
+    wsb = B.lmoe_fc2_workspace_bytes(T, K, out_dim)
+    ws = torch.empty(max(wsb // 4, 1), device=DEV)
+    B.lmoe_fc2_combine(T, E, K, d, out_dim, tile_m, B.LMOE_BF16, act.to(DEV), None, r2p, te, B.LMOE_BF16,
+                       B.packed(W2.to(DEV)), None, torch.from_numpy(wts).to(DEV), B.LMOE_F32, z, rc, ws, wsb)
+    torch.cuda.synchronize()
+    a64, W2_64 = f64(act), f64(W2)
+    ref = np.zeros((T, out_dim))
+    p2r = perm["pair_to_row"]
+    for t in range(T):
+        for k in range(K):
+            ref[t] += wts[t, k].astype(np.float64) * (W2_64[ids[t, k]] @ a64[p2r[t * K + k]])
+    assert norm_err(f64(z), oracle.f32_round(ref)) <= 1e-4
+
+
 @pytest.mark.parametrize("T,E,K,L,d,tile_m,dt", [(8, 64, 16, 2048, 512, 16, "bf16"), (4, 16, 4, 128, 64, 16, "f32"),
                                                  (300, 16, 2, 256, 128, 128, "bf16"), (5, 1, 1, 256, 128, 16, "bf16")])
 def test_fc2_combine_norm_matches_two_calls_and_oracle(B, T, E, K, L, d, tile_m, dt):
@@ -474,7 +503,8 @@ def _mx_weights(rng, E, N, Kd):
     return codes, scales
 
 
-@pytest.mark.parametrize("T,E,K,L,d,tile_m", [(24, 8, 4, 1024, 512, 16), (40, 16, 8, 512, 512, 32)])
+@pytest.mark.parametrize("T,E,K,L,d,tile_m", [(24, 8, 4, 1024, 512, 16), (40, 16, 8, 512, 512, 32),
+                                             (50, 8, 4, 512, 512, 64)])
 def test_fc1_fc2_mx_match_oracle(B, T, E, K, L, d, tile_m):
     rng = np.random.default_rng(T + E)
     ids = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
