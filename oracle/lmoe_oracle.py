@@ -227,6 +227,63 @@ def route(logits, bias, K, rsf, renormalize=True):
     return ids, f32_round(w), s + b[None, :]
 
 
+def route_grouped(logits, bias, K, rsf, n_group, topk_group, renormalize=True):
+    """Grouped DeepSeekV3 top-k routing, the general case that single-group routing
+    specializes ([P1] commit 1: n_group == topk_group == 1 is the degenerate case of the
+    grouped kernels; commit 4: sigmoid + grouped-topk with bias and group counts). The
+    pages give no formula; the reading taken is DeepSeek-V3's published rule:
+
+      kappa = fp32(fp32(sigmoid(logits)) + bias), experts cut into n_group contiguous
+      groups of E / n_group; a group's score is the fp32 sum of its two largest kappa
+      (its only kappa when groups hold one expert); the topk_group groups with the highest
+      scores are kept (ties -> lower group index); ids are the K largest kappa among the
+      kept groups' experts (ties -> lower expert index), in descending order; weights as
+      in route() from the unbiased scores.
+
+    Returns ids int32 [T, K], weights (fp32 values) [T, K], group scores [T, n_group]."""
+    logits = np.asarray(logits, dtype=np.float64)
+    T, E = logits.shape
+    assert E % n_group == 0 and 1 <= topk_group <= n_group
+    gs = E // n_group
+    assert K <= topk_group * gs
+    b = np.zeros(E) if bias is None else np.asarray(bias, dtype=np.float64)
+    s = sigmoid(logits)
+    kappa32 = f32_round(f32_round(s) + b[None, :])
+    grp = kappa32.reshape(T, n_group, gs)
+    top = -np.sort(-grp, axis=2)
+    gscore = f32_round(top[:, :, 0] + top[:, :, 1]) if gs > 1 else top[:, :, 0]
+    gidx = np.broadcast_to(np.arange(n_group), (T, n_group))
+    gorder = np.lexsort((gidx, -gscore), axis=-1)
+    keep = np.zeros((T, n_group), dtype=bool)
+    np.put_along_axis(keep, gorder[:, :topk_group], True, axis=1)
+    cand = np.repeat(keep, gs, axis=1)
+    masked = np.where(cand, kappa32, -np.inf)
+    idx = np.broadcast_to(np.arange(E), (T, E))
+    order = np.lexsort((idx, -masked), axis=-1)
+    ids = order[:, :K].astype(np.int32)
+    sel = np.take_along_axis(s, ids.astype(np.int64), axis=1)
+    w = rsf * sel / np.sum(sel, axis=1, keepdims=True) if renormalize else rsf * sel
+    return ids, f32_round(w), gscore
+
+
+def route_renormalize(logits, K):
+    """The "Renormalize" routing method ([P1] commit 4: on that path the logits are cast
+    to BF16 and no bias, group counts or routed scaling factor are used; [P2] "Test
+    Coverage": Renormalize routing next to the DeepSeekV3 method). Reading taken: the
+    K largest bf16 logits (ties -> lower expert index), in descending order, weighted by
+    the softmax of the selected logits.
+
+    Returns ids int32 [T, K], weights (fp32 values) [T, K]."""
+    lb = bf16_round(np.asarray(logits, dtype=np.float64))
+    T, E = lb.shape
+    idx = np.broadcast_to(np.arange(E), (T, E))
+    order = np.lexsort((idx, -lb), axis=-1)
+    ids = order[:, :K].astype(np.int32)
+    sel = np.take_along_axis(lb, ids.astype(np.int64), axis=1)
+    ex = np.exp(sel - sel[:, :1])
+    return ids, f32_round(ex / np.sum(ex, axis=1, keepdims=True))
+
+
 def permute(ids, E, tile_m):
     """Expert-sorted permutation of the (token, slot) pairs ([P2] "Commit 1": the
     routing workspace that FC1 / FC2 / finalize read, computed for the runner's tile).
@@ -389,6 +446,26 @@ def layer_forward(X, W_r, bias, W_down, W1, W2, W_s1, W_s2, gamma, W_up, *,
     if mx:
         res.update(actq=actq, acts=acts)
     return res
+
+
+def grouped_gaps_ok(kappa, gscore, K, n_group, topk_group, min_gap=1e-4):
+    """Per token: True when the group decision and the expert decision are both clear:
+    adjacent gaps among the topk_group + 1 largest group scores, and among the K + 1
+    largest keys of the kept groups' experts, are at least min_gap."""
+    kappa = np.asarray(kappa, dtype=np.float64)
+    gscore = np.asarray(gscore, dtype=np.float64)
+    T, E = kappa.shape
+    gs = E // n_group
+    gtop = -np.sort(-gscore, axis=1)[:, :topk_group + 1]
+    ok = np.all(gtop[:, :-1] - gtop[:, 1:] >= min_gap, axis=1) if topk_group < n_group else np.ones(T, bool)
+    gidx = np.broadcast_to(np.arange(n_group), (T, n_group))
+    gorder = np.lexsort((gidx, -gscore), axis=-1)
+    keep = np.zeros((T, n_group), dtype=bool)
+    np.put_along_axis(keep, gorder[:, :topk_group], True, axis=1)
+    masked = np.where(np.repeat(keep, gs, axis=1), kappa, -np.inf)
+    top = -np.sort(-masked, axis=1)[:, :K + 1]
+    gaps = top[:, :-1] - top[:, 1:]
+    return ok & np.all(np.where(np.isfinite(gaps), gaps, np.inf) >= min_gap, axis=1)
 
 
 def kappa_gaps_ok(kappa, K, min_gap=1e-4):

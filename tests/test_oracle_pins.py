@@ -289,6 +289,97 @@ def _brute_force_topk(kappa_row, K):
     return res
 
 
+def _read_routing_golden(name):
+    d = dict(logits={}, ids={}, w={}, gscore={})
+    for ln in lines(name):
+        f = ln.split()
+        if f[0] in ("K", "n_group", "topk_group"):
+            d[f[0]] = int(f[1])
+        elif f[0] == "rsf":
+            d["rsf"] = float(f[1])
+        elif f[0] == "bias":
+            d["bias"] = np.array([float(x) for x in f[1:]], dtype=np.float32).astype(np.float64)
+        elif f[0] == "logit":
+            d["logits"][int(f[1])] = f[2:]
+        elif f[0] == "ids":
+            d["ids"][int(f[1])] = [int(x) for x in f[2:]]
+        elif f[0] in ("w", "gscore"):
+            d[f[0]][int(f[1])] = [float(frac(x)) if "/" in x or x.isdigit() else float(x) for x in f[2:]]
+    return d
+
+
+def test_route_grouped_golden_rational_example():
+    d = _read_routing_golden("grouped_routing.txt")
+    L = oracle.f32_round(np.array([_rational_logits(d["logits"][t]) for t in sorted(d["logits"])]))
+    ids, w, gscore = oracle.route_grouped(L, d["bias"], d["K"], d["rsf"], d["n_group"], d["topk_group"])
+    for t in sorted(d["logits"]):
+        assert list(ids[t]) == d["ids"][t]
+        np.testing.assert_allclose(w[t], d["w"][t], rtol=1e-6)
+        np.testing.assert_allclose(gscore[t], d["gscore"][t], rtol=1e-6)
+    # the group stage matters here: plain top-3 picks differently
+    plain, _, _ = oracle.route(L, d["bias"], d["K"], d["rsf"])
+    assert list(plain[0]) != d["ids"][0] and list(plain[1]) != d["ids"][1]
+
+
+def test_route_grouped_reduces_to_single_group():
+    rng = np.random.default_rng(21)
+    lg = rng.standard_normal((40, 64)) * 1.4
+    b = rng.uniform(-0.05, 0.05, 64)
+    ids, w, _ = oracle.route(lg, b, 8, 2.5)
+    for n_group in (1, 4, 8):   # one group, or every group kept
+        gi, gw, _ = oracle.route_grouped(lg, b, 8, 2.5, n_group, n_group)
+        assert np.array_equal(gi, ids) and np.array_equal(gw, w)
+
+
+@pytest.mark.parametrize("trial", range(20))
+def test_route_grouped_matches_brute_force(trial):
+    """Group choice and expert choice by enumeration of all subsets (tiny E)."""
+    rng = np.random.default_rng(300 + trial)
+    n_group, gs = int(rng.integers(2, 5)), int(rng.integers(1, 4))
+    E = n_group * gs
+    topk_group = int(rng.integers(1, n_group + 1))
+    K = int(rng.integers(1, topk_group * gs + 1))
+    lg = oracle.f32_round(rng.standard_normal((1, E)) * 2)
+    b = np.array(rng.uniform(-0.1, 0.1, E), dtype=np.float32).astype(np.float64)
+    ids, _, gscore = oracle.route_grouped(lg, b, K, 1.0, n_group, topk_group)
+    kap = oracle.f32_round(oracle.f32_round(oracle.sigmoid(lg[0])) + b)
+    # group scores: the two largest members, by pairwise enumeration
+    for g in range(n_group):
+        mem = kap[g * gs:(g + 1) * gs]
+        best = max(mem) if gs == 1 else max(oracle.f32_round(mem[i] + mem[j])
+                                             for i, j in itertools.combinations(range(gs), 2))
+        assert gscore[0, g] == best
+    kept = _brute_force_topk(gscore[0], topk_group)
+    cand = [e for e in range(E) if e // gs in kept]
+    sub = _brute_force_topk(kap[cand], K)
+    assert list(ids[0]) == [cand[i] for i in sub]
+
+
+def test_route_renormalize_golden():
+    d = _read_routing_golden("renormalize_routing.txt")
+    L = np.array([[float(x) for x in d["logits"][t]] for t in sorted(d["logits"])])
+    ids, w = oracle.route_renormalize(L, d["K"])
+    for t in sorted(d["logits"]):
+        assert list(ids[t]) == d["ids"][t]
+        np.testing.assert_allclose(w[t], d["w"][t], rtol=1e-7)
+
+
+def test_route_renormalize_invariants():
+    rng = np.random.default_rng(5)
+    lg = oracle.f32_round(rng.standard_normal((50, 96)) * 2)
+    ids, w = oracle.route_renormalize(lg, 6)
+    np.testing.assert_allclose(w.sum(1), 1.0, rtol=1e-6)
+    lb = oracle.bf16_round(lg)
+    # ids: the top-6 of the bf16 logits by a stable sort; weights: the full softmax renormalized
+    assert np.array_equal(ids, np.argsort(-lb, axis=1, kind="stable")[:, :6])
+    full = np.exp(lb - lb.max(1, keepdims=True))
+    full /= full.sum(1, keepdims=True)
+    sel = np.take_along_axis(full, ids.astype(np.int64), axis=1)
+    np.testing.assert_allclose(w, sel / sel.sum(1, keepdims=True), rtol=1e-6)
+    i1, w1 = oracle.route_renormalize(lg, 1)
+    assert np.all(w1 == 1.0) and np.array_equal(i1[:, 0], np.argmax(lb, axis=1))
+
+
 @pytest.mark.parametrize("trial", range(60))
 def test_route_matches_brute_force_with_ties(trial):
     rng = np.random.default_rng(trial)
