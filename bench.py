@@ -78,21 +78,30 @@ def fc1_traffic(cfg, seed):
 
 
 def route_microbench(torch, B, LI, reps=200):
+    """lmoe_route at T=1024, E=896, K=16 (us per call, algorithmic bytes), plus the grouped
+    (8 groups, 4 kept) and Renormalize methods on the same logits."""
     cfg = LI.ROUTE_MASKED
     logits = LI.make_route_logits(cfg, 3, device="cuda")
     bias = LI.make_bias(cfg, 3, device="cuda")
     ids = torch.empty(cfg.T, cfg.K, dtype=torch.int32, device="cuda")
     w = torch.empty(cfg.T, cfg.K, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
-    for _ in range(20):
-        B.lmoe_route(cfg.T, cfg.E, cfg.K, logits, bias, cfg.rsf, 1, ids, w)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(reps):
-        B.lmoe_route(cfg.T, cfg.E, cfg.K, logits, bias, cfg.rsf, 1, ids, w)
-    b.record(stream)
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) * 1000.0 / reps
+    calls = {
+        "sigmoid": lambda: B.lmoe_route(cfg.T, cfg.E, cfg.K, logits, bias, cfg.rsf, 1, ids, w),
+        "grouped_8_4": lambda: B.lmoe_route_grouped(cfg.T, cfg.E, cfg.K, 8, 4, logits, bias, cfg.rsf, 1, ids, w),
+        "renormalize": lambda: B.lmoe_route_renormalize(cfg.T, cfg.E, cfg.K, logits, ids, w),
+    }
+    us = {}
+    for name, call in calls.items():
+        for _ in range(20):
+            call()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        us[name] = a.elapsed_time(b) * 1000.0 / reps
     nbytes = cfg.T * cfg.E * 4 + cfg.E * 4 + cfg.T * cfg.K * 8
     return us, nbytes
 
@@ -226,8 +235,9 @@ def main():
         f"layer bytes={lb / 1e6:.1f}MB")
     log("per-step us: " + ", ".join(f"{k}={v * 1e3:.1f}" for k, v in dur.items()))
 
-    route_us, route_bytes = route_microbench(torch, B, LI)
-    log(f"route T=1024: {route_us:.2f} us/call")
+    route_all, route_bytes = route_microbench(torch, B, LI)
+    route_us = route_all["sigmoid"]
+    log("route T=1024 us/call: " + ", ".join(f"{k}={v:.2f}" for k, v in route_all.items()))
 
     res = {
         "metric": METRIC,
@@ -254,6 +264,7 @@ def main():
                       "frac": round(lb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "route_us_per_call": round(route_us, 3),
         "route_hbm_frac": round(route_bytes / (route_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 5),
+        "route_other_us_per_call": {k: round(v, 3) for k, v in route_all.items() if k != "sigmoid"},
         "step_us": {k: round(v * 1e3, 2) for k, v in dur.items()},
     }
     if not args.no_cpu_baseline:

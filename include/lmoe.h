@@ -127,6 +127,31 @@ lmoe_status lmoe_route(int T, int E, int K, const float* logits, const float* bi
                        float routed_scaling_factor, int renormalize,
                        int32_t* topk_ids, float* topk_weights, hipStream_t stream);
 
+/* Grouped top-k routing, the general case of lmoe_route ([P1] commit 1: n_group ==
+ * topk_group == 1 is the degenerate case of the grouped kernels; [P1] commit 4: sigmoid +
+ * grouped top-k with the selection bias, group counts and routed scaling factor). The
+ * pages give no formula; this follows DeepSeek-V3's rule: with key = sigmoid(logit) +
+ * bias (fp32), the E experts form n_group contiguous groups of E / n_group; a group's
+ * score is the fp32 sum of its two largest keys (its only key for groups of one); the
+ * topk_group groups with the highest scores are kept (ties -> lower group index);
+ * topk_ids are the K largest keys among the kept groups' experts (ties -> lower expert
+ * index, slot order descending) and topk_weights are formed as in lmoe_route.
+ * n_group == 1 (or topk_group == n_group) gives exactly lmoe_route. Requirements:
+ * 1 <= n_group <= 64, E % n_group == 0, 1 <= topk_group <= n_group,
+ * K <= topk_group * (E / n_group), plus those of lmoe_route. */
+lmoe_status lmoe_route_grouped(int T, int E, int K, int n_group, int topk_group, const float* logits,
+                               const float* bias, float routed_scaling_factor, int renormalize,
+                               int32_t* topk_ids, float* topk_weights, hipStream_t stream);
+
+/* "Renormalize" routing ([P1] commit 4: on this path the logits are cast to BF16 and no
+ * bias, group counts or routed scaling factor are used; [P2] "Test Coverage": Renormalize
+ * next to the DeepSeekV3 method). The fp32 logits are rounded to bf16 (nearest even);
+ * topk_ids[t, k] = expert with the k-th largest bf16 logit (ties -> lower expert index);
+ * topk_weights[t, k] = softmax of the K selected bf16 logits (fp32). 1 <= K <= min(E, 64),
+ * E <= 1024. */
+lmoe_status lmoe_route_renormalize(int T, int E, int K, const float* logits, int32_t* topk_ids,
+                                   float* topk_weights, hipStream_t stream);
+
 /* a5 -- stable expert-sorted permutation of the T*K (token, slot) pairs, pair p = t*K + k
  * ([P2] "Commit 1": the routing workspace that FC1 / FC2 / finalize read, computed for
  * the tile the runner reports). Outputs (all int32, caller-allocated):

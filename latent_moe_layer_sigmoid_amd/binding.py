@@ -37,6 +37,8 @@ SIGNATURES = [
     ("lmoe_linear", _i, [_i, _i, _i, _i, _p, _i, _p, _i, _p, _p]),
     ("lmoe_linear_multi", _i, [_i, _i, _i, _p, _i, _p, _p, _p, _p, _p, _f, _f, _p]),
     ("lmoe_route", _i, [_i, _i, _i, _p, _p, _f, _i, _p, _p, _p]),
+    ("lmoe_route_grouped", _i, [_i, _i, _i, _i, _i, _p, _p, _f, _i, _p, _p, _p]),
+    ("lmoe_route_renormalize", _i, [_i, _i, _i, _p, _p, _p, _p]),
     ("lmoe_permute_workspace_bytes", _z, [_i, _i, _i]),
     ("lmoe_permute_rows_cap", _i, [_i, _i, _i, _i]),
     ("lmoe_permute", _i, [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _i, _p, _z, _p]),
@@ -156,6 +158,18 @@ def lmoe_linear_multi(M, Kd, x_dtype, x, n_proj, N, w, y_dtype, y, situ, beta, l
 def lmoe_route(T, E, K, logits, bias, routed_scaling_factor, renormalize, topk_ids, topk_weights, stream=None):
     _check("lmoe_route", lib().lmoe_route(T, E, K, _ptr(logits), _ptr(bias), float(routed_scaling_factor),
                                           int(renormalize), _ptr(topk_ids), _ptr(topk_weights), _stream(stream)))
+
+
+def lmoe_route_grouped(T, E, K, n_group, topk_group, logits, bias, routed_scaling_factor, renormalize, topk_ids,
+                       topk_weights, stream=None):
+    _check("lmoe_route_grouped", lib().lmoe_route_grouped(T, E, K, n_group, topk_group, _ptr(logits), _ptr(bias),
+                                                          float(routed_scaling_factor), int(renormalize),
+                                                          _ptr(topk_ids), _ptr(topk_weights), _stream(stream)))
+
+
+def lmoe_route_renormalize(T, E, K, logits, topk_ids, topk_weights, stream=None):
+    _check("lmoe_route_renormalize", lib().lmoe_route_renormalize(T, E, K, _ptr(logits), _ptr(topk_ids),
+                                                                  _ptr(topk_weights), _stream(stream)))
 
 
 def lmoe_permute_workspace_bytes(T, E, K):

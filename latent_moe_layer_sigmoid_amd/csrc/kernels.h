@@ -79,6 +79,12 @@ hipError_t launch_permute(int npairs, int E, int tile_m, int max_tiles, const in
                           int32_t* offsets, int32_t* tile_offsets, int32_t* row_to_pair, int32_t* tile_expert,
                           int32_t* pair_to_row, void* workspace, hipStream_t stream);
 
+hipError_t launch_route_renormalize(int T, int E, int K, const float* logits, int32_t* ids, float* weights,
+                                    hipStream_t stream);
+hipError_t launch_route_grouped(int T, int E, int K, int n_group, int topk_group, const float* logits,
+                                const float* bias, float rsf, int renorm, int32_t* ids, float* weights,
+                                hipStream_t stream);
+
 // Routing then permutation (one workgroup when route_permute_fusable(T, K)).
 bool route_permute_fusable(int T, int K);
 hipError_t launch_route_permute(int T, int E, int K, const float* logits, const float* bias, float rsf,

@@ -141,6 +141,31 @@ lmoe_status lmoe_route(int T, int E, int K, const float* logits, const float* bi
   return hip_status(launch_route(T, E, K, logits, bias, rsf, renormalize, topk_ids, topk_weights, stream));
 }
 
+lmoe_status lmoe_route_grouped(int T, int E, int K, int n_group, int topk_group, const float* logits,
+                               const float* bias, float rsf, int renormalize, int32_t* topk_ids, float* topk_weights,
+                               hipStream_t stream) {
+  if (T < 0 || E < 1 || K < 1 || K > E || K > 64 || !isfinite(rsf)) return LMOE_ERR_INVALID_ARG;
+  if (n_group < 1 || n_group > 64 || E % n_group != 0 || topk_group < 1 || topk_group > n_group ||
+      K > topk_group * (E / n_group))
+    return LMOE_ERR_INVALID_ARG;
+  if (E > 1024) return LMOE_ERR_UNSUPPORTED;
+  if (T == 0) return LMOE_OK;
+  if (!logits || !topk_ids || !topk_weights) return LMOE_ERR_INVALID_ARG;
+  if (n_group == 1 || topk_group == n_group)   // every expert competes: single-group routing
+    return hip_status(launch_route(T, E, K, logits, bias, rsf, renormalize, topk_ids, topk_weights, stream));
+  return hip_status(launch_route_grouped(T, E, K, n_group, topk_group, logits, bias, rsf, renormalize, topk_ids,
+                                         topk_weights, stream));
+}
+
+lmoe_status lmoe_route_renormalize(int T, int E, int K, const float* logits, int32_t* topk_ids, float* topk_weights,
+                                   hipStream_t stream) {
+  if (T < 0 || E < 1 || K < 1 || K > E || K > 64) return LMOE_ERR_INVALID_ARG;
+  if (E > 1024) return LMOE_ERR_UNSUPPORTED;
+  if (T == 0) return LMOE_OK;
+  if (!logits || !topk_ids || !topk_weights) return LMOE_ERR_INVALID_ARG;
+  return hip_status(launch_route_renormalize(T, E, K, logits, topk_ids, topk_weights, stream));
+}
+
 size_t lmoe_permute_workspace_bytes(int T, int E, int K) {
   if (T <= 0 || E < 1 || K < 1) return 0;
   return permute_workspace_bytes((int)((long)T * K), E);

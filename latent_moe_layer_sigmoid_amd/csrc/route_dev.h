@@ -46,11 +46,25 @@ LMOE_DEV void sort_desc(uint64_t* k) {
 
 LMOE_DEV float score_of(float logit) { return __builtin_amdgcn_rcpf(1.0f + __expf(-logit)); }
 
+// Selection key of one expert: METHOD 0 (sigmoid scores with the selection bias, [P1]
+// commit 4) gives sigmoid(logit) + bias; METHOD 1 ("Renormalize": logits cast to bf16,
+// no bias) gives the bf16 value of the logit.
+template <int METHOD>
+LMOE_DEV float route_key(float logit, float bias) {
+  if (METHOD == 0) return score_of(logit) + bias;
+  return bf16_to_f32(f32_to_bf16(logit));
+}
+
 // Routes token t with the calling wavefront: lane k < K returns expert *e and weight *w of
 // slot k (other lanes return e = -1). Every lane of the wavefront must call it.
-template <int KPL, int NP>   // keys per lane, padded to the power of two NP
+// group_size > 0: only experts whose group (e / group_size) has its bit set in the
+// wave-uniform keep_groups mask compete (grouped top-k).
+// Weights: METHOD 0 -- rsf * s / sum(s) over the K winners' unbiased scores (or rsf * s
+// without renorm); METHOD 1 -- softmax of the K winners' bf16 logits.
+template <int KPL, int NP, int METHOD = 0>
 LMOE_DEV void route_token(int t, int E, int K, const float* __restrict__ logits, const float* __restrict__ bias,
-                          float rsf, int renorm, int* e_out, float* w_out) {
+                          float rsf, int renorm, int* e_out, float* w_out, int group_size = 0,
+                          uint64_t keep_groups = ~0ull) {
   const int lane = threadIdx.x & 63;
   const float* row = logits + (size_t)t * E;
 
@@ -60,15 +74,16 @@ LMOE_DEV void route_token(int t, int E, int K, const float* __restrict__ logits,
   for (int j = 0; j < KPL; ++j) {
     const int e = min(lane + 64 * j, E - 1);
     lg[j] = row[e];
-    bs[j] = bias ? bias[e] : 0.0f;
+    bs[j] = (METHOD == 0 && bias) ? bias[e] : 0.0f;
   }
   uint64_t key[NP];
 #pragma unroll
   for (int j = 0; j < NP; ++j) {
     const int e = lane + 64 * j;
-    key[j] = 0;   // below every real key; never selected since K <= E
-    if (j < KPL && e < E) {
-      const float kap = score_of(lg[j]) + bs[j];
+    key[j] = 0;   // below every real key; never selected since K <= the competing experts
+    const bool competes = e < E && (group_size <= 0 || ((keep_groups >> (e / max(group_size, 1))) & 1ull));
+    if (j < KPL && competes) {
+      const float kap = route_key<METHOD>(lg[j], bs[j]);
       key[j] = ((uint64_t)orderable(kap) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
     }
   }
@@ -99,15 +114,28 @@ LMOE_DEV void route_token(int t, int E, int K, const float* __restrict__ logits,
   }
   int e = -1;
   float s = 0.0f;
-  if (lane < K) {
-    e = (int)(0xFFFFFFFFu - my_lo);
-    s = score_of(my_lg);   // same expression as at selection time
+  if (METHOD == 0) {
+    if (lane < K) {
+      e = (int)(0xFFFFFFFFu - my_lo);
+      s = score_of(my_lg);   // same expression as at selection time
+    }
+  } else {
+    // softmax over the winners: slot 0 holds the largest bf16 logit
+    const float v = route_key<1>(my_lg, 0.0f);
+    const float vmax = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    if (lane < K) {
+      e = (int)(0xFFFFFFFFu - my_lo);
+      s = __expf(v - vmax);
+    }
   }
   float sum = s;            // butterfly: every lane ends with the same total
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) sum += __shfl_xor(sum, off, WAVE);
   *e_out = e;
-  *w_out = renorm ? rsf * s / sum : rsf * s;
+  if (METHOD == 0)
+    *w_out = renorm ? rsf * s / sum : rsf * s;
+  else
+    *w_out = s / sum;
 }
 
 }  // namespace lmoe

@@ -28,6 +28,9 @@ class LayerShape:
     rsf: float
     eps: float
     tile_m: int = 16
+    routing: str = "sigmoid"   # "sigmoid" (bias-corrected, DeepSeekV3) or "renormalize"
+    n_group: int = 1          # grouped top-k for sigmoid routing
+    topk_group: int = 1
 
 
 def _lmoe_dtype(dtype):
@@ -185,9 +188,19 @@ class LatentMoELayer:
         dt = _lmoe_dtype(s.dtype)
         rc = b["rows_cap"]
         mark("route_permute")
-        B.lmoe_route_permute(T, s.E, s.K, b["logits"], w["bias"], s.rsf, 1, b["ids"], b["weights"], s.tile_m,
-                             b["counts"], b["offsets"], b["tile_offsets"], b["row_to_pair"], b["tile_expert"],
-                             b["pair_to_row"], rc, b["perm_ws"], b["perm_ws_bytes"], stream)
+        if s.routing == "sigmoid" and s.n_group == 1:
+            B.lmoe_route_permute(T, s.E, s.K, b["logits"], w["bias"], s.rsf, 1, b["ids"], b["weights"], s.tile_m,
+                                 b["counts"], b["offsets"], b["tile_offsets"], b["row_to_pair"], b["tile_expert"],
+                                 b["pair_to_row"], rc, b["perm_ws"], b["perm_ws_bytes"], stream)
+        else:
+            if s.routing == "renormalize":
+                B.lmoe_route_renormalize(T, s.E, s.K, b["logits"], b["ids"], b["weights"], stream)
+            else:
+                B.lmoe_route_grouped(T, s.E, s.K, s.n_group, s.topk_group, b["logits"], w["bias"], s.rsf, 1,
+                                     b["ids"], b["weights"], stream)
+            B.lmoe_permute(T, s.E, s.K, s.tile_m, b["ids"], b["counts"], b["offsets"], b["tile_offsets"],
+                           b["row_to_pair"], b["tile_expert"], b["pair_to_row"], rc, b["perm_ws"],
+                           b["perm_ws_bytes"], stream)
         if s.experts == "mx":
             mark("quant")
             B.lmoe_quant_mxfp8(T, s.L, dt, b["x"], b["xq"], b["xs"], stream)

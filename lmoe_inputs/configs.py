@@ -28,6 +28,9 @@ class LayerConfig:
     x_mean: float = 0.0   # hidden ~ N(x_mean, 1); 0.5 skews the expert histogram
     eps: float = 1e-6
     tile_m: int = 16
+    routing: str = "sigmoid"   # "sigmoid" (bias-corrected, DeepSeekV3) or "renormalize" (bf16 logits, softmax)
+    n_group: int = 1      # grouped top-k (sigmoid routing): expert groups and groups kept
+    topk_group: int = 1
     kind: str = "layer"   # "layer" or "route_masked"
     T_max: int = 0        # masked-activation buffer depth (route_masked only)
     notes: str = field(default="", compare=False)

@@ -389,7 +389,8 @@ def shared_expert(X, W_s1, W_s2, beta, linear_beta, dtype):
 
 def layer_forward(X, W_r, bias, W_down, W1, W2, W_s1, W_s2, gamma, W_up, *,
                   K, rsf, beta, linear_beta, eps, dtype, mx=False,
-                  W1_scales=None, W2_scales=None, renormalize=True):
+                  W1_scales=None, W2_scales=None, renormalize=True,
+                  routing="sigmoid", n_group=1, topk_group=1):
     """One latent-MoE layer forward for the token rows in X ([P2] "Description" step
     order: router GEMM, latent down projection, input quantization, routing, FC1 /
     FC2, then the routed reduction with RMSNorm and the latent up projection; [P1]
@@ -398,13 +399,21 @@ def layer_forward(X, W_r, bias, W_down, W1, W2, W_s1, W_s2, gamma, W_up, *,
     X: float64 [T, H] exact input values. W1[e] / W2[e]: per-expert weights, float64
     [2d, L] / [L, d], or (mx=True) packed MXFP4 codes with W1_scales[e] / W2_scales[e].
     Every token's output depends only on its own row, so a subset of tokens can be
-    passed on its own.
+    passed on its own. routing / n_group / topk_group select route_renormalize or
+    route_grouped instead of single-group routing.
 
     Returns a dict of every intermediate the GPU path stores."""
     X = np.asarray(X, dtype=np.float64)
     T = X.shape[0]
     logits = router_logits(X, W_r)                                   # a1
-    ids, w, kappa = route(logits, bias, K, rsf, renormalize)         # a2
+    if routing == "renormalize":                                     # routing
+        ids, w = route_renormalize(logits, K)
+        kappa = None
+    elif n_group > 1:
+        ids, w, _ = route_grouped(logits, bias, K, rsf, n_group, topk_group, renormalize)
+        kappa = None
+    else:
+        ids, w, kappa = route(logits, bias, K, rsf, renormalize)
     x = round_to(linear(X, W_down), dtype)                           # a3
     res = dict(logits=logits, ids=ids, weights=w, kappa=kappa, x=x)
     if mx:                                                           # a4

@@ -78,8 +78,15 @@ def guarded_x(cfg, seed, W_r64, b64, max_rounds=40):
     rows = np.arange(cfg.T)
     for _ in range(max_rounds):
         lg = oracle.router_logits(f64(X[torch.from_numpy(rows)]), W_r64)
-        _, _, kappa = oracle.route(lg, b64, cfg.K, cfg.rsf)
-        ok = oracle.kappa_gaps_ok(kappa, cfg.K, MIN_GAP)
+        if cfg.routing == "renormalize":   # decisions on exactly cast bf16 values: no guard
+            ok = np.ones(len(rows), dtype=bool)
+        elif cfg.n_group > 1:
+            _, _, gsc = oracle.route_grouped(lg, b64, cfg.K, cfg.rsf, cfg.n_group, cfg.topk_group)
+            kappa = oracle.f32_round(oracle.f32_round(oracle.sigmoid(lg)) + b64[None, :])
+            ok = oracle.grouped_gaps_ok(kappa, gsc, cfg.K, cfg.n_group, cfg.topk_group, MIN_GAP)
+        else:
+            _, _, kappa = oracle.route(lg, b64, cfg.K, cfg.rsf)
+            ok = oracle.kappa_gaps_ok(kappa, cfg.K, MIN_GAP)
         rows = rows[~ok]
         if rows.size == 0:
             return X, att
@@ -102,12 +109,24 @@ def oracle_weights(cfg, seed, w_cpu):
     return o
 
 
+def oracle_route(cfg, logits64, b64):
+    """The oracle's routing (ids, weights) for the config's routing method."""
+    if cfg.routing == "renormalize":
+        return oracle.route_renormalize(logits64, cfg.K)
+    if cfg.n_group > 1:
+        ids, w, _ = oracle.route_grouped(logits64, b64, cfg.K, cfg.rsf, cfg.n_group, cfg.topk_group)
+        return ids, w
+    ids, w, _ = oracle.route(logits64, b64, cfg.K, cfg.rsf)
+    return ids, w
+
+
 def run_oracle_layer(cfg, o, X64):
     return oracle.layer_forward(X64, o["W_r"], o["bias"], o["W_down"], o["W1"], o["W2"], o["W_s1"], o["W_s2"],
                                 o["gamma"], o["W_up"], K=cfg.K, rsf=cfg.rsf, beta=cfg.beta,
                                 linear_beta=cfg.linear_beta, eps=cfg.eps, dtype=cfg.dtype,
                                 mx=cfg.experts == "mx", W1_scales=o.get("W1_scales"),
-                                W2_scales=o.get("W2_scales"))
+                                W2_scales=o.get("W2_scales"), routing=cfg.routing, n_group=cfg.n_group,
+                                topk_group=cfg.topk_group)
 
 
 def tile_expert_from_offsets(tile_offsets, tile_m, n_tiles):

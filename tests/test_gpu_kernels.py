@@ -90,6 +90,72 @@ def test_route_deterministic_and_empty(B):
     B.lmoe_route(0, 896, 16, None, None, 1.0, 1, None, None)    # T == 0: no-op
 
 
+
+@pytest.mark.parametrize("T,E,K", [(4, 16, 4), (50, 256, 8), (1024, 896, 16), (9, 1000, 64), (33, 64, 64)])
+def test_route_renormalize_matches_oracle(B, T, E, K):
+    """Renormalize routing: ids bit-exact (decisions on exactly cast bf16 logits, ties to
+    the lower index on both sides), softmax weights within 1e-5."""
+    cfg = LI.scaled(LI.ROUTE_MASKED, T=T, E=E, K=K)
+    logits = LI.make_route_logits(cfg, 4000 + E + K)
+    ids = torch.full((T, K), -7, dtype=torch.int32, device=DEV)
+    w = torch.full((T, K), float("nan"), device=DEV)
+    B.lmoe_route_renormalize(T, E, K, logits.to(DEV), ids, w)
+    torch.cuda.synchronize()
+    rid, rw = oracle.route_renormalize(logits.double().numpy(), K)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=1e-5, atol=0)
+
+
+def _guarded_grouped_logits(cfg, seed, n_group, topk_group, max_rounds=200):
+    bias = LI.make_bias(cfg, seed)
+    att = torch.zeros(cfg.T, dtype=torch.int64)
+    for _ in range(max_rounds):
+        logits = LI.make_route_logits(cfg, seed, att)
+        lg = logits.double().numpy()
+        _, _, gsc = oracle.route_grouped(lg, bias.double().numpy(), cfg.K, cfg.rsf, n_group, topk_group)
+        kap = oracle.f32_round(oracle.f32_round(oracle.sigmoid(lg)) + bias.double().numpy()[None, :])
+        bad = ~oracle.grouped_gaps_ok(kap, gsc, cfg.K, n_group, topk_group)
+        if not bad.any():
+            return logits, bias
+        att[torch.from_numpy(bad)] += 1
+    raise RuntimeError("gap guard did not converge")
+
+
+@pytest.mark.parametrize("T,E,K,n_group,topk_group", [(64, 256, 8, 8, 4), (40, 896, 16, 8, 4), (33, 64, 6, 64, 8),
+                                                      (20, 120, 16, 4, 2), (16, 1024, 64, 16, 8), (8, 256, 8, 8, 8),
+                                                      (8, 896, 16, 1, 1)])
+def test_route_grouped_matches_oracle(B, T, E, K, n_group, topk_group):
+    cfg = LI.scaled(LI.ROUTE_MASKED, T=T, E=E, K=K)
+    if K == 64:
+        cfg = LI.scaled(cfg, logit_var=0.25)
+    logits, bias = _guarded_grouped_logits(cfg, 5000 + E + K, n_group, topk_group)
+    ids = torch.full((T, K), -7, dtype=torch.int32, device=DEV)
+    w = torch.full((T, K), float("nan"), device=DEV)
+    B.lmoe_route_grouped(T, E, K, n_group, topk_group, logits.to(DEV), bias.to(DEV), cfg.rsf, 1, ids, w)
+    torch.cuda.synchronize()
+    rid, rw, _ = oracle.route_grouped(logits.double().numpy(), bias.double().numpy(), K, cfg.rsf, n_group,
+                                      topk_group)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=1e-5, atol=0)
+
+
+def test_route_grouped_and_renormalize_checks(B):
+    f = torch.zeros(64, device=DEV)
+    z = torch.zeros(64, dtype=torch.int32, device=DEV)
+    B.lmoe_route_grouped(0, 16, 4, 4, 2, None, None, 1.0, 1, None, None)       # T == 0: no-op
+    B.lmoe_route_renormalize(0, 16, 4, None, None, None)
+    for args, st in [((2, 16, 4, 3, 2), B.LMOE_ERR_INVALID_ARG),    # E % n_group != 0
+                     ((2, 16, 9, 4, 2), B.LMOE_ERR_INVALID_ARG),    # K > topk_group * group size
+                     ((2, 16, 4, 4, 5), B.LMOE_ERR_INVALID_ARG),    # topk_group > n_group
+                     ((2, 2048, 4, 4, 2), B.LMOE_ERR_UNSUPPORTED)]:
+        with pytest.raises(B.LmoeError) as ei:
+            B.lmoe_route_grouped(*args, f, None, 1.0, 1, z, f)
+        assert ei.value.status == st
+    with pytest.raises(B.LmoeError) as ei:
+        B.lmoe_route_renormalize(2, 4, 8, f, z, f)
+    assert ei.value.status == B.LMOE_ERR_INVALID_ARG
+
+
 # --------------------------------------------------------------------------- permutation
 
 def _random_ids(T, E, K, rng, skew=0.0):

@@ -8,7 +8,8 @@ import torch
 
 import lmoe_inputs as LI
 import oracle
-from gpu_helpers import f64, guarded_x, norm_err, oracle_weights, run_oracle_layer, tile_expert_from_offsets
+from gpu_helpers import (f64, guarded_x, norm_err, oracle_route, oracle_weights, run_oracle_layer,
+                         tile_expert_from_offsets)
 
 pytestmark = pytest.mark.gpu
 
@@ -19,7 +20,8 @@ def build_layer(cfg, seed, fused=True, shared_stream=False):
     from latent_moe_layer_sigmoid_amd import LatentMoELayer, LayerShape
     w_dev = LI.make_layer_weights(cfg, seed, device=DEV)
     shape = LayerShape(H=cfg.H, L=cfg.L, E=cfg.E, K=cfg.K, d=cfg.d, I=cfg.I, dtype=cfg.dtype, experts=cfg.experts,
-                       beta=cfg.beta, linear_beta=cfg.linear_beta, rsf=cfg.rsf, eps=cfg.eps, tile_m=cfg.tile_m)
+                       beta=cfg.beta, linear_beta=cfg.linear_beta, rsf=cfg.rsf, eps=cfg.eps, tile_m=cfg.tile_m,
+                       routing=cfg.routing, n_group=cfg.n_group, topk_group=cfg.topk_group)
     return LatentMoELayer(shape, w_dev, fused=fused, shared_stream=shared_stream), w_dev
 
 
@@ -37,7 +39,7 @@ def check_layer(cfg, seed, tokens=None, out_tol=1e-2, fused=True, shared_stream=
 
     # routing and permutation for every token: bit-exact
     logits_all = oracle.router_logits(f64(X), o["W_r"])
-    ids_all, w_all, _ = oracle.route(logits_all, o["bias"], cfg.K, cfg.rsf)
+    ids_all, w_all = oracle_route(cfg, logits_all, o["bias"])
     assert np.array_equal(b["ids"].cpu().numpy(), ids_all)
     np.testing.assert_allclose(b["weights"].cpu().numpy(), w_all, rtol=1e-5)
     assert norm_err(b["logits"].cpu().numpy(), logits_all) <= 1e-5
@@ -145,3 +147,14 @@ def test_layer_decode_graph_replays_match_eager(shared_stream):
         assert torch.equal(layer.buffers(cfg.T)["out"].view(torch.int16), want.view(torch.int16)), f"replay {r}"
         layer.forward(X2.to(DEV))           # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("routing,n_group,topk_group", [("renormalize", 1, 1), ("sigmoid", 4, 2)])
+def test_layer_tiny_other_routing_methods(routing, n_group, topk_group):
+    cfg = LI.scaled(LI.TINY, routing=routing, n_group=n_group, topk_group=topk_group)
+    check_layer(cfg, 7)
+
+
+def test_layer_decode_grouped_routing():
+    # DeepSeek-V3-style groups on the decode layer: 896 experts in 8 groups, 4 kept
+    check_layer(LI.scaled(LI.DECODE, n_group=8, topk_group=4), 12)
