@@ -89,7 +89,7 @@ lmoe_status lmoe_pack_weights(int batch, int N, int Kd, lmoe_dtype dtype, const 
 lmoe_status lmoe_pack_mxfp4_weights(int batch, int N, int Kd, const uint8_t* codes_src, const uint8_t* scales_src,
                                     uint8_t* codes_dst, uint8_t* scales_dst, hipStream_t stream);
 
-/* a1 / a3 -- dense projection y[M,N] = x[M,Kd] @ w[N,Kd]^T with fp32 accumulation.
+/* Dense projection (router GEMM, latent down projection) y[M,N] = x[M,Kd] @ w[N,Kd]^T with fp32 accumulation.
  * Used for the router GEMM (y LMOE_F32: [P1] commit 4, DeepSeekV3 routing takes FP32
  * logits; [P2] "Description": the router GEMM runs first) and the latent down projection
  * ([P2] "Description"; [P3] _fused_forward: routed input transform on hidden).
@@ -99,7 +99,7 @@ lmoe_status lmoe_linear(int M, int N, int Kd, lmoe_dtype x_dtype, const void* x,
                         lmoe_dtype w_dtype, const void* w, lmoe_dtype y_dtype, void* y,
                         hipStream_t stream);
 
-/* a1 + a3 + a10 (first half) in one launch -- up to four projections of the same input:
+/* Several projections of one input in one launch -- up to four of them:
  *   y_i = x @ w_i^T                                    (situ == NULL or situ[i] == 0), or
  *   y_i = SituGLU(x @ w_i^T) with w_i of 2*N[i] rows   (situ[i] != 0; gate rows first)
  * for i < n_proj <= 4. The decode-time projections of the hidden input -- the router GEMM
@@ -114,7 +114,7 @@ lmoe_status lmoe_linear_multi(int M, int Kd, lmoe_dtype x_dtype, const void* x, 
                               const void* const* w, const lmoe_dtype* y_dtype, void* const* y, const int* situ,
                               float beta, float linear_beta, hipStream_t stream);
 
-/* a2 -- single-group DeepSeekV3 top-k routing ([P1] commit 1: with one group the
+/* Single-group DeepSeekV3 top-k routing ([P1] commit 1: with one group the
  * grouped top-k is a plain top-k over all experts, result k held in lane k; [P1]
  * commit 4: sigmoid scores, selection bias, routed scaling factor, FP32 logits).
  *   s = sigmoid(logits[t, :]);  selection key = s + bias (bias may be NULL = 0);
@@ -152,7 +152,7 @@ lmoe_status lmoe_route_grouped(int T, int E, int K, int n_group, int topk_group,
 lmoe_status lmoe_route_renormalize(int T, int E, int K, const float* logits, int32_t* topk_ids,
                                    float* topk_weights, hipStream_t stream);
 
-/* a5 -- stable expert-sorted permutation of the T*K (token, slot) pairs, pair p = t*K + k
+/* Stable expert-sorted permutation of the T*K (token, slot) pairs, pair p = t*K + k
  * ([P2] "Commit 1": the routing workspace that FC1 / FC2 / finalize read, computed for
  * the tile the runner reports). Outputs (all int32, caller-allocated):
  *   expert_counts[E]       pairs routed to each expert;
@@ -186,7 +186,7 @@ lmoe_status lmoe_route_permute(int T, int E, int K, const float* logits, const f
                                int32_t* row_to_pair, int32_t* tile_expert, int32_t* pair_to_row,
                                int rows_cap, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* a4 / a8 -- MXFP8 (E4M3) quantization along rows ([OCP-MX]; [P2] "Description": input
+/* MXFP8 (E4M3) quantization along rows ([OCP-MX]; [P2] "Description": input
  * quantization before the MXE4M3 x MXE2M1 experts; [P1] commit 3: the general gated
  * activations apply the activation, then requantize). Per 32 consecutive elements:
  * exponent X = floor(log2 max|v|) - 8 clamped to [-127,127] (0 for an all-zero block);
@@ -196,7 +196,7 @@ lmoe_status lmoe_route_permute(int T, int E, int K, const float* logits, const f
 lmoe_status lmoe_quant_mxfp8(int rows, int cols, lmoe_dtype in_dtype, const void* in,
                              uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
-/* a6 + a7 (+ a8) -- grouped FC1 with the SituGLU epilogue ([P1] commit 2: SituGLU,
+/* Grouped FC1 with the SituGLU epilogue ([P1] commit 2: SituGLU,
  * fp32 accumulate, written straight to the output; [P1] commit 5: SituGLU acts on the
  * dequantized gate/up; [P3] enable_quantized_routed_input: gate and up not interleaved).
  *   For every row r of a tile with expert e = tile_expert[r / tile_m] >= 0 and pair
@@ -223,7 +223,7 @@ lmoe_status lmoe_fc1_situ(int T, int E, int K, int in_dim, int d, int tile_m,
                           lmoe_dtype act_dtype, void* act, uint8_t* act_scale,
                           int rows_cap, hipStream_t stream);
 
-/* a9 -- grouped FC2 with the weighted combine ([P2] "Commit 1": finalize reads the
+/* Grouped FC2 with the weighted combine ([P2] "Commit 1": finalize reads the
  * routing workspace; [P3] enable_quantized_routed_input: router weights are applied
  * after the experts, not on their input).
  *   y_r = act[r, :] @ w2[e]^T (w2 [E, out_dim, d]) for every valid row r, then
@@ -260,7 +260,7 @@ lmoe_status lmoe_fc2_combine_norm(int T, int E, int K, int d, int out_dim, int t
                                   void* workspace, size_t workspace_bytes, const void* gamma, float eps,
                                   lmoe_dtype norm_dtype, void* norm_out, hipStream_t stream);
 
-/* a11 + a12 -- latent tail ([P1] commit 7: the routed output is summed before the
+/* Latent tail ([P1] commit 7: the routed output is summed before the
  * output transform because it contains an RMSNorm; [P3] _shard_up_proj_tail: norm of
  * the reduced latent, then shared += latent @ up_proj^T in the GEMM's epilogue; [P1]
  * commit 6: the up projection folds in the shared-expert add).
@@ -275,8 +275,8 @@ lmoe_status lmoe_tail(int T, int L, int H, const float* latent, const void* gamm
                       const void* w_up, const void* shared, lmoe_dtype io_dtype, void* out,
                       void* norm_out, hipStream_t stream);
 
-/* a10 (second half) + a11 + a12 in two launches -- the tail with the shared expert's FC2
- * folded into the up projection ([P3] _shard_up_proj_tail: hidden += latent @ up_proj^T
+/* The tail with the shared expert's FC2 folded into the up projection, in two launches
+ * ([P3] _shard_up_proj_tail: hidden += latent @ up_proj^T
  * accumulated into the shared output; [P1] commit 6: the up projection folds in the
  * shared-expert add):
  *   norm_out = RMSNorm(latent; gamma, eps)                        (as lmoe_tail)

@@ -405,7 +405,7 @@ def layer_forward(X, W_r, bias, W_down, W1, W2, W_s1, W_s2, gamma, W_up, *,
     Returns a dict of every intermediate the GPU path stores."""
     X = np.asarray(X, dtype=np.float64)
     T = X.shape[0]
-    logits = router_logits(X, W_r)                                   # a1
+    logits = router_logits(X, W_r)                                   # router GEMM
     if routing == "renormalize":                                     # routing
         ids, w = route_renormalize(logits, K)
         kappa = None
@@ -414,9 +414,9 @@ def layer_forward(X, W_r, bias, W_down, W1, W2, W_s1, W_s2, gamma, W_up, *,
         kappa = None
     else:
         ids, w, kappa = route(logits, bias, K, rsf, renormalize)
-    x = round_to(linear(X, W_down), dtype)                           # a3
+    x = round_to(linear(X, W_down), dtype)                           # latent down projection
     res = dict(logits=logits, ids=ids, weights=w, kappa=kappa, x=x)
-    if mx:                                                           # a4
+    if mx:                                                           # input quantization
         xq, xs = mxfp8_quantize(x)
         x_in = mxfp8_dequant(xq, xs)
         res.update(xq=xq, xs=xs)
@@ -426,16 +426,16 @@ def layer_forward(X, W_r, bias, W_down, W1, W2, W_s1, W_s2, gamma, W_up, *,
     Y = np.zeros((T, K, L))
     d = None
     act = None
-    for e in np.unique(ids):                                         # a6..a9 per expert
+    for e in np.unique(ids):                                         # routed experts
         tt, kk = np.nonzero(ids == e)
-        h = _expert_fc1(int(e), x_in[tt], W1, W1_scales, mx)         # a6 (never rounded)
-        a = situ_glu_rows(h, beta, linear_beta)                      # a7
+        h = _expert_fc1(int(e), x_in[tt], W1, W1_scales, mx)         # FC1 (never rounded)
+        a = situ_glu_rows(h, beta, linear_beta)                      # SituGLU
         if d is None:
             d = a.shape[1]
             act = np.zeros((T, K, d))
             actq = np.zeros((T, K, d), dtype=np.uint8) if mx else None
             acts = np.zeros((T, K, d // 32), dtype=np.uint8) if mx else None
-        if mx:                                                       # a8
+        if mx:                                                       # requantization
             aq, as_ = mxfp8_quantize(f32_round(a))
             a_in = mxfp8_dequant(aq, as_)
             actq[tt, kk] = aq
@@ -444,13 +444,13 @@ def layer_forward(X, W_r, bias, W_down, W1, W2, W_s1, W_s2, gamma, W_up, *,
         else:
             a_in = round_to(a, dtype)
             act[tt, kk] = a_in
-        Y[tt, kk] = _expert_fc2(int(e), a_in, W2, W2_scales, mx)     # a9 (expert output)
+        Y[tt, kk] = _expert_fc2(int(e), a_in, W2, W2_scales, mx)     # FC2 (expert output)
     z = np.zeros((T, L))
-    for k in range(K):                                               # a9 weighted combine
+    for k in range(K):                                               # weighted combine
         z = z + w[:, k:k + 1] * Y[:, k, :]
     z = f32_round(z)
-    sh = shared_expert(X, W_s1, W_s2, beta, linear_beta, dtype)      # a10
-    n, out = tail(z, gamma, eps, W_up, sh, dtype)                    # a11, a12
+    sh = shared_expert(X, W_s1, W_s2, beta, linear_beta, dtype)      # shared expert
+    n, out = tail(z, gamma, eps, W_up, sh, dtype)                    # RMSNorm, up projection
     res.update(act=act, z=z, sh=sh, n=n, out=out)
     if mx:
         res.update(actq=actq, acts=acts)
