@@ -156,8 +156,9 @@ def main():
                          "layer, as the reference kernel for HBM byte counters")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph of the layer step instead of eager launches")
-    ap.add_argument("--schedule", choices=["one_stream", "shared_stream"], default="shared_stream",
-                    help="shared_stream: the shared expert runs on a second stream")
+    ap.add_argument("--schedule", choices=["one_stream", "shared_stream", "router_stream"], default="shared_stream",
+                    help="shared_stream: the shared expert runs on a second stream; router_stream: also the "
+                         "router GEMM and routing on a third")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no multi-GPU path)",
@@ -177,7 +178,8 @@ def main():
     w = LI.make_layer_weights(cfg, args.seed, device="cuda")
     shape = LayerShape(H=cfg.H, L=cfg.L, E=cfg.E, K=cfg.K, d=cfg.d, I=cfg.I, dtype=cfg.dtype, experts=cfg.experts,
                        beta=cfg.beta, linear_beta=cfg.linear_beta, rsf=cfg.rsf, eps=cfg.eps, tile_m=cfg.tile_m)
-    layer = LatentMoELayer(shape, w, shared_stream=args.schedule == "shared_stream")
+    layer = LatentMoELayer(shape, w, shared_stream=args.schedule == "shared_stream",
+                           router_stream=args.schedule == "router_stream")
     X_cpu = LI.make_x(cfg, args.seed)
     X = X_cpu.to("cuda")
     stream = torch.cuda.current_stream()

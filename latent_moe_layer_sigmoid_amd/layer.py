@@ -49,7 +49,8 @@ class LatentMoELayer:
     W_s1 [2I,H], W_s2 [H,I], gamma [L], W_up [H,L]; the projections are packed on the
     device (lmoe_pack_weights) when the layer is built."""
 
-    def __init__(self, shape: LayerShape, weights: dict, device="cuda", fused=True, shared_stream=False):
+    def __init__(self, shape: LayerShape, weights: dict, device="cuda", fused=True, shared_stream=False,
+                 router_stream=False):
         B.lib()   # fail loudly now if the library is missing
         self.s = shape
         # fused: the hidden-input projections share one launch (lmoe_linear_multi) and the
@@ -60,9 +61,15 @@ class LatentMoELayer:
         # router GEMM, routing, permutation and the routed experts, and the tail waits for
         # it (TensorRT-LLM PR 20541, "Commit 2": shared experts on their own stream, joined
         # by an event before the routed reduction). Same kernels, same results.
-        self.shared_stream = shared_stream
+        self.shared_stream = shared_stream or router_stream
+        # router_stream: additionally, the router GEMM, routing and permutation run on a
+        # router stream while the main stream computes the latent down projection
+        # (TensorRT-LLM PR 20541, "Commit 2": router stream, shared stream, main stream).
+        self.router_stream = router_stream
         self.device = torch.device(device)
-        self._side = torch.cuda.Stream(self.device) if shared_stream else None   # default priority
+        # extra streams at the default priority
+        self._side = torch.cuda.Stream(self.device) if self.shared_stream else None
+        self._router = torch.cuda.Stream(self.device) if router_stream else None
         self._bufs = {}
         # weights go to HBM in the packed MFMA-operand layout once, at construction
         self.w = {}
@@ -183,11 +190,15 @@ class LatentMoELayer:
     def _routed(self, X, b, stream, mark, norm=False):
         """Routing, permutation and the routed experts on `stream`; with norm, the FC2 call
         also leaves the RMS-normalized latent in b["n"] (combine and RMSNorm in one kernel)."""
-        s, w = self.s, self.w
         T = X.shape[0]
-        dt = _lmoe_dtype(s.dtype)
-        rc = b["rows_cap"]
         mark("route_permute")
+        self._route(T, b, stream)
+        self._experts(T, b, stream, mark, norm)
+
+    def _route(self, T, b, stream):
+        """Routing and the permutation on `stream`."""
+        s, w = self.s, self.w
+        rc = b["rows_cap"]
         if s.routing == "sigmoid" and s.n_group == 1:
             B.lmoe_route_permute(T, s.E, s.K, b["logits"], w["bias"], s.rsf, 1, b["ids"], b["weights"], s.tile_m,
                                  b["counts"], b["offsets"], b["tile_offsets"], b["row_to_pair"], b["tile_expert"],
@@ -201,6 +212,13 @@ class LatentMoELayer:
             B.lmoe_permute(T, s.E, s.K, s.tile_m, b["ids"], b["counts"], b["offsets"], b["tile_offsets"],
                            b["row_to_pair"], b["tile_expert"], b["pair_to_row"], rc, b["perm_ws"],
                            b["perm_ws_bytes"], stream)
+
+    def _experts(self, T, b, stream, mark, norm=False):
+        """The routed experts (input quantization for MX, FC1 + SituGLU, FC2 + combine, and
+        with norm the RMS-normalized latent) on `stream`."""
+        s, w = self.s, self.w
+        dt = _lmoe_dtype(s.dtype)
+        rc = b["rows_cap"]
         if s.experts == "mx":
             mark("quant")
             B.lmoe_quant_mxfp8(T, s.L, dt, b["x"], b["xq"], b["xs"], stream)
@@ -229,7 +247,9 @@ class LatentMoELayer:
         """Main stream: router GEMM + down projection (one launch), routing, permutation,
         experts, then RMSNorm + up projection with the shared add. Side stream: the shared
         expert (FC1 + SituGLU, FC2), started once the main stream reaches this call and
-        joined by an event before the tail."""
+        joined by an event before the tail. With the router stream, the router GEMM,
+        routing and permutation run there and the main stream computes the down projection
+        meanwhile, then waits for the routing before the experts."""
         s, w = self.s, self.w
         T = X.shape[0]
         dt = _lmoe_dtype(s.dtype)
@@ -246,10 +266,24 @@ class LatentMoELayer:
                            dt, b["sh"], T, None, 0, side)
         shared_done = torch.cuda.Event()
         shared_done.record(side)
-        mark("front")
-        B.lmoe_linear_multi(T, s.H, dt, X, 2, [s.E, s.L], [w["W_r"], w["W_down"]], [B.LMOE_F32, dt],
-                            [b["logits"], b["x"]], None, s.beta, s.linear_beta, main)
-        self._routed(X, b, main, mark, norm=True)
+        if self.router_stream:
+            rs = self._router
+            rs.wait_event(start)
+            if not torch.cuda.is_current_stream_capturing():
+                X.record_stream(rs)
+            B.lmoe_linear(T, s.E, s.H, dt, X, dt, w["W_r"], B.LMOE_F32, b["logits"], rs)
+            self._route(T, b, rs)
+            routed = torch.cuda.Event()
+            routed.record(rs)
+            mark("front")
+            B.lmoe_linear(T, s.L, s.H, dt, X, dt, w["W_down"], dt, b["x"], main)
+            main.wait_event(routed)
+            self._experts(T, b, main, mark, norm=True)
+        else:
+            mark("front")
+            B.lmoe_linear_multi(T, s.H, dt, X, 2, [s.E, s.L], [w["W_r"], w["W_down"]], [B.LMOE_F32, dt],
+                                [b["logits"], b["x"]], None, s.beta, s.linear_beta, main)
+            self._routed(X, b, main, mark, norm=True)
         main.wait_event(shared_done)
         mark("tail")
         B.lmoe_tail(T, s.L, s.H, None, w["gamma"], s.eps, w["W_up"], b["sh"], dt, b["out"], b["n"], main)

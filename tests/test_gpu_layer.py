@@ -16,20 +16,21 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def build_layer(cfg, seed, fused=True, shared_stream=False):
+def build_layer(cfg, seed, fused=True, shared_stream=False, router_stream=False):
     from latent_moe_layer_sigmoid_amd import LatentMoELayer, LayerShape
     w_dev = LI.make_layer_weights(cfg, seed, device=DEV)
     shape = LayerShape(H=cfg.H, L=cfg.L, E=cfg.E, K=cfg.K, d=cfg.d, I=cfg.I, dtype=cfg.dtype, experts=cfg.experts,
                        beta=cfg.beta, linear_beta=cfg.linear_beta, rsf=cfg.rsf, eps=cfg.eps, tile_m=cfg.tile_m,
                        routing=cfg.routing, n_group=cfg.n_group, topk_group=cfg.topk_group)
-    return LatentMoELayer(shape, w_dev, fused=fused, shared_stream=shared_stream), w_dev
+    return LatentMoELayer(shape, w_dev, fused=fused, shared_stream=shared_stream, router_stream=router_stream), w_dev
 
 
-def check_layer(cfg, seed, tokens=None, out_tol=1e-2, fused=True, shared_stream=False):
+def check_layer(cfg, seed, tokens=None, out_tol=1e-2, fused=True, shared_stream=False, router_stream=False):
     """Run the layer on the GPU for all T tokens; compare routing / permutation for all
     tokens and the float outputs for `tokens` (all when None) against the oracle."""
-    print(f"[layer parity] {cfg.name} T={cfg.T} seed={seed} fused={fused} shared_stream={shared_stream}", flush=True)
-    layer, w_dev = build_layer(cfg, seed, fused, shared_stream)
+    print(f"[layer parity] {cfg.name} T={cfg.T} seed={seed} fused={fused} shared_stream={shared_stream} "
+          f"router_stream={router_stream}", flush=True)
+    layer, w_dev = build_layer(cfg, seed, fused, shared_stream, router_stream)
     w_cpu = LI.make_layer_weights(cfg, seed, device="cpu", experts=False)
     o = oracle_weights(cfg, seed, w_cpu)
     X, _ = guarded_x(cfg, seed, o["W_r"], o["bias"])
@@ -66,7 +67,7 @@ def check_layer(cfg, seed, tokens=None, out_tol=1e-2, fused=True, shared_stream=
     # MX requantization amplifies one-ulp differences of the latent upstream: the MX bar
     # (3e-2) applies to the tensors downstream of the expert GEMMs as well
     assert norm_err(f64(b["z"])[sel], ref["z"]) <= out_tol
-    if not fused or shared_stream:
+    if not fused or shared_stream or router_stream:
         assert norm_err(f64(b["sh"])[sel], ref["sh"]) <= 1e-2
     assert norm_err(f64(b["n"])[sel], ref["n"]) <= out_tol
     err = norm_err(f64(out)[sel], ref["out"])
@@ -91,6 +92,20 @@ def test_layer_decode_bf16_full_size():
 
 def test_layer_decode_second_seed_unfused_path():
     check_layer(LI.DECODE, 102, fused=False)
+
+
+def test_layer_three_streams_decode_and_mx():
+    """Router GEMM + routing on a router stream, shared expert on a shared stream, down
+    projection and experts on the main stream: same results, repeated calls identical."""
+    check_layer(LI.TINY, 4, router_stream=True)
+    layer, X = check_layer(LI.DECODE, 2, router_stream=True)
+    first = layer.buffers(LI.DECODE.T)["out"].clone()
+    for _ in range(3):
+        layer.forward(X.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), layer.buffers(LI.DECODE.T)["out"].view(torch.int16))
+    check_layer(LI.scaled(LI.MX, name="mx_reduced", T=64, H=1024, L=1024, E=32, K=4, d=512, I=256), 5,
+                out_tol=3e-2, router_stream=True)
 
 
 def test_layer_tiny_and_decode_shared_expert_stream():
@@ -124,12 +139,12 @@ def test_layer_prefill_full_size_sampled_tokens():
     check_layer(cfg, 4, tokens=[0, 1, 2, 4095, 8190, 8191])
 
 
-@pytest.mark.parametrize("shared_stream", [False, True])
-def test_layer_decode_graph_replays_match_eager(shared_stream):
+@pytest.mark.parametrize("shared_stream,router_stream", [(False, False), (True, False), (False, True)])
+def test_layer_decode_graph_replays_match_eager(shared_stream, router_stream):
     """A captured graph of the decode layer, replayed several times with eager work and
     synchronizations in between, reproduces the eager output bit for bit every time."""
     cfg = LI.DECODE
-    layer, _ = build_layer(cfg, 2, shared_stream=shared_stream)
+    layer, _ = build_layer(cfg, 2, shared_stream=shared_stream, router_stream=router_stream)
     w_cpu = LI.make_layer_weights(cfg, 2, device="cpu", experts=False)
     o = oracle_weights(cfg, 2, w_cpu)
     X, _ = guarded_x(cfg, 2, o["W_r"], o["bias"])
