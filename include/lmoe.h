@@ -114,6 +114,21 @@ lmoe_status lmoe_linear_multi(int M, int Kd, lmoe_dtype x_dtype, const void* x, 
                               const void* const* w, const lmoe_dtype* y_dtype, void* const* y, const int* situ,
                               float beta, float linear_beta, hipStream_t stream);
 
+/* lmoe_linear_multi with a caller-provided fp32 workspace for split-K: when M is large
+ * enough for the LDS-tiled kernel (BF16, M >= 256) but its 128 x 512 tiles would leave
+ * CUs idle, each tile's K range is cut into slices computed by separate workgroups into
+ * `workspace`, and a second kernel adds the slices in fixed order and applies the
+ * epilogues (results are reproducible; they may differ in the last bits from the
+ * unsplit call). lmoe_linear_multi_workspace_bytes returns the bytes this call needs for
+ * the same shapes (0: no split, workspace unused). workspace NULL: no split; non-NULL but
+ * smaller than needed: LMOE_ERR_WORKSPACE. */
+size_t lmoe_linear_multi_workspace_bytes(int M, int Kd, lmoe_dtype x_dtype, int n_proj, const int* N,
+                                         const int* situ);
+lmoe_status lmoe_linear_multi_ws(int M, int Kd, lmoe_dtype x_dtype, const void* x, int n_proj, const int* N,
+                                 const void* const* w, const lmoe_dtype* y_dtype, void* const* y, const int* situ,
+                                 float beta, float linear_beta, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
 /* Single-group DeepSeekV3 top-k routing ([P1] commit 1: with one group the
  * grouped top-k is a plain top-k over all experts, result k held in lane k; [P1]
  * commit 4: sigmoid scores, selection bias, routed scaling factor, FP32 logits).

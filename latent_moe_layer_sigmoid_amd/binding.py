@@ -36,6 +36,8 @@ SIGNATURES = [
     ("lmoe_pack_mxfp4_weights", _i, [_i, _i, _i, _p, _p, _p, _p, _p]),
     ("lmoe_linear", _i, [_i, _i, _i, _i, _p, _i, _p, _i, _p, _p]),
     ("lmoe_linear_multi", _i, [_i, _i, _i, _p, _i, _p, _p, _p, _p, _p, _f, _f, _p]),
+    ("lmoe_linear_multi_workspace_bytes", _z, [_i, _i, _i, _i, _p, _p]),
+    ("lmoe_linear_multi_ws", _i, [_i, _i, _i, _p, _i, _p, _p, _p, _p, _p, _f, _f, _p, _z, _p]),
     ("lmoe_route", _i, [_i, _i, _i, _p, _p, _f, _i, _p, _p, _p]),
     ("lmoe_route_grouped", _i, [_i, _i, _i, _i, _i, _p, _p, _f, _i, _p, _p, _p]),
     ("lmoe_route_renormalize", _i, [_i, _i, _i, _p, _p, _p, _p]),
@@ -153,6 +155,26 @@ def lmoe_linear_multi(M, Kd, x_dtype, x, n_proj, N, w, y_dtype, y, situ, beta, l
     sa = None if situ is None else (ctypes.c_int * n)(*[int(v) for v in situ])
     _check("lmoe_linear_multi", lib().lmoe_linear_multi(M, Kd, x_dtype, _ptr(x), n, Na, wa, ta, ya, sa,
                                                         float(beta), float(linear_beta), _stream(stream)))
+
+
+def lmoe_linear_multi_workspace_bytes(M, Kd, x_dtype, n_proj, N, situ=None):
+    n = int(n_proj)
+    Na = (ctypes.c_int * n)(*N)
+    sa = None if situ is None else (ctypes.c_int * n)(*[int(v) for v in situ])
+    return int(lib().lmoe_linear_multi_workspace_bytes(M, Kd, x_dtype, n, Na, sa))
+
+
+def lmoe_linear_multi_ws(M, Kd, x_dtype, x, n_proj, N, w, y_dtype, y, situ, beta, linear_beta, workspace,
+                         workspace_bytes, stream=None):
+    n = int(n_proj)
+    Na = (ctypes.c_int * n)(*N)
+    wa = (ctypes.c_void_p * n)(*[_ptr(t) for t in w])
+    ta = (ctypes.c_int * n)(*y_dtype)
+    ya = (ctypes.c_void_p * n)(*[_ptr(t) for t in y])
+    sa = None if situ is None else (ctypes.c_int * n)(*[int(v) for v in situ])
+    _check("lmoe_linear_multi_ws", lib().lmoe_linear_multi_ws(M, Kd, x_dtype, _ptr(x), n, Na, wa, ta, ya, sa,
+                                                              float(beta), float(linear_beta), _ptr(workspace),
+                                                              int(workspace_bytes), _stream(stream)))
 
 
 def lmoe_route(T, E, K, logits, bias, routed_scaling_factor, renormalize, topk_ids, topk_weights, stream=None):

@@ -100,17 +100,23 @@ struct Frag {
 };
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void tiled_gemm_kernel(
-    const StreamGemm g, int blocks_total, int m_tiles, int nch) {
+    const StreamGemm g, int blocks_total, int m_tiles, int nch_total) {
   __shared__ __attribute__((aligned(1024))) char smem[NSLOT * SLOT];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 15, g4 = lane >> 4;
 
-  // ---- tile of this workgroup: XCD-contiguous logical ids, then row-tile groups of 8
+  // ---- tile of this workgroup: XCD-contiguous logical ids, then row-tile groups of 8;
+  // with split-K the K slice is the outermost index
   const int G = m_tiles * blocks_total;
-  const int G8 = (G + 7) & ~7;
-  const int lid = (int)(blockIdx.x & 7) * (G8 >> 3) + (int)(blockIdx.x >> 3);
-  if (lid >= G) return;
+  const int ksplit = g.ksplit > 1 ? g.ksplit : 1;
+  const int GK8 = (G * ksplit + 7) & ~7;
+  const int lid_k = (int)(blockIdx.x & 7) * (GK8 >> 3) + (int)(blockIdx.x >> 3);
+  if (lid_k >= G * ksplit) return;
+  const int ks = lid_k / G;
+  const int lid = lid_k - ks * G;
+  const int k0 = (int)((long)nch_total * ks / ksplit);                 // this slice's K steps
+  const int nch = (int)((long)nch_total * (ks + 1) / ksplit) - k0;
   const int per_group = GROUP_M * blocks_total;
   const int grp = lid / per_group;
   const int first_m = grp * GROUP_M;
@@ -166,9 +172,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   auto issue = [&](int c) {
     char* base = smem + (c % NSLOT) * SLOT;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) to_lds(a_rs, base + (2 * wave + h) * 1024, a_off[h], (uint32_t)c * 64u);
+    for (int h = 0; h < 2; ++h) to_lds(a_rs, base + (2 * wave + h) * 1024, a_off[h], (uint32_t)(c + k0) * 64u);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) to_lds(w_rs, base + B_OFF + (8 * wave + j) * 1024, b_off[j], (uint32_t)c * 1024u);
+    for (int j = 0; j < 8; ++j)
+      to_lds(w_rs, base + B_OFF + (8 * wave + j) * 1024, b_off[j], (uint32_t)(c + k0) * 1024u);
   };
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)smem + lane * 16;
   auto read = [&](int c, Frag& f) {
@@ -251,7 +258,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     });
     __builtin_amdgcn_sched_barrier(0);
     const int rbase = row0 + 64 * h;
-    if (situ) {
+    if (ksplit > 1) {
+      // raw fp32 partial sums of this K slice: 32 lanes per row, 4 weight-row columns each
+      int pbase = 0, ptot = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i < g.nseg) {
+          if (i < s) pbase += g.seg[i].n_total;
+          ptot += g.seg[i].n_total;
+        }
+      }
+      const int q = lane & 31;
+      int pcol, valid;
+      if (situ) {
+        const int c = 4 * q;   // LDS columns 0..63: gate, 64..127: up
+        const int oc = 256 * nb + 64 * wave + (c & 63);
+        valid = oc < sg.n_out;
+        pcol = (c < 64 ? 0 : sg.n_out) + oc;
+      } else {
+        pcol = TILE_N * nb + 128 * wave + 4 * q;
+        valid = pcol < sg.n_out;
+      }
+      float* dst = g.part + (size_t)ks * g.M * ptot + pbase + pcol;
+      for (int r = lane >> 5; r < 64; r += 2) {
+        const int row = rbase + r;
+        const floatx4 v = *reinterpret_cast<const floatx4*>(red + r * RS + 4 * q);
+        if (row < g.M && valid) *reinterpret_cast<floatx4*>(dst + (size_t)row * ptot) = v;
+      }
+    } else if (situ) {
       // 16 lanes per row (4 outputs each): gate columns c .. c + 3, up columns 64 + c ..
       const int q = lane & 15;
       const int col = 256 * nb + 64 * wave + 4 * q;
@@ -312,8 +346,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   });
 }
 
-hipError_t launch_tiled_gemm(StreamGemm g, hipStream_t stream) {
-  const int nch = g.Kd / 32;
+static int tiled_blocks(StreamGemm& g) {
   int b0 = 0;
   for (int i = 0; i < g.nseg; ++i) {
     const int per = g.seg[i].epi == Epi::SITU ? TILE_N / 2 : TILE_N;
@@ -321,10 +354,85 @@ hipError_t launch_tiled_gemm(StreamGemm g, hipStream_t stream) {
     g.seg[i].block0 = b0;
     b0 += g.seg[i].blocks;
   }
+  return b0;
+}
+
+// Dense calls whose tiles do not fill the CUs split K so that tiles x slices reach about
+// one workgroup per CU, each slice keeping at least 16 K steps (512 elements).
+int tiled_splitk(const StreamGemm& g0) {
+  if (g0.row_to_pair) return 1;
+  StreamGemm g = g0;
+  const int G = ((g.M + TILE_M - 1) / TILE_M) * tiled_blocks(g);
+  int k = 256 / (G > 0 ? G : 1);
+  k = min(k, (g.Kd / 32) / 16);
+  k = min(k, 8);
+  return k < 2 ? 1 : k;
+}
+
+size_t tiled_splitk_bytes(const StreamGemm& g, int ksplit) {
+  if (ksplit <= 1) return 0;
+  size_t cols = 0;
+  for (int i = 0; i < g.nseg; ++i) cols += (size_t)g.seg[i].n_total;
+  return (size_t)ksplit * (size_t)g.M * cols * sizeof(float);
+}
+
+// Sum of the K slices (in slice order) and the segment's epilogue; one thread per 4
+// output columns of one row.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const StreamGemm g, int ptot) {
+  const int si = blockIdx.z, row = blockIdx.y;
+  const Seg sg = g.seg[si];
+  const int col = 4 * (int)(blockIdx.x * 256 + threadIdx.x);
+  if (col >= sg.n_out) return;
+  int pbase = 0;
+  for (int i = 0; i < si; ++i) pbase += g.seg[i].n_total;
+  const size_t slice = (size_t)g.M * ptot;
+  const float* src = g.part + (size_t)row * ptot + pbase + col;
+  floatx4 v = *reinterpret_cast<const floatx4*>(src);
+  for (int k = 1; k < g.ksplit; ++k) v += *reinterpret_cast<const floatx4*>(src + k * slice);
+  if (sg.epi == Epi::SITU) {
+    floatx4 u = *reinterpret_cast<const floatx4*>(src + sg.n_out);
+    for (int k = 1; k < g.ksplit; ++k) u += *reinterpret_cast<const floatx4*>(src + sg.n_out + k * slice);
+    const float inv_b = 1.0f / g.beta;
+    const float inv_lb = g.lbeta > 0.0f ? 1.0f / g.lbeta : 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = situ_f(v[q], u[q], g.beta, inv_b, g.lbeta, inv_lb);
+  }
+  const size_t idx = (size_t)row * sg.ldo + col;
+  if (sg.epi == Epi::ADD && g.add != nullptr) {
+    if (sg.out_elt == Elt::F32) {
+      v += *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(g.add) + idx);
+    } else {
+      const uint2 a = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(g.add) + idx);
+      v += floatx4{bf16_to_f32((uint16_t)a.x), bf16_to_f32((uint16_t)(a.x >> 16)), bf16_to_f32((uint16_t)a.y),
+                   bf16_to_f32((uint16_t)(a.y >> 16))};
+    }
+  }
+  if (sg.out_elt == Elt::F32) {
+    *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(sg.out) + idx) = v;
+  } else {
+    const uint32_t lo = f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    const uint32_t hi = f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(sg.out) + idx) = make_uint2(lo, hi);
+  }
+}
+
+hipError_t launch_tiled_gemm(StreamGemm g, hipStream_t stream) {
+  const int nch = g.Kd / 32;
+  const int b0 = tiled_blocks(g);
+  if (g.ksplit < 2 || !g.part || g.row_to_pair) g.ksplit = 1;
   const int m_tiles = (g.M + TILE_M - 1) / TILE_M;
   const int G = m_tiles * b0;
-  const unsigned G8 = (unsigned)((G + 7) & ~7);
-  hipLaunchKernelGGL(tiled_gemm_kernel, dim3(G8), dim3(256), 0, stream, g, b0, m_tiles, nch);
+  const unsigned GK8 = (unsigned)((G * g.ksplit + 7) & ~7);
+  hipLaunchKernelGGL(tiled_gemm_kernel, dim3(GK8), dim3(256), 0, stream, g, b0, m_tiles, nch);
+  if (g.ksplit > 1) {
+    int ptot = 0, wmax = 0;
+    for (int i = 0; i < g.nseg; ++i) {
+      ptot += g.seg[i].n_total;
+      wmax = max(wmax, g.seg[i].n_out);
+    }
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((wmax / 4 + 255) / 256), (unsigned)g.M, (unsigned)g.nseg),
+                       dim3(256), 0, stream, g, ptot);
+  }
   return hipGetLastError();
 }
 

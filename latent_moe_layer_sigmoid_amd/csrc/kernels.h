@@ -62,12 +62,21 @@ struct StreamGemm {
   uint32_t a_scale_bytes;
   const uint8_t* w_scale;
   uint8_t* out_scale;        // SITU_MX: [rows_cap, n_out/32]
+  // split-K of the dense tiled GEMM: ksplit workgroups per tile each sum one slice of K
+  // into `part` ([ksplit][M][sum of the segments' n_total] fp32); a reduce kernel adds
+  // the slices in order and applies the epilogues. ksplit <= 1: no split.
+  float* part;
+  int ksplit;
 };
 
 // live_tiles: expected number of 16-row tiles that hold rows (sizes the split-K factor).
 hipError_t launch_stream_gemm(StreamGemm g, Elt elt, int live_tiles, hipStream_t stream);
 // LDS-tiled bf16 GEMM: 128-row tiles (dense rows, or grouped tiles with tile_m == 128); Kd % 128 == 0.
 hipError_t launch_tiled_gemm(StreamGemm g, hipStream_t stream);
+// Split-K factor the tiled kernel would use for dense g (1: none) and the fp32 workspace
+// bytes it then needs.
+int tiled_splitk(const StreamGemm& g);
+size_t tiled_splitk_bytes(const StreamGemm& g, int ksplit);
 // MXFP8 x packed MXFP4 (grouped mode, one segment: SITU_MX or PAIR / TOKEN); Kd % 512 == 0.
 hipError_t launch_stream_gemm_mx(StreamGemm g, int live_tiles, hipStream_t stream);
 

@@ -95,14 +95,17 @@ lmoe_status lmoe_linear(int M, int N, int Kd, lmoe_dtype x_dtype, const void* x,
   return hip_status(run_gemm(g, x_dtype, use_tiled_dense(M, x_dtype), (M + 15) / 16, stream));
 }
 
-lmoe_status lmoe_linear_multi(int M, int Kd, lmoe_dtype x_dtype, const void* x, int n_proj, const int* N,
-                              const void* const* w, const lmoe_dtype* y_dtype, void* const* y, const int* situ,
-                              float beta, float linear_beta, hipStream_t stream) {
-  if (M < 0 || Kd <= 0 || n_proj < 1 || n_proj > 4 || !N || !w || !y_dtype || !y) return LMOE_ERR_INVALID_ARG;
+// Validates a lmoe_linear_multi call and fills g; LMOE_OK when a launch is needed.
+static lmoe_status linear_multi_setup(int M, int Kd, lmoe_dtype x_dtype, const void* x, int n_proj, const int* N,
+                                      const void* const* w, const lmoe_dtype* y_dtype, void* const* y,
+                                      const int* situ, float beta, float linear_beta, bool check_ptrs,
+                                      StreamGemm* out) {
+  if (M < 0 || Kd <= 0 || n_proj < 1 || n_proj > 4 || !N) return LMOE_ERR_INVALID_ARG;
+  if (check_ptrs && (!w || !y_dtype || !y)) return LMOE_ERR_INVALID_ARG;
   if (!dense_elt(x_dtype)) return LMOE_ERR_INVALID_ARG;
   bool any_situ = false;
   for (int i = 0; i < n_proj; ++i) {
-    if (N[i] <= 0 || !dense_elt(y_dtype[i])) return LMOE_ERR_INVALID_ARG;
+    if (N[i] <= 0 || (check_ptrs && !dense_elt(y_dtype[i]))) return LMOE_ERR_INVALID_ARG;
     if (N[i] % 16 != 0) return LMOE_ERR_UNSUPPORTED;
     any_situ |= situ && situ[i];
   }
@@ -110,7 +113,7 @@ lmoe_status lmoe_linear_multi(int M, int Kd, lmoe_dtype x_dtype, const void* x, 
     return LMOE_ERR_INVALID_ARG;
   if (Kd % kchunk_of(x_dtype) != 0) return LMOE_ERR_UNSUPPORTED;
   if (M == 0) return LMOE_OK;
-  if (!x) return LMOE_ERR_INVALID_ARG;
+  if (check_ptrs && !x) return LMOE_ERR_INVALID_ARG;
   if (!fits32(M, Kd, x_dtype)) return LMOE_ERR_UNSUPPORTED;
   StreamGemm g{};
   g.a = x;
@@ -124,12 +127,50 @@ lmoe_status lmoe_linear_multi(int M, int Kd, lmoe_dtype x_dtype, const void* x, 
   g.nseg = n_proj;
   for (int i = 0; i < n_proj; ++i) {
     const bool si = situ && situ[i];
-    if (!w[i] || !y[i]) return LMOE_ERR_INVALID_ARG;
+    if (check_ptrs && (!w[i] || !y[i])) return LMOE_ERR_INVALID_ARG;
     if (!fits32(si ? 2L * N[i] : N[i], Kd, x_dtype)) return LMOE_ERR_UNSUPPORTED;
-    g.seg[i] = Seg{w[i], si ? 2 * N[i] : N[i], N[i], si ? Epi::SITU : Epi::STORE, elt_of(y_dtype[i]), y[i], N[i], 0,
-                   0};
+    g.seg[i] = Seg{check_ptrs ? w[i] : nullptr, si ? 2 * N[i] : N[i], N[i], si ? Epi::SITU : Epi::STORE,
+                   check_ptrs ? elt_of(y_dtype[i]) : Elt::F32, check_ptrs ? y[i] : nullptr, N[i], 0, 0};
   }
-  return hip_status(run_gemm(g, x_dtype, use_tiled_dense(M, x_dtype), (M + 15) / 16, stream));
+  *out = g;
+  return LMOE_OK;
+}
+
+size_t lmoe_linear_multi_workspace_bytes(int M, int Kd, lmoe_dtype x_dtype, int n_proj, const int* N,
+                                         const int* situ) {
+  StreamGemm g{};
+  if (M <= 0 || linear_multi_setup(M, Kd, x_dtype, nullptr, n_proj, N, nullptr, nullptr, nullptr, situ, 1.0f,
+                                   0.0f, false, &g) != LMOE_OK)
+    return 0;
+  if (!use_tiled_dense(M, x_dtype)) return 0;
+  return tiled_splitk_bytes(g, tiled_splitk(g));
+}
+
+lmoe_status lmoe_linear_multi_ws(int M, int Kd, lmoe_dtype x_dtype, const void* x, int n_proj, const int* N,
+                                 const void* const* w, const lmoe_dtype* y_dtype, void* const* y, const int* situ,
+                                 float beta, float linear_beta, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  StreamGemm g{};
+  lmoe_status st = linear_multi_setup(M, Kd, x_dtype, x, n_proj, N, w, y_dtype, y, situ, beta, linear_beta, true,
+                                      &g);
+  if (st != LMOE_OK || M == 0) return st;
+  const bool tiled = use_tiled_dense(M, x_dtype);
+  if (tiled && workspace) {
+    const int k = tiled_splitk(g);
+    if (k > 1) {
+      if (workspace_bytes < tiled_splitk_bytes(g, k)) return LMOE_ERR_WORKSPACE;
+      g.part = static_cast<float*>(workspace);
+      g.ksplit = k;
+    }
+  }
+  return hip_status(run_gemm(g, x_dtype, tiled, (M + 15) / 16, stream));
+}
+
+lmoe_status lmoe_linear_multi(int M, int Kd, lmoe_dtype x_dtype, const void* x, int n_proj, const int* N,
+                              const void* const* w, const lmoe_dtype* y_dtype, void* const* y, const int* situ,
+                              float beta, float linear_beta, hipStream_t stream) {
+  return lmoe_linear_multi_ws(M, Kd, x_dtype, x, n_proj, N, w, y_dtype, y, situ, beta, linear_beta, nullptr, 0,
+                              stream);
 }
 
 lmoe_status lmoe_route(int T, int E, int K, const float* logits, const float* bias, float rsf, int renormalize,

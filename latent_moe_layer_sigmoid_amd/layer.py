@@ -114,6 +114,14 @@ class LatentMoELayer:
             n=torch.empty(T, s.L, dtype=dt, device=dev),
             out=torch.empty(T, s.H, dtype=dt, device=dev),
         )
+        # split-K workspace of the front projections (used when their tiles alone would
+        # leave CUs idle): the two- and three-projection variants
+        dtl = _lmoe_dtype(s.dtype)
+        fw2 = B.lmoe_linear_multi_workspace_bytes(T, s.H, dtl, 2, [s.E, s.L], None)
+        fw3 = B.lmoe_linear_multi_workspace_bytes(T, s.H, dtl, 3, [s.E, s.L, s.I], [0, 0, 1])
+        fws = max(fw2, fw3)
+        b["front_ws"] = torch.empty(max(fws // 4, 1), dtype=torch.float32, device=dev) if fws else None
+        b["front_ws_bytes"] = fws
         if s.experts == "mx":
             b["xq"] = torch.empty(T, s.L, dtype=torch.uint8, device=dev)
             b["xs"] = torch.empty(T, s.L // 32, dtype=torch.uint8, device=dev)
@@ -141,9 +149,9 @@ class LatentMoELayer:
         if self.fused:
             # router GEMM, latent down projection, shared FC1 + SituGLU: one launch
             mark("front")
-            B.lmoe_linear_multi(T, s.H, dt, X, 3, [s.E, s.L, s.I], [w["W_r"], w["W_down"], w["W_s1"]],
-                                [B.LMOE_F32, dt, dt], [b["logits"], b["x"], b["act_s"]], [0, 0, 1], s.beta,
-                                s.linear_beta, stream)
+            B.lmoe_linear_multi_ws(T, s.H, dt, X, 3, [s.E, s.L, s.I], [w["W_r"], w["W_down"], w["W_s1"]],
+                                   [B.LMOE_F32, dt, dt], [b["logits"], b["x"], b["act_s"]], [0, 0, 1], s.beta,
+                                   s.linear_beta, b["front_ws"], b["front_ws_bytes"], stream)
         else:
             # router GEMM -> fp32 logits, latent down projection
             mark("router")
@@ -281,8 +289,9 @@ class LatentMoELayer:
             self._experts(T, b, main, mark, norm=True)
         else:
             mark("front")
-            B.lmoe_linear_multi(T, s.H, dt, X, 2, [s.E, s.L], [w["W_r"], w["W_down"]], [B.LMOE_F32, dt],
-                                [b["logits"], b["x"]], None, s.beta, s.linear_beta, main)
+            B.lmoe_linear_multi_ws(T, s.H, dt, X, 2, [s.E, s.L], [w["W_r"], w["W_down"]], [B.LMOE_F32, dt],
+                                   [b["logits"], b["x"]], None, s.beta, s.linear_beta, b["front_ws"],
+                                   b["front_ws_bytes"], main)
             self._routed(X, b, main, mark, norm=True)
         main.wait_event(shared_done)
         mark("tail")

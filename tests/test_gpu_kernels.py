@@ -671,6 +671,40 @@ def test_linear_multi_matches_oracle(B, M, Kd, dt):
     assert norm_err(f64(ys[2]), ref2) <= 1e-2
 
 
+@pytest.mark.parametrize("M,Kd,N,situ", [(1024, 7168, [896, 2048], [0, 0]), (260, 2048, [48, 128, 64], [0, 0, 1]),
+                                          (384, 1024, [400], [1])])
+def test_linear_multi_split_k(B, M, Kd, N, situ):
+    """Split-K of the tiled kernel (caller workspace): against the oracle, and within
+    rounding of the unsplit call."""
+    rng = np.random.default_rng(M + Kd + len(N))
+    x = torch.from_numpy(rng.standard_normal((M, Kd))).to(torch.bfloat16)
+    ws = [torch.from_numpy(rng.standard_normal((n * (2 if si else 1), Kd)) / math.sqrt(Kd)).to(torch.bfloat16)
+          for n, si in zip(N, situ)]
+    yt = [B.LMOE_F32 if i == 0 else B.LMOE_BF16 for i in range(len(N))]
+    mk = lambda: [torch.full((M, n), float("nan"), dtype=torch.float32 if i == 0 else torch.bfloat16, device=DEV)
+                  for i, n in enumerate(N)]
+    wsb = B.lmoe_linear_multi_workspace_bytes(M, Kd, B.LMOE_BF16, len(N), N, situ)
+    assert wsb > 0                      # these shapes split
+    wp = [B.packed(w.to(DEV)) for w in ws]
+    xd = x.to(DEV)
+    y_split, y_plain = mk(), mk()
+    work = torch.empty(wsb // 4, device=DEV)
+    B.lmoe_linear_multi_ws(M, Kd, B.LMOE_BF16, xd, len(N), N, wp, yt, y_split, situ, 1.0, 0.5, work, wsb)
+    B.lmoe_linear_multi(M, Kd, B.LMOE_BF16, xd, len(N), N, wp, yt, y_plain, situ, 1.0, 0.5)
+    with pytest.raises(B.LmoeError) as ei:
+        B.lmoe_linear_multi_ws(M, Kd, B.LMOE_BF16, xd, len(N), N, wp, yt, y_split, situ, 1.0, 0.5, work, wsb - 4)
+    assert ei.value.status == B.LMOE_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    x64 = f64(x)
+    for i, (n, si) in enumerate(zip(N, situ)):
+        h = oracle.linear(x64, f64(ws[i]))
+        ref = oracle.situ_glu_rows(h, 1.0, 0.5) if si else h
+        ref = oracle.f32_round(ref) if i == 0 else oracle.round_to(ref, "bf16")
+        tol = 1e-5 if i == 0 else 1e-2
+        assert norm_err(f64(y_split[i]), ref) <= tol
+        assert norm_err(f64(y_split[i]), f64(y_plain[i])) <= tol
+
+
 @pytest.mark.parametrize("T,L,H,I,dt", [(8, 2048, 7168, 4096, "bf16"), (4, 128, 256, 128, "f32"),
                                         (21, 256, 512, 384, "bf16"), (300, 256, 400, 384, "bf16")])
 def test_tail_shared_matches_oracle(B, T, L, H, I, dt):
