@@ -129,9 +129,16 @@ __global__ __launch_bounds__(256) void combine_kernel(int K, int N, const float*
   if (c4 * 4 >= N) return;
   const float4* src = reinterpret_cast<const float4*>(ws + (size_t)t * K * N) + c4;
   float4 s = src[0];
-  for (int k = 1; k < K; ++k) {
-    const float4 v = src[(size_t)k * (N / 4)];
-    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  for (int k0 = 1; k0 < K; k0 += 8) {   // requested 8 at a time, added in k order
+    float4 u[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (k0 + j < K) u[j] = src[(size_t)(k0 + j) * (N / 4)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (k0 + j < K) {
+        s.x += u[j].x; s.y += u[j].y; s.z += u[j].z; s.w += u[j].w;
+      }
   }
   if (out_bf16) {
     uint2 o;
@@ -202,10 +209,18 @@ __global__ __launch_bounds__(256) void combine_norm_kernel(int K, int L, const f
   const float* src = ws + (size_t)t * K * L;
   float ss = 0.0f;
   for (int i = threadIdx.x * 4; i < L; i += 256 * 4) {
+    // the K products are requested 8 at a time and then added in k order
     float4 v = *reinterpret_cast<const float4*>(src + i);
-    for (int k = 1; k < K; ++k) {
-      const float4 u = *reinterpret_cast<const float4*>(src + (size_t)k * L + i);
-      v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+    for (int k0 = 1; k0 < K; k0 += 8) {
+      float4 u[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (k0 + j < K) u[j] = *reinterpret_cast<const float4*>(src + (size_t)(k0 + j) * L + i);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (k0 + j < K) {
+          v.x += u[j].x; v.y += u[j].y; v.z += u[j].z; v.w += u[j].w;
+        }
     }
     *reinterpret_cast<float4*>(zrow + i) = v;
     ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
