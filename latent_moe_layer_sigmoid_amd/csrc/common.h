@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 #define LMOE_DEV __device__ __forceinline__
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -85,6 +87,25 @@ LMOE_DEV T wave_max(T v) {
     v = o > v ? o : v;
   }
   return v;
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1, so that register
+// arrays indexed by I stay in registers.
+template <typename F, int... I>
+LMOE_DEV void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+LMOE_DEV void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Workgroup barrier that orders LDS accesses only: global stores issued before it are not
+// waited for (use it where threads exchange data through LDS alone).
+LMOE_DEV void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 LMOE_DEV float wave_sum(float v) {

@@ -158,110 +158,140 @@ hipError_t launch_combine(int T, int K, int N, const float* ws, Elt out_elt, voi
 
 // ---- latent RMSNorm (vLLM PR 50088, commit 7: normalize the summed routed output):
 // n = z / sqrt(mean(z^2) + eps) * gamma in fp32; one workgroup per token row.
-__global__ __launch_bounds__(256) void rmsnorm_kernel(int L, const float* __restrict__ z,
-                                                      const void* __restrict__ gamma, int gamma_bf16, float eps,
-                                                      int out_bf16, void* __restrict__ out) {
-  __shared__ float s_part[4];
+//
+// Row layout shared by rmsnorm_kernel and combine_norm_kernel, so that both routes give
+// the same bits: a workgroup of norm_threads(L) threads owns a row; thread i handles the
+// column pairs c = 2i + 2 * nthreads * it (it = 0, 1, ...), accumulates their squares with
+// fmas in that order, and the per-thread sums are added over the wavefront by butterfly and
+// over the wavefronts in index order.
+constexpr int kNormMaxThreads = 1024;
+constexpr int kNormKeep = 4;   // column pairs per thread kept in registers by combine_norm_kernel
+
+static int norm_threads(int L) {
+  const int t = (L / 2 + 63) / 64 * 64;
+  return t > kNormMaxThreads ? kNormMaxThreads : t;
+}
+
+LMOE_DEV float sq_acc(float ss, float2 v) { return __builtin_fmaf(v.y, v.y, __builtin_fmaf(v.x, v.x, ss)); }
+
+// Sum of v over the workgroup (wavefronts in index order); every thread gets the total.
+LMOE_DEV float block_sum(float v, float* s_part) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = v;
+  lds_sync();   // the z stores before it need not complete
+  float t = s_part[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) t += s_part[w];
+  return t;
+}
+
+LMOE_DEV float2 gamma2(const void* gamma, int gamma_bf16, int c) {
+  if (!gamma) return make_float2(1.0f, 1.0f);
+  if (gamma_bf16) {
+    const uint16_t* g = reinterpret_cast<const uint16_t*>(gamma) + c;
+    return make_float2(bf16_to_f32(g[0]), bf16_to_f32(g[1]));
+  }
+  const float* g = reinterpret_cast<const float*>(gamma) + c;
+  return make_float2(g[0], g[1]);
+}
+
+// out[c], out[c + 1] = v * r * gamma (gamma applied only when present, as in the oracle).
+LMOE_DEV void store_norm2(void* out, int out_bf16, size_t idx, float2 v, float r, const void* gamma, int gamma_bf16,
+                          int c) {
+  float o0 = v.x * r, o1 = v.y * r;
+  if (gamma) {
+    const float2 g = gamma2(gamma, gamma_bf16, c);
+    o0 *= g.x;
+    o1 *= g.y;
+  }
+  if (out_bf16)
+    *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(out) + idx) =
+        (uint32_t)f32_to_bf16(o0) | ((uint32_t)f32_to_bf16(o1) << 16);
+  else
+    *reinterpret_cast<float2*>(reinterpret_cast<float*>(out) + idx) = make_float2(o0, o1);
+}
+
+__global__ __launch_bounds__(kNormMaxThreads) void rmsnorm_kernel(int L, const float* __restrict__ z,
+                                                                  const void* __restrict__ gamma, int gamma_bf16,
+                                                                  float eps, int out_bf16, void* __restrict__ out) {
+  __shared__ float s_part[kNormMaxThreads / 64];
   const int t = blockIdx.x;
+  const int step = 2 * blockDim.x;
   const float* row = z + (size_t)t * L;
   float ss = 0.0f;
-  for (int i = threadIdx.x * 4; i < L; i += 256 * 4) {
-    const float4 v = *reinterpret_cast<const float4*>(row + i);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-  }
-  ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float tot = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+  for (int c = 2 * threadIdx.x; c < L; c += step) ss = sq_acc(ss, *reinterpret_cast<const float2*>(row + c));
+  const float tot = block_sum(ss, s_part);
   const float r = 1.0f / sqrtf(tot / (float)L + eps);
-  for (int i = threadIdx.x * 4; i < L; i += 256 * 4) {
-    const float4 v = *reinterpret_cast<const float4*>(row + i);
-    float o[4] = {v.x * r, v.y * r, v.z * r, v.w * r};
-    if (gamma) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        o[q] *= gamma_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(gamma)[i + q])
-                           : reinterpret_cast<const float*>(gamma)[i + q];
-    }
-    if (out_bf16) {
-      uint2 p;
-      p.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
-      p.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
-      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + (size_t)t * L + i) = p;
-    } else {
-      *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + (size_t)t * L + i) =
-          make_float4(o[0], o[1], o[2], o[3]);
-    }
-  }
+  for (int c = 2 * threadIdx.x; c < L; c += step)
+    store_norm2(out, out_bf16, (size_t)t * L + c, *reinterpret_cast<const float2*>(row + c), r, gamma, gamma_bf16, c);
 }
 
 // ---- combine + latent RMSNorm in one pass per token: z[t, :] = sum_{k ascending} ws[t*K + k, :]
-// (stored fp32), then n = z / sqrt(mean(z^2) + eps) * gamma with the summation order of
-// rmsnorm_kernel, so both routes give the same bits. Each thread reads back only the z
-// values it wrote itself.
-__global__ __launch_bounds__(256) void combine_norm_kernel(int K, int L, const float* __restrict__ ws,
-                                                           float* __restrict__ z, const void* __restrict__ gamma,
-                                                           int gamma_bf16, float eps, int out_bf16,
-                                                           void* __restrict__ out) {
-  __shared__ float s_part[4];
+// (stored fp32, the same additions as combine_kernel), then the RMSNorm of rmsnorm_kernel.
+// A thread requests the K products of its column pair together (up to 16 at a time), so a
+// decode-sized batch pays one memory round trip for the whole combine; z is kept in
+// registers for the normalization (re-read, own writes only, past kNormKeep pairs).
+__global__ __launch_bounds__(kNormMaxThreads) void combine_norm_kernel(int K, int L, const float* __restrict__ ws,
+                                                                       float* __restrict__ z,
+                                                                       const void* __restrict__ gamma, int gamma_bf16,
+                                                                       float eps, int out_bf16,
+                                                                       void* __restrict__ out) {
+  __shared__ float s_part[kNormMaxThreads / 64];
   const int t = blockIdx.x;
+  const int step = 2 * blockDim.x;
   float* zrow = z + (size_t)t * L;
   const float* src = ws + (size_t)t * K * L;
-  float ss = 0.0f;
-  for (int i = threadIdx.x * 4; i < L; i += 256 * 4) {
-    // the K products are requested 8 at a time and then added in k order
-    float4 v = *reinterpret_cast<const float4*>(src + i);
-    for (int k0 = 1; k0 < K; k0 += 8) {
-      float4 u[8];
+  auto combine = [&](int c) {
+    float2 v = *reinterpret_cast<const float2*>(src + c);
+    for (int k0 = 1; k0 < K; k0 += 16) {
+      float2 u[16];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (k0 + j < K) u[j] = *reinterpret_cast<const float4*>(src + (size_t)(k0 + j) * L + i);
+      for (int j = 0; j < 16; ++j)
+        if (k0 + j < K) u[j] = *reinterpret_cast<const float2*>(src + (size_t)(k0 + j) * L + c);
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < 16; ++j)
         if (k0 + j < K) {
-          v.x += u[j].x; v.y += u[j].y; v.z += u[j].z; v.w += u[j].w;
+          v.x += u[j].x;
+          v.y += u[j].y;
         }
     }
-    *reinterpret_cast<float4*>(zrow + i) = v;
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-  }
-  ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float tot = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
-  const float r = 1.0f / sqrtf(tot / (float)L + eps);
-  for (int i = threadIdx.x * 4; i < L; i += 256 * 4) {
-    const float4 v = *reinterpret_cast<const float4*>(zrow + i);
-    float o[4] = {v.x * r, v.y * r, v.z * r, v.w * r};
-    if (gamma) {
+    *reinterpret_cast<float2*>(zrow + c) = v;
+    return v;
+  };
+  float2 keep[kNormKeep];
+  float ss = 0.0f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        o[q] *= gamma_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(gamma)[i + q])
-                           : reinterpret_cast<const float*>(gamma)[i + q];
-    }
-    if (out_bf16) {
-      uint2 p;
-      p.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
-      p.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
-      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + (size_t)t * L + i) = p;
-    } else {
-      *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + (size_t)t * L + i) =
-          make_float4(o[0], o[1], o[2], o[3]);
-    }
+  for (int it = 0; it < kNormKeep; ++it) {
+    const int c = 2 * threadIdx.x + step * it;
+    keep[it] = c < L ? combine(c) : make_float2(0.0f, 0.0f);
+    if (c < L) ss = sq_acc(ss, keep[it]);
   }
+  for (int c = 2 * threadIdx.x + step * kNormKeep; c < L; c += step) ss = sq_acc(ss, combine(c));
+  const float tot = block_sum(ss, s_part);
+  const float r = 1.0f / sqrtf(tot / (float)L + eps);
+#pragma unroll
+  for (int it = 0; it < kNormKeep; ++it) {
+    const int c = 2 * threadIdx.x + step * it;
+    if (c < L) store_norm2(out, out_bf16, (size_t)t * L + c, keep[it], r, gamma, gamma_bf16, c);
+  }
+  for (int c = 2 * threadIdx.x + step * kNormKeep; c < L; c += step)
+    store_norm2(out, out_bf16, (size_t)t * L + c, *reinterpret_cast<const float2*>(zrow + c), r, gamma, gamma_bf16,
+                c);
 }
 
 hipError_t launch_combine_norm(int T, int K, int L, const float* ws, float* z, const void* gamma, float eps, Elt elt,
                                void* out, hipStream_t stream) {
+  if (L % 2 != 0) return hipErrorInvalidValue;
   const int bf = elt == Elt::BF16 ? 1 : 0;
-  hipLaunchKernelGGL(combine_norm_kernel, dim3(T), dim3(256), 0, stream, K, L, ws, z, gamma, bf, eps, bf, out);
+  hipLaunchKernelGGL(combine_norm_kernel, dim3(T), dim3(norm_threads(L)), 0, stream, K, L, ws, z, gamma, bf, eps, bf,
+                     out);
   return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm(int T, int L, const float* z, const void* gamma, float eps, Elt elt, void* out,
                           hipStream_t stream) {
+  if (L % 2 != 0) return hipErrorInvalidValue;
   const int bf = elt == Elt::BF16 ? 1 : 0;
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(256), 0, stream, L, z, gamma, bf, eps, bf, out);
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(norm_threads(L)), 0, stream, L, z, gamma, bf, eps, bf, out);
   return hipGetLastError();
 }
 

@@ -11,7 +11,7 @@
 // instruction, which streams HBM at full rate where row-major 64-byte pieces do not);
 // piece q feeds one v_mfma_f32_16x16x32_bf16 (or four v_mfma_f32_16x16x4_f32) covering
 // chunk elements [32q, 32q + 32) in the same order for A and B. The next chunk's loads
-// are issued before the current chunk's MFMAs. Up to 8 wavefronts of a workgroup split the K range; their fp32
+// (and up to D - 1 further chunks) are issued before the current chunk's MFMAs. Up to 8 wavefronts of a workgroup split the K range; their fp32
 // partial tiles are summed in LDS in fixed wave order (deterministic), and wave 0 runs
 // the fused epilogue: plain store, SituGLU (vLLM PR 50088, commit 2: gate = first d
 // columns, up = last d), weighted per-pair store for the combine (TensorRT-LLM PR
@@ -105,9 +105,14 @@ LMOE_DEV float load_elt(Elt elt, const void* base, size_t idx) {
                          : bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
 }
 
-template <Elt ELT, int NT, bool DUAL>
-__global__ __launch_bounds__(512) void stream_gemm_kernel(const StreamGemm g, int blocks_total, int nch0,
+// MB (several blocks per wave): one segment, no split-K, no second phase. The wave walks
+// nbw consecutive column blocks of its row tile; its ring runs on across block boundaries
+// (the next block's first chunks are requested while the current block finishes), and
+// each block's epilogue runs as soon as its last chunk has been consumed.
+template <Elt ELT, int NT, bool DUAL, int D, bool MB>
+__global__ __launch_bounds__(512) void stream_gemm_kernel(const StreamGemm g, int groups_total, int nbw, int nch0,
                                                           int nch1) {
+  static_assert(!(MB && DUAL), "several blocks per wave: single phase only");
   using TR = EltTraits<ELT>;
   constexpr int CB = TR::KCH * TR::BYTES;   // bytes per chunk row (256)
   constexpr int NACC = DUAL ? 2 * NT : NT;
@@ -115,8 +120,8 @@ __global__ __launch_bounds__(512) void stream_gemm_kernel(const StreamGemm g, in
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   const int splits = blockDim.x >> 6;
-  const int mt = blockIdx.x / blocks_total;
-  const int nb_all = blockIdx.x - mt * blocks_total;
+  const int mt = blockIdx.x / groups_total;
+  const int nb_all = (blockIdx.x - mt * groups_total) * nbw;   // first column block of this workgroup
   const int row0 = mt * 16;
   if (row0 >= g.M) return;
 
@@ -127,6 +132,7 @@ __global__ __launch_bounds__(512) void stream_gemm_kernel(const StreamGemm g, in
     if (i < g.nseg && nb_all >= g.seg[i].block0) s = i;
   const Seg sg = g.seg[s];
   const int nb = nb_all - sg.block0;
+  const int nblk = MB ? min(nbw, sg.blocks - nb) : 1;
   const bool situ = sg.epi == Epi::SITU;
 
   const bool grouped = g.row_to_pair != nullptr;
@@ -148,10 +154,12 @@ __global__ __launch_bounds__(512) void stream_gemm_kernel(const StreamGemm g, in
     for (int i = 0; i < 4; ++i) pair_o[i] = g.row_to_pair[row0 + 4 * g4 + i];
   }
 
-  // ---- weight tiles: start of tile j's row group in the packed layout, plus the lane's 16 bytes
+  // ---- weight tiles: start of tile j's row group in the packed layout, plus the lane's 16 bytes.
+  // The next column block's tiles start bstride bytes further (half or NT row groups on).
   const int half = NT / 2;
   const uint32_t w_bytes = (uint32_t)sg.n_total * (uint32_t)(g.Kd * TR::BYTES);   // one expert
   const rsrc_t w_rs = make_rsrc(reinterpret_cast<const char*>(sg.w) + (size_t)e * w_bytes, w_bytes);
+  const uint32_t bstride = (uint32_t)(situ ? half : NT) * (uint32_t)nch0 * 4096u;
   uint32_t b_off[NT], b1_off[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
@@ -175,14 +183,14 @@ __global__ __launch_bounds__(512) void stream_gemm_kernel(const StreamGemm g, in
   const int v0 = (int)((long)nch * wu / splits);
   const int v1 = (int)((long)nch * (wu + 1) / splits);
 
-  Chunk a0, a1, b0[NT], b1[NT];
+  Chunk a[D], b[D][NT];   // ring of D chunks in flight
   if (v0 < v1) {   // first weight chunk (phase 0 unless the range starts in phase 1)
     if (!DUAL || v0 < nch0) {
 #pragma unroll
-      for (int j = 0; j < NT; ++j) b0[j] = load_chunk_w(w_rs, b_off[j], (uint32_t)v0 * 4096u);
+      for (int j = 0; j < NT; ++j) b[0][j] = load_chunk_w(w_rs, b_off[j], (uint32_t)v0 * 4096u);
     } else {
 #pragma unroll
-      for (int j = 0; j < NT; ++j) b0[j] = load_chunk_w(w1_rs, b1_off[j], (uint32_t)(v0 - nch0) * 4096u);
+      for (int j = 0; j < NT; ++j) b[0][j] = load_chunk_w(w1_rs, b1_off[j], (uint32_t)(v0 - nch0) * 4096u);
     }
   }
 
@@ -212,50 +220,147 @@ __global__ __launch_bounds__(512) void stream_gemm_kernel(const StreamGemm g, in
 #pragma unroll
   for (int j = 0; j < NACC; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  auto issue = [&](int v, Chunk& a, Chunk (&b)[NT]) {
-    if (!DUAL || v < nch0) {
-      a = load_chunk_a(a_rs, a_off, (uint32_t)v * CB);
+  // ---- epilogue of column block nbk: lane holds rows row0 + 4*g4 + i, column (tile j) ... + m
+  auto epilogue = [&](int nbk) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < NT; ++j) b[j] = load_chunk_w(w_rs, b_off[j], (uint32_t)v * 4096u);
-    } else {
-      const uint32_t c = (uint32_t)(v - nch0);
-      a = load_chunk_a(a1_rs, a1_off, c * CB);
+    for (int i = 0; i < 4; ++i) {
+      const int orow = row0 + 4 * g4 + i;
+      int pair = -1;
+      if (grouped) {
+        pair = pair_o[i];
+        if (pair < 0) continue;
+      } else {
+        if (orow >= g.M) continue;
+        pair = orow;
+      }
+      if (situ) {
+        const float inv_b = 1.0f / g.beta;
+        const float inv_lb = g.lbeta > 0.0f ? 1.0f / g.lbeta : 0.0f;
 #pragma unroll
-      for (int j = 0; j < NT; ++j) b[j] = load_chunk_w(w1_rs, b1_off[j], c * 4096u);
-    }
-  };
-  auto consume = [&](int v, const Chunk& a, const Chunk (&b)[NT]) {
-    if (!DUAL || v < nch0) {
+        for (int j = 0; j < half; ++j) {
+          const int col = nbk * half * 16 + j * 16 + m;
+          if (col >= sg.n_out) continue;   // partial last block of the segment
+          const float v = situ_f(acc[j][i], acc[j + half][i], g.beta, inv_b, g.lbeta, inv_lb);
+          store_elt(sg.out_elt, sg.out, (size_t)orow * sg.ldo + col, v);
+        }
+      } else {
 #pragma unroll
-      for (int j = 0; j < NT; ++j) acc[j] = mfma_chunk<ELT>(a, b[j], acc[j]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < NT; ++j) acc[NT + j] = mfma_chunk<ELT>(a, b[j], acc[NT + j]);
+        for (int j = 0; j < NT; ++j) {
+          const int col = nbk * NT * 16 + j * 16 + m;
+          if (col >= sg.n_out) continue;   // partial last block of the segment
+          float v = acc[j][i];
+          if (sg.epi == Epi::STORE) {
+            store_elt(sg.out_elt, sg.out, (size_t)orow * sg.ldo + col, v);
+          } else if (sg.epi == Epi::PAIR) {
+            const float wgt = g.pair_w ? g.pair_w[pair] : 1.0f;
+            reinterpret_cast<float*>(sg.out)[(size_t)pair * sg.ldo + col] = wgt * v;
+          } else if (sg.epi == Epi::TOKEN) {
+            const float wgt = g.pair_w ? g.pair_w[pair] : 1.0f;
+            store_elt(sg.out_elt, sg.out, (size_t)(pair / g.topk) * sg.ldo + col, wgt * v);
+          } else if (sg.epi == Epi::ADD) {
+            const size_t idx = (size_t)orow * sg.ldo + col;
+            const float add = g.add ? load_elt(sg.out_elt, g.add, idx) : 0.0f;
+            store_elt(sg.out_elt, sg.out, idx, add + v);
+          } else if (DUAL) {   // ADD2: the first phase's result rounded to the output type, plus the second's
+            if (sg.out_elt == Elt::BF16) v = bf16_to_f32(f32_to_bf16(v));
+            store_elt(sg.out_elt, sg.out, (size_t)orow * sg.ldo + col, v + acc[NT + j][i]);
+          }
+        }
+      }
     }
   };
 
-  // Ping-pong buffers: chunk v + 1 is requested before chunk v is consumed. The request
-  // index is clamped to the wave's last chunk, so the final requests re-read a chunk that
-  // is still cached instead of running past the range; they are never consumed.
-  // sched_barrier keeps the compiler from sinking the requests below the MFMAs that
-  // consume the older buffer (which would serialize every chunk on memory latency).
+  // Operands of chunk c (K chunk of the phase) of column block ib; the phase is wave-uniform,
+  // so the selects below are scalar, and the block enters through the scalar offset.
+  auto issue_at = [&](bool p1, uint32_t c, uint32_t ib, Chunk& ca, Chunk (&cb)[NT]) __attribute__((always_inline)) {
+    ca = load_chunk_a(p1 ? a1_rs : a_rs, p1 ? a1_off : a_off, c * CB);
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      cb[j] = load_chunk_w(p1 ? w1_rs : w_rs, p1 ? b1_off[j] : b_off[j], c * 4096u + ib * bstride);
+  };
+  auto issue = [&](int v, Chunk& ca, Chunk (&cb)[NT]) __attribute__((always_inline)) {
+    const bool p1 = DUAL && v >= nch0;
+    issue_at(p1, (uint32_t)(p1 ? v - nch0 : v), 0u, ca, cb);
+  };
+  auto consume = [&](int v, const Chunk& ca, const Chunk (&cb)[NT]) __attribute__((always_inline)) {
+    if (!DUAL || v < nch0) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[j] = mfma_chunk<ELT>(ca, cb[j], acc[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[NT + j] = mfma_chunk<ELT>(ca, cb[j], acc[NT + j]);
+    }
+  };
+
+  // Ring of D chunk buffers: the chunk D - 1 places ahead is requested before the current
+  // chunk is consumed. The request position stops at the wave's last chunk, so the final
+  // requests re-read a chunk that is still cached instead of running past the range; they
+  // are never consumed. sched_barrier keeps the compiler from sinking the requests below the
+  // MFMAs that consume the older buffers (which would serialize every chunk on memory latency).
+  if (MB) {
+    // (ib, ic): next chunk to request; (cbk, cc): next chunk to consume. v0 = 0, v1 = nch0.
+    a[0] = load_chunk_a(a_rs, a_off, 0u);
+    int ib = 0, ic = 0;
+    auto advance = [&]() __attribute__((always_inline)) {
+      if (++ic == nch0) {
+        if (ib + 1 < nblk) {
+          ++ib;
+          ic = 0;
+        } else {
+          ic = nch0 - 1;
+        }
+      }
+    };
+    advance();
+    static_for<D - 2>([&](auto i) {
+      constexpr int sl = decltype(i)::value + 1;
+      issue_at(false, (uint32_t)ic, (uint32_t)ib, a[sl], b[sl]);
+      advance();
+    });
+    int cbk = 0, cc = 0;
+    bool more = true;
+    while (more) {
+      static_for<D>([&](auto i) {
+        constexpr int sl = decltype(i)::value;
+        if (!more) return;
+        issue_at(false, (uint32_t)ic, (uint32_t)ib, a[(sl + D - 1) % D], b[(sl + D - 1) % D]);
+        advance();
+        __builtin_amdgcn_sched_barrier(0);
+        consume(0, a[sl], b[sl]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (++cc == nch0) {
+          epilogue(nb + cbk);
+#pragma unroll
+          for (int j = 0; j < NACC; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+          cc = 0;
+          if (++cbk >= nblk) more = false;
+        }
+      });
+    }
+    return;
+  }
+
   if (v0 < v1) {
     if (!DUAL || v0 < nch0)
-      a0 = load_chunk_a(a_rs, a_off, (uint32_t)v0 * CB);
+      a[0] = load_chunk_a(a_rs, a_off, (uint32_t)v0 * CB);
     else
-      a0 = load_chunk_a(a1_rs, a1_off, (uint32_t)(v0 - nch0) * CB);
+      a[0] = load_chunk_a(a1_rs, a1_off, (uint32_t)(v0 - nch0) * CB);
+    static_for<D - 2>([&](auto i) {
+      constexpr int sl = decltype(i)::value + 1;
+      issue(min(v0 + sl, v1 - 1), a[sl], b[sl]);
+    });
     int v = v0;
-    while (true) {
-      issue(min(v + 1, v1 - 1), a1, b1);
-      __builtin_amdgcn_sched_barrier(0);
-      consume(v, a0, b0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (++v >= v1) break;
-      issue(min(v + 1, v1 - 1), a0, b0);
-      __builtin_amdgcn_sched_barrier(0);
-      consume(v, a1, b1);
-      __builtin_amdgcn_sched_barrier(0);
-      if (++v >= v1) break;
+    bool more = true;
+    while (more) {
+      static_for<D>([&](auto i) {
+        constexpr int sl = decltype(i)::value;
+        if (!more) return;
+        issue(min(v + D - 1, v1 - 1), a[(sl + D - 1) % D], b[(sl + D - 1) % D]);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(v, a[sl], b[sl]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (++v >= v1) more = false;
+      });
     }
   }
 
@@ -276,63 +381,28 @@ __global__ __launch_bounds__(512) void stream_gemm_kernel(const StreamGemm g, in
         acc[j][i] = t;
       }
   }
+  epilogue(nb);
+}
 
-  // ---- epilogue: lane holds rows row0 + 4*g4 + i, column (tile j) ... + m
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int orow = row0 + 4 * g4 + i;
-    int pair = -1;
-    if (grouped) {
-      pair = pair_o[i];
-      if (pair < 0) continue;
-    } else {
-      if (orow >= g.M) continue;
-      pair = orow;
-    }
-    if (situ) {
-      const float inv_b = 1.0f / g.beta;
-      const float inv_lb = g.lbeta > 0.0f ? 1.0f / g.lbeta : 0.0f;
-#pragma unroll
-      for (int j = 0; j < half; ++j) {
-        const int col = nb * half * 16 + j * 16 + m;
-        if (col >= sg.n_out) continue;   // partial last block of the segment
-        const float v = situ_f(acc[j][i], acc[j + half][i], g.beta, inv_b, g.lbeta, inv_lb);
-        store_elt(sg.out_elt, sg.out, (size_t)orow * sg.ldo + col, v);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const int col = nb * NT * 16 + j * 16 + m;
-        if (col >= sg.n_out) continue;   // partial last block of the segment
-        float v = acc[j][i];
-        if (sg.epi == Epi::STORE) {
-          store_elt(sg.out_elt, sg.out, (size_t)orow * sg.ldo + col, v);
-        } else if (sg.epi == Epi::PAIR) {
-          const float wgt = g.pair_w ? g.pair_w[pair] : 1.0f;
-          reinterpret_cast<float*>(sg.out)[(size_t)pair * sg.ldo + col] = wgt * v;
-        } else if (sg.epi == Epi::TOKEN) {
-          const float wgt = g.pair_w ? g.pair_w[pair] : 1.0f;
-          store_elt(sg.out_elt, sg.out, (size_t)(pair / g.topk) * sg.ldo + col, wgt * v);
-        } else if (sg.epi == Epi::ADD) {
-          const size_t idx = (size_t)orow * sg.ldo + col;
-          const float add = g.add ? load_elt(sg.out_elt, g.add, idx) : 0.0f;
-          store_elt(sg.out_elt, sg.out, idx, add + v);
-        } else if (DUAL) {   // ADD2: the first phase's result rounded to the output type, plus the second's
-          if (sg.out_elt == Elt::BF16) v = bf16_to_f32(f32_to_bf16(v));
-          store_elt(sg.out_elt, sg.out, (size_t)orow * sg.ldo + col, v + acc[NT + j][i]);
-        }
-      }
-    }
-  }
+// Chunks in flight per wave (the ring depth).
+template <int NT>
+constexpr int depth_of() {
+  return 2;
 }
 
 template <Elt ELT, int NT>
-static void launch_nt(bool dual, dim3 grid, dim3 block, size_t lds, hipStream_t stream, const StreamGemm& g,
-                      int blocks_total, int nch0, int nch1) {
+static void launch_nt(bool dual, int nbw, dim3 grid, dim3 block, size_t lds, hipStream_t stream, const StreamGemm& g,
+                      int groups_total, int nch0, int nch1) {
+  constexpr int D = depth_of<NT>();
   if (dual)
-    hipLaunchKernelGGL((stream_gemm_kernel<ELT, NT, true>), grid, block, lds, stream, g, blocks_total, nch0, nch1);
+    hipLaunchKernelGGL((stream_gemm_kernel<ELT, NT, true, D, false>), grid, block, lds, stream, g, groups_total, 1,
+                       nch0, nch1);
+  else if (nbw > 1)
+    hipLaunchKernelGGL((stream_gemm_kernel<ELT, NT, false, D, true>), grid, block, lds, stream, g, groups_total, nbw,
+                       nch0, nch1);
   else
-    hipLaunchKernelGGL((stream_gemm_kernel<ELT, NT, false>), grid, block, lds, stream, g, blocks_total, nch0, nch1);
+    hipLaunchKernelGGL((stream_gemm_kernel<ELT, NT, false, D, false>), grid, block, lds, stream, g, groups_total, 1,
+                       nch0, nch1);
 }
 
 // Waves a launch aims for (8 per CU). More, thinner waves measured slower: each wave
@@ -350,7 +420,8 @@ static hipError_t launch_elt(StreamGemm g, int live, hipStream_t stream) {
   // Columns per wave: NT tiles of 16 (a SituGLU segment pairs NT/2 gate tiles with their
   // up tiles; a segment's last block may be partial). Take the largest NT that still gives
   // kTargetWaves live waves, else the smallest allowed; then split K over up to 8 waves of
-  // a workgroup to reach that count.
+  // a workgroup to reach that count. With more live waves than the target (one segment, one
+  // phase), a wave takes several consecutive column blocks instead.
   bool any_situ = false;
   for (int i = 0; i < g.nseg; ++i) any_situ |= g.seg[i].epi == Epi::SITU;
   auto blocks_of = [&](int i, int NT) {
@@ -375,12 +446,18 @@ static hipError_t launch_elt(StreamGemm g, int live, hipStream_t stream) {
   int splits = (int)((kTargetWaves + (long)live * blocks_total - 1) / ((long)live * blocks_total));
   splits = splits < 1 ? 1 : (splits > 8 ? 8 : splits);
   if (splits > nch0 + nch1) splits = nch0 + nch1;
-  const dim3 grid((unsigned)(m_tiles * blocks_total)), block(64 * splits);
+  int nbw = 1;
+  if (splits == 1 && !dual && g.nseg == 1) {
+    nbw = (int)((long)live * blocks_total / kTargetWaves);
+    nbw = nbw < 1 ? 1 : (nbw > blocks_total ? blocks_total : nbw);
+  }
+  const int groups_total = (blocks_total + nbw - 1) / nbw;
+  const dim3 grid((unsigned)(m_tiles * groups_total)), block(64 * splits);
   const size_t lds = splits > 1 ? (size_t)splits * (dual ? 2 : 1) * NT * 4 * 64 * sizeof(float) : 0;
   switch (NT) {
-    case 1: launch_nt<ELT, 1>(dual, grid, block, lds, stream, g, blocks_total, nch0, nch1); break;
-    case 2: launch_nt<ELT, 2>(dual, grid, block, lds, stream, g, blocks_total, nch0, nch1); break;
-    default: launch_nt<ELT, 4>(dual, grid, block, lds, stream, g, blocks_total, nch0, nch1); break;
+    case 1: launch_nt<ELT, 1>(dual, nbw, grid, block, lds, stream, g, groups_total, nch0, nch1); break;
+    case 2: launch_nt<ELT, 2>(dual, nbw, grid, block, lds, stream, g, groups_total, nch0, nch1); break;
+    default: launch_nt<ELT, 4>(dual, nbw, grid, block, lds, stream, g, groups_total, nch0, nch1); break;
   }
   return hipGetLastError();
 }

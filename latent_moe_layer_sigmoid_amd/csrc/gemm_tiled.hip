@@ -24,8 +24,6 @@
 #include "common.h"
 #include "kernels.h"
 
-#include <utility>
-
 namespace lmoe {
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -51,17 +49,6 @@ LMOE_DEV void store_out(Elt elt, void* base, size_t idx, float v) {
     reinterpret_cast<float*>(base)[idx] = v;
   else
     reinterpret_cast<uint16_t*>(base)[idx] = f32_to_bf16(v);
-}
-
-// Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1, so that register
-// arrays indexed by I stay in registers.
-template <typename F, int... I>
-LMOE_DEV void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-LMOE_DEV void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // A wave-uniform copy of a pointer / value (kept in scalar registers, so that buffer

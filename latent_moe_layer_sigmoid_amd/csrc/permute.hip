@@ -9,6 +9,8 @@
 // lanes, and the per-wave counts in LDS give the offset of each earlier wave.
 //   1 block  : one fused kernel (count, scan, rank, scatter).
 //   >1 blocks: count per block -> one-block scan over (expert, block) -> rank + scatter.
+// Threads of a workgroup share data through LDS only, so its barriers order LDS alone (the
+// global outputs are read by later launches).
 // Decode-sized batches (T <= 16 tokens, T*K <= 1024 pairs) can also run routing and the
 // permutation as one workgroup: wavefront t routes token t (TensorRT-LLM PR 20541,
 // "Commit 1": the routing kernel writes the workspace FC1 / FC2 read), the ids stay in LDS
@@ -47,7 +49,7 @@ LMOE_DEV int block_exclusive_scan(int v, int* s_wave, int* total) {
     if (lane >= off) x += y;
   }
   if (lane == 63) s_wave[w] = x;
-  __syncthreads();
+  lds_sync();
   if (w == 0) {
     int s = lane < PW ? s_wave[lane] : 0;
 #pragma unroll
@@ -57,10 +59,10 @@ LMOE_DEV int block_exclusive_scan(int v, int* s_wave, int* total) {
     }
     if (lane < PW) s_wave[lane] = s;   // inclusive per-wave totals
   }
-  __syncthreads();
+  lds_sync();
   const int before = (w ? s_wave[w - 1] : 0) + x - v;
   *total = s_wave[PW - 1];
-  __syncthreads();
+  lds_sync();
   return before;
 }
 
@@ -109,11 +111,11 @@ LMOE_DEV void rank_scatter(const int32_t* ids, int npairs, int E, int nbits, int
   const int p = block0 + threadIdx.x;
   const int e = p < npairs ? ids[p] : -1;
   for (int i = threadIdx.x; i < PW * E; i += PB) s_wcnt[i] = 0;
-  __syncthreads();
+  lds_sync();
   const uint64_t m = match_lanes(e, nbits);
   const int r_in_wave = lanes_below(m, lane);
   if (e >= 0 && r_in_wave == 0) s_wcnt[w * E + e] = (unsigned short)__popcll(m);
-  __syncthreads();
+  lds_sync();
   if (e >= 0) {
     int r = r_in_wave;
     for (int w2 = 0; w2 < w; ++w2) r += s_wcnt[w2 * E + e];
@@ -141,12 +143,12 @@ __global__ __launch_bounds__(PB) void permute_fused_kernel(int npairs, int E, in
   int* s_scr = s_toff + E;                // [PW]
   unsigned short* s_wcnt = (unsigned short*)(s_scr + PW);   // [PW * E]
   for (int e = threadIdx.x; e < E; e += PB) s_cnt[e] = 0;
-  __syncthreads();
+  lds_sync();
   if ((int)threadIdx.x < npairs) atomicAdd(&s_cnt[ids[threadIdx.x]], 1);
-  __syncthreads();
+  lds_sync();
   scan_experts(s_cnt, E, tile_m, max_tiles, counts, offsets, tile_offsets, row_to_pair, tile_expert,
                s_scr, s_toff);
-  __syncthreads();
+  lds_sync();
   rank_scatter(ids, npairs, E, id_bits(E), 0, s_wcnt, [&](int e) { return s_toff[e]; }, row_to_pair,
                pair_to_row);
 }
@@ -178,12 +180,12 @@ __global__ __launch_bounds__(PB) void route_permute_kernel(int T, int E, int K, 
       s_ids[w * K + lane] = e;
     }
   }
-  __syncthreads();
+  lds_sync();
   if ((int)threadIdx.x < npairs) atomicAdd(&s_cnt[s_ids[threadIdx.x]], 1);
-  __syncthreads();
+  lds_sync();
   scan_experts(s_cnt, E, tile_m, max_tiles, counts, offsets, tile_offsets, row_to_pair, tile_expert,
                s_scr, s_toff);
-  __syncthreads();
+  lds_sync();
   rank_scatter(s_ids, npairs, E, id_bits(E), 0, s_wcnt, [&](int e) { return s_toff[e]; }, row_to_pair,
                pair_to_row);
 }
@@ -221,10 +223,10 @@ __global__ __launch_bounds__(PB) void permute_count_kernel(int npairs, int E, co
                                                            int32_t* __restrict__ block_counts) {
   extern __shared__ int s_cnt[];
   for (int e = threadIdx.x; e < E; e += PB) s_cnt[e] = 0;
-  __syncthreads();
+  lds_sync();
   const int p = blockIdx.x * PB + threadIdx.x;
   if (p < npairs) atomicAdd(&s_cnt[ids[p]], 1);
-  __syncthreads();
+  lds_sync();
   for (int e = threadIdx.x; e < E; e += PB) block_counts[(size_t)blockIdx.x * E + e] = s_cnt[e];
 }
 
@@ -245,7 +247,7 @@ __global__ __launch_bounds__(PB) void permute_scan_kernel(int nblk, int E, int t
     }
     s_cnt[e] = run;
   }
-  __syncthreads();
+  lds_sync();
   scan_experts(s_cnt, E, tile_m, max_tiles, counts, offsets, tile_offsets, row_to_pair, tile_expert,
                s_scr, nullptr);
 }

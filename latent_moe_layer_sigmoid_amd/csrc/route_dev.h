@@ -61,10 +61,17 @@ LMOE_DEV float route_key(float logit, float bias) {
 // wave-uniform keep_groups mask compete (grouped top-k).
 // Weights: METHOD 0 -- rsf * s / sum(s) over the K winners' unbiased scores (or rsf * s
 // without renorm); METHOD 1 -- softmax of the K winners' bf16 logits.
+//
+// Each lane keeps its sorted keys in a register vector and a head index; a round reads
+// registers at wave-uniform indices only (the winning lane's next key, the winner's logit
+// slot), which compile to relative register moves rather than per-slot selects. The
+// second (expert index) reduction runs only when several lanes hold the top score.
 template <int KPL, int NP, int METHOD = 0>
 LMOE_DEV void route_token(int t, int E, int K, const float* __restrict__ logits, const float* __restrict__ bias,
                           float rsf, int renorm, int* e_out, float* w_out, int group_size = 0,
                           uint64_t keep_groups = ~0ull) {
+  typedef uint32_t u32v __attribute__((ext_vector_type(NP)));
+  typedef float f32v __attribute__((ext_vector_type(NP)));
   const int lane = threadIdx.x & 63;
   const float* row = logits + (size_t)t * E;
 
@@ -76,10 +83,12 @@ LMOE_DEV void route_token(int t, int E, int K, const float* __restrict__ logits,
     lg[j] = row[e];
     bs[j] = (METHOD == 0 && bias) ? bias[e] : 0.0f;
   }
+  f32v vlg;
   uint64_t key[NP];
 #pragma unroll
   for (int j = 0; j < NP; ++j) {
     const int e = lane + 64 * j;
+    vlg[j] = j < KPL ? lg[j] : 0.0f;
     key[j] = 0;   // below every real key; never selected since K <= the competing experts
     const bool competes = e < E && (group_size <= 0 || ((keep_groups >> (e / max(group_size, 1))) & 1ull));
     if (j < KPL && competes) {
@@ -88,28 +97,48 @@ LMOE_DEV void route_token(int t, int E, int K, const float* __restrict__ logits,
     }
   }
   sort_desc<NP>(key);
+  u32v vh, vl;
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    vh[j] = (uint32_t)(key[j] >> 32);
+    vl[j] = (uint32_t)key[j];
+  }
 
+  uint32_t hh = vh[0], ll = vl[0];   // this lane's current head key
+  int head = 0;
   uint32_t my_lo = 0;
   float my_lg = 0.0f;
   for (int k = 0; k < K; ++k) {
-    const uint32_t hh = (uint32_t)(key[0] >> 32), ll = (uint32_t)key[0];
     const uint32_t mh = wave_max_u32(hh);
-    const uint32_t ml = wave_max_u32(hh == mh ? ll : 0u);
-    if (hh == mh && ll == ml) {   // the unique winning lane pops its head
-#pragma unroll
-      for (int j = 0; j + 1 < NP; ++j) key[j] = key[j + 1];
-      key[NP - 1] = 0;
+    const uint64_t tied = __ballot(hh == mh);
+    int wl;
+    uint32_t ml;
+    if (__popcll(tied) == 1) {
+      wl = __ffsll((unsigned long long)tied) - 1;
+      ml = (uint32_t)__builtin_amdgcn_readlane((int)ll, wl);
+    } else {   // equal scores: the larger ~expert (lower expert index) wins
+      ml = wave_max_u32(hh == mh ? ll : 0u);
+      wl = __ffsll((unsigned long long)__ballot(hh == mh && ll == ml)) - 1;
     }
-    // the winner's logit, from the registers of lane (e % 64), slot e / 64 (e is uniform)
+    // the winner's logit: register slot e / 64 of lane e % 64 (both wave-uniform). The slot
+    // index goes through readfirstlane: written directly inside the readlane operand, the
+    // compiler has been seen to drop the vector index (always reading slot 0).
     const uint32_t ew = 0xFFFFFFFFu - ml;
-    const int jw = (int)(ew >> 6);
-    float pick = lg[0];
-#pragma unroll
-    for (int j = 1; j < KPL; ++j) pick = (j == jw) ? lg[j] : pick;
-    const float lw = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pick), (int)(ew & 63)));
+    const int jw = __builtin_amdgcn_readfirstlane((int)(ew >> 6) & (NP - 1));
+    const float xw = vlg[jw];
+    const float lw = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xw), (int)(ew & 63)));
     if (lane == k) {
       my_lo = ml;
       my_lg = lw;
+    }
+    // the winning lane moves its head to its next key
+    const int nxt = __builtin_amdgcn_readlane(head, wl) + 1;
+    const uint32_t nh = nxt < NP ? vh[nxt & (NP - 1)] : 0u;
+    const uint32_t nl = nxt < NP ? vl[nxt & (NP - 1)] : 0u;
+    if (lane == wl) {
+      hh = nh;
+      ll = nl;
+      head = nxt;
     }
   }
   int e = -1;

@@ -372,7 +372,9 @@ def test_pack_weights_layout(B, N, Kd, dt):
                                           (8, 2048, 7168, "bf16", "bf16"), (17, 48, 256, "bf16", "bf16"),
                                           (4, 16, 256, "f32", "f32"), (33, 128, 192, "f32", "f32"),
                                           (200, 64, 384, "bf16", "f32"), (300, 400, 640, "bf16", "bf16"),
-                                          (256, 128, 128, "bf16", "f32")])
+                                          (256, 128, 128, "bf16", "f32"),
+                                          # several column blocks per wave, partial last group
+                                          (240, 17600, 384, "bf16", "bf16"), (200, 20240, 64, "f32", "f32")])
 def test_linear_matches_oracle(B, M, N, Kd, dt, yt):
     rng = np.random.default_rng(M + N + Kd)
     td = torch.bfloat16 if dt == "bf16" else torch.float32
@@ -408,7 +410,10 @@ def _expert_case(B, T, E, K, L, d, tile_m, dt, seed):
 @pytest.mark.parametrize("T,E,K,L,d,tile_m,dt", [(4, 16, 4, 128, 64, 16, "f32"), (8, 64, 16, 2048, 512, 16, "bf16"),
                                                  (50, 32, 4, 256, 128, 32, "bf16"),
                                                  (300, 16, 2, 256, 128, 128, "bf16"),
-                                                 (600, 64, 8, 1024, 256, 128, "bf16")])
+                                                 (600, 64, 8, 1024, 256, 128, "bf16"),
+                                                 # several column blocks per wave: FC2 (three) and FC1 (two)
+                                                 (256, 64, 8, 2048, 128, 16, "bf16"),
+                                                 (256, 128, 8, 256, 512, 16, "bf16")])
 def test_fc1_fc2_grouped_match_oracle(B, T, E, K, L, d, tile_m, dt):
     c = _expert_case(B, T, E, K, L, d, tile_m, dt, seed=T + E)
     ldt = B.LMOE_BF16 if dt == "bf16" else B.LMOE_F32
