@@ -39,58 +39,74 @@ LMOE_DEV int lanes_below(uint64_t m, int lane) {
   return __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
 }
 
+// Inclusive sum of x over the lanes of the wavefront (lane i gets lanes 0..i): row shifts
+// 1, 2, 4, 8 scan each row of 16 lanes (lanes shifted in from outside the row read 0), then
+// row broadcasts of lanes 15 and 31 add the earlier rows' totals.
+LMOE_DEV int wave_inclusive_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);    // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);    // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);    // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);    // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
 // Block-wide exclusive scan of v over PB threads; returns the prefix and sets *total.
 LMOE_DEV int block_exclusive_scan(int v, int* s_wave, int* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, WAVE);
-    if (lane >= off) x += y;
-  }
+  const int x = wave_inclusive_sum(v);
   if (lane == 63) s_wave[w] = x;
   lds_sync();
   if (w == 0) {
-    int s = lane < PW ? s_wave[lane] : 0;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(s, off, WAVE);
-      if (lane >= off) s += y;
-    }
-    if (lane < PW) s_wave[lane] = s;   // inclusive per-wave totals
+    const int s = wave_inclusive_sum(lane < PW ? s_wave[lane] : 0);
+    if (lane < PW) s_wave[PW + lane] = s;   // inclusive per-wave totals
   }
   lds_sync();
-  const int before = (w ? s_wave[w - 1] : 0) + x - v;
-  *total = s_wave[PW - 1];
+  const int before = (w ? s_wave[PW + w - 1] : 0) + x - v;
+  *total = s_wave[2 * PW - 1];
   lds_sync();
   return before;
 }
 
 // Scan of counts over experts (each thread owns a contiguous range of experts), writing
 // offsets, tile_offsets, pad rows and the tile -> expert map. s_cnt holds counts[E].
+// While every padded row index fits in 16 bits, the two sums (pairs and padded rows)
+// share one scan as the halves of a 32-bit value.
 LMOE_DEV void scan_experts(const int* s_cnt, int E, int tile_m, int max_tiles, int32_t* counts,
                            int32_t* offsets, int32_t* tile_offsets, int32_t* row_to_pair,
                            int32_t* tile_expert, int* s_scratch, int* s_tile_off) {
   const int per = (E + PB - 1) / PB;
   const int e0 = threadIdx.x * per, e1 = min(E, e0 + per);
+  const int tsh = __builtin_ctz(tile_m);   // tile_m is a power of two
+  const int tmask = tile_m - 1;
   int c_sum = 0, p_sum = 0;
   for (int e = e0; e < e1; ++e) {
     const int c = s_cnt[e];
     c_sum += c;
-    p_sum += (c + tile_m - 1) / tile_m * tile_m;
+    p_sum += (c + tmask) & ~tmask;
   }
-  int c_tot, p_tot;
-  int c_pre = block_exclusive_scan(c_sum, s_scratch, &c_tot);
-  int p_pre = block_exclusive_scan(p_sum, s_scratch, &p_tot);
+  int c_tot, p_tot, c_pre, p_pre;
+  if ((long)max_tiles * tile_m < 65536) {
+    int tot;
+    const int pre = block_exclusive_scan((p_sum << 16) | c_sum, s_scratch, &tot);
+    c_pre = pre & 0xFFFF;
+    p_pre = pre >> 16;
+    c_tot = tot & 0xFFFF;
+    p_tot = tot >> 16;
+  } else {
+    c_pre = block_exclusive_scan(c_sum, s_scratch, &c_tot);
+    p_pre = block_exclusive_scan(p_sum, s_scratch, &p_tot);
+  }
   for (int e = e0; e < e1; ++e) {
     const int c = s_cnt[e];
-    const int pc = (c + tile_m - 1) / tile_m * tile_m;
+    const int pc = (c + tmask) & ~tmask;
     counts[e] = c;
     offsets[e] = c_pre;
     tile_offsets[e] = p_pre;
     if (s_tile_off) s_tile_off[e] = p_pre;
     for (int r = p_pre + c; r < p_pre + pc; ++r) row_to_pair[r] = -1;
-    for (int tt = p_pre / tile_m; tt < (p_pre + pc) / tile_m; ++tt) tile_expert[tt] = e;
+    for (int tt = p_pre >> tsh; tt < (p_pre + pc) >> tsh; ++tt) tile_expert[tt] = e;
     c_pre += c;
     p_pre += pc;
   }
@@ -98,7 +114,7 @@ LMOE_DEV void scan_experts(const int* s_cnt, int E, int tile_m, int max_tiles, i
     offsets[E] = c_tot;
     tile_offsets[E] = p_tot;
   }
-  for (int tt = p_tot / tile_m + threadIdx.x; tt < max_tiles; tt += PB) tile_expert[tt] = -1;
+  for (int tt = (p_tot >> tsh) + threadIdx.x; tt < max_tiles; tt += PB) tile_expert[tt] = -1;
 }
 
 // Rank the block's pairs inside their experts (pair order) and scatter them.
@@ -110,7 +126,8 @@ LMOE_DEV void rank_scatter(const int32_t* ids, int npairs, int E, int nbits, int
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int p = block0 + threadIdx.x;
   const int e = p < npairs ? ids[p] : -1;
-  for (int i = threadIdx.x; i < PW * E; i += PB) s_wcnt[i] = 0;
+  const int rows = min(PW, (npairs - block0 + WAVE - 1) / WAVE);   // waves of this block holding pairs
+  for (int i = threadIdx.x; i < rows * E; i += PB) s_wcnt[i] = 0;
   lds_sync();
   const uint64_t m = match_lanes(e, nbits);
   const int r_in_wave = lanes_below(m, lane);
@@ -140,8 +157,8 @@ __global__ __launch_bounds__(PB) void permute_fused_kernel(int npairs, int E, in
   extern __shared__ int smem[];
   int* s_cnt = smem;                      // [E]
   int* s_toff = s_cnt + E;                // [E]
-  int* s_scr = s_toff + E;                // [PW]
-  unsigned short* s_wcnt = (unsigned short*)(s_scr + PW);   // [PW * E]
+  int* s_scr = s_toff + E;                // [2 * PW]
+  unsigned short* s_wcnt = (unsigned short*)(s_scr + 2 * PW);   // [PW * E]
   for (int e = threadIdx.x; e < E; e += PB) s_cnt[e] = 0;
   lds_sync();
   if ((int)threadIdx.x < npairs) atomicAdd(&s_cnt[ids[threadIdx.x]], 1);
@@ -165,8 +182,8 @@ __global__ __launch_bounds__(PB) void route_permute_kernel(int T, int E, int K, 
   const int npairs = T * K;
   int* s_cnt = smem;                      // [E]
   int* s_toff = s_cnt + E;                // [E]
-  int* s_scr = s_toff + E;                // [PW]
-  int* s_ids = s_scr + PW;                // [T * K]
+  int* s_scr = s_toff + E;                // [2 * PW]
+  int* s_ids = s_scr + 2 * PW;            // [T * K]
   unsigned short* s_wcnt = (unsigned short*)(s_ids + npairs);   // [PW * E]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   for (int e = threadIdx.x; e < E; e += PB) s_cnt[e] = 0;
@@ -203,7 +220,7 @@ hipError_t launch_route_permute(int T, int E, int K, const float* logits, const 
     return launch_permute(T * K, E, tile_m, max_tiles, ids, counts, offsets, tile_offsets, row_to_pair,
                           tile_expert, pair_to_row, workspace, stream);
   }
-  const size_t sm = (size_t)(2 * E + PW + T * K) * sizeof(int) + (size_t)PW * E * sizeof(unsigned short);
+  const size_t sm = (size_t)(2 * E + 2 * PW + T * K) * sizeof(int) + (size_t)PW * E * sizeof(unsigned short);
 #define LMOE_RP(KPL, NP)                                                                                    \
   hipLaunchKernelGGL((route_permute_kernel<KPL, NP>), dim3(1), dim3(PB), sm, stream, T, E, K, logits, bias, \
                      rsf, renorm, ids, weights, tile_m, max_tiles, counts, offsets, tile_offsets, row_to_pair, \
@@ -237,7 +254,7 @@ __global__ __launch_bounds__(PB) void permute_scan_kernel(int nblk, int E, int t
                                                           int32_t* row_to_pair, int32_t* tile_expert) {
   extern __shared__ int smem[];
   int* s_cnt = smem;          // [E]
-  int* s_scr = s_cnt + E;     // [PW]
+  int* s_scr = s_cnt + E;     // [2 * PW]
   for (int e = threadIdx.x; e < E; e += PB) {
     int run = 0;
     for (int b = 0; b < nblk; ++b) {
@@ -272,7 +289,7 @@ hipError_t launch_permute(int npairs, int E, int tile_m, int max_tiles, const in
                           int32_t* tile_expert, int32_t* pair_to_row, void* workspace, hipStream_t stream) {
   const int nblk = (npairs + PB - 1) / PB;
   if (nblk <= 1) {
-    const size_t sm = (size_t)(2 * E + PW) * sizeof(int) + (size_t)PW * E * sizeof(unsigned short);
+    const size_t sm = (size_t)(2 * E + 2 * PW) * sizeof(int) + (size_t)PW * E * sizeof(unsigned short);
     hipLaunchKernelGGL(permute_fused_kernel, dim3(1), dim3(PB), sm, stream, npairs, E, tile_m, max_tiles, ids,
                        counts, offsets, tile_offsets, row_to_pair, tile_expert, pair_to_row);
     return hipGetLastError();
@@ -280,7 +297,7 @@ hipError_t launch_permute(int npairs, int E, int tile_m, int max_tiles, const in
   int32_t* block_counts = (int32_t*)workspace;
   hipLaunchKernelGGL(permute_count_kernel, dim3(nblk), dim3(PB), (size_t)E * sizeof(int), stream, npairs, E,
                      ids, block_counts);
-  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(PB), (size_t)(E + PW) * sizeof(int), stream, nblk, E,
+  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(PB), (size_t)(E + 2 * PW) * sizeof(int), stream, nblk, E,
                      tile_m, max_tiles, block_counts, counts, offsets, tile_offsets, row_to_pair, tile_expert);
   hipLaunchKernelGGL(permute_scatter_kernel, dim3(nblk), dim3(PB), (size_t)PW * E * sizeof(unsigned short),
                      stream, npairs, E, ids, block_counts, tile_offsets, row_to_pair, pair_to_row);
