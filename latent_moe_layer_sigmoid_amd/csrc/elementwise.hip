@@ -160,19 +160,45 @@ hipError_t launch_combine(int T, int K, int N, const float* ws, Elt out_elt, voi
 // n = z / sqrt(mean(z^2) + eps) * gamma in fp32; one workgroup per token row.
 //
 // Row layout shared by rmsnorm_kernel and combine_norm_kernel, so that both routes give
-// the same bits: a workgroup of norm_threads(L) threads owns a row; thread i handles the
-// column pairs c = 2i + 2 * nthreads * it (it = 0, 1, ...), accumulates their squares with
-// fmas in that order, and the per-thread sums are added over the wavefront by butterfly and
-// over the wavefronts in index order.
+// the same bits: a workgroup of norm_threads(T, L) threads owns a row; thread i handles the
+// column groups c = VW*i + VW*nthreads*it (it = 0, 1, ...) of VW = norm_vw(T) consecutive
+// columns, accumulates their squares with fmas in that order, and the per-thread sums are
+// added over the wavefront by butterfly and over the wavefronts in index order. Few rows
+// (decode) take two columns per thread, so that a row spreads over up to 1024 threads and
+// a thread's loads are few; many rows take four.
 constexpr int kNormMaxThreads = 1024;
-constexpr int kNormKeep = 4;   // column pairs per thread kept in registers by combine_norm_kernel
+constexpr int kNormKeep = 4;   // column groups per thread kept in registers by combine_norm_kernel
 
-static int norm_threads(int L) {
-  const int t = (L / 2 + 63) / 64 * 64;
+static int norm_vw(int T) { return T < 64 ? 2 : 4; }
+static int norm_threads(int T, int L) {
+  const int vw = norm_vw(T);
+  const int t = (L / vw + 63) / 64 * 64;
   return t > kNormMaxThreads ? kNormMaxThreads : t;
 }
 
-LMOE_DEV float sq_acc(float ss, float2 v) { return __builtin_fmaf(v.y, v.y, __builtin_fmaf(v.x, v.x, ss)); }
+template <int VW>
+struct Vec;
+template <>
+struct Vec<2> {
+  typedef float2 T;
+  LMOE_DEV static float at(const T& v, int q) { return q == 0 ? v.x : v.y; }
+  LMOE_DEV static T zero() { return make_float2(0.f, 0.f); }
+  LMOE_DEV static void add(T& a, const T& b) { a.x += b.x; a.y += b.y; }
+};
+template <>
+struct Vec<4> {
+  typedef float4 T;
+  LMOE_DEV static float at(const T& v, int q) { return q == 0 ? v.x : (q == 1 ? v.y : (q == 2 ? v.z : v.w)); }
+  LMOE_DEV static T zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+  LMOE_DEV static void add(T& a, const T& b) { a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w; }
+};
+
+template <int VW>
+LMOE_DEV float sq_acc(float ss, const typename Vec<VW>::T& v) {
+#pragma unroll
+  for (int q = 0; q < VW; ++q) ss = __builtin_fmaf(Vec<VW>::at(v, q), Vec<VW>::at(v, q), ss);
+  return ss;
+}
 
 // Sum of v over the workgroup (wavefronts in index order); every thread gets the total.
 LMOE_DEV float block_sum(float v, float* s_part) {
@@ -184,114 +210,128 @@ LMOE_DEV float block_sum(float v, float* s_part) {
   return t;
 }
 
-LMOE_DEV float2 gamma2(const void* gamma, int gamma_bf16, int c) {
-  if (!gamma) return make_float2(1.0f, 1.0f);
-  if (gamma_bf16) {
-    const uint16_t* g = reinterpret_cast<const uint16_t*>(gamma) + c;
-    return make_float2(bf16_to_f32(g[0]), bf16_to_f32(g[1]));
+// out[c .. c + VW) = v * r * gamma (gamma applied only when present, as in the oracle).
+template <int VW>
+LMOE_DEV void store_norm(void* out, int out_bf16, size_t idx, const typename Vec<VW>::T& v, float r,
+                         const void* gamma, int gamma_bf16, int c) {
+  float o[VW];
+#pragma unroll
+  for (int q = 0; q < VW; ++q) {
+    o[q] = Vec<VW>::at(v, q) * r;
+    if (gamma)
+      o[q] *= gamma_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(gamma)[c + q])
+                         : reinterpret_cast<const float*>(gamma)[c + q];
   }
-  const float* g = reinterpret_cast<const float*>(gamma) + c;
-  return make_float2(g[0], g[1]);
+  if (out_bf16) {
+    uint16_t* p = reinterpret_cast<uint16_t*>(out) + idx;
+    if (VW == 2) {
+      *reinterpret_cast<uint32_t*>(p) = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+    } else {
+      uint2 w;
+      w.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+      w.y = (uint32_t)f32_to_bf16(o[VW - 2]) | ((uint32_t)f32_to_bf16(o[VW - 1]) << 16);
+      *reinterpret_cast<uint2*>(p) = w;
+    }
+  } else {
+    typename Vec<VW>::T w;
+    float* wf = reinterpret_cast<float*>(&w);
+#pragma unroll
+    for (int q = 0; q < VW; ++q) wf[q] = o[q];
+    *reinterpret_cast<typename Vec<VW>::T*>(reinterpret_cast<float*>(out) + idx) = w;
+  }
 }
 
-// out[c], out[c + 1] = v * r * gamma (gamma applied only when present, as in the oracle).
-LMOE_DEV void store_norm2(void* out, int out_bf16, size_t idx, float2 v, float r, const void* gamma, int gamma_bf16,
-                          int c) {
-  float o0 = v.x * r, o1 = v.y * r;
-  if (gamma) {
-    const float2 g = gamma2(gamma, gamma_bf16, c);
-    o0 *= g.x;
-    o1 *= g.y;
-  }
-  if (out_bf16)
-    *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(out) + idx) =
-        (uint32_t)f32_to_bf16(o0) | ((uint32_t)f32_to_bf16(o1) << 16);
-  else
-    *reinterpret_cast<float2*>(reinterpret_cast<float*>(out) + idx) = make_float2(o0, o1);
-}
-
+template <int VW>
 __global__ __launch_bounds__(kNormMaxThreads) void rmsnorm_kernel(int L, const float* __restrict__ z,
                                                                   const void* __restrict__ gamma, int gamma_bf16,
                                                                   float eps, int out_bf16, void* __restrict__ out) {
+  typedef typename Vec<VW>::T V;
   __shared__ float s_part[kNormMaxThreads / 64];
   const int t = blockIdx.x;
-  const int step = 2 * blockDim.x;
+  const int step = VW * blockDim.x;
   const float* row = z + (size_t)t * L;
   float ss = 0.0f;
-  for (int c = 2 * threadIdx.x; c < L; c += step) ss = sq_acc(ss, *reinterpret_cast<const float2*>(row + c));
+  for (int c = VW * threadIdx.x; c < L; c += step) ss = sq_acc<VW>(ss, *reinterpret_cast<const V*>(row + c));
   const float tot = block_sum(ss, s_part);
   const float r = 1.0f / sqrtf(tot / (float)L + eps);
-  for (int c = 2 * threadIdx.x; c < L; c += step)
-    store_norm2(out, out_bf16, (size_t)t * L + c, *reinterpret_cast<const float2*>(row + c), r, gamma, gamma_bf16, c);
+  for (int c = VW * threadIdx.x; c < L; c += step)
+    store_norm<VW>(out, out_bf16, (size_t)t * L + c, *reinterpret_cast<const V*>(row + c), r, gamma, gamma_bf16, c);
 }
 
 // ---- combine + latent RMSNorm in one pass per token: z[t, :] = sum_{k ascending} ws[t*K + k, :]
 // (stored fp32, the same additions as combine_kernel), then the RMSNorm of rmsnorm_kernel.
-// A thread requests the K products of its column pair together (up to 16 at a time), so a
+// A thread requests the K products of its columns together (up to 16 at a time), so a
 // decode-sized batch pays one memory round trip for the whole combine; z is kept in
-// registers for the normalization (re-read, own writes only, past kNormKeep pairs).
+// registers for the normalization (re-read, own writes only, past kNormKeep groups).
+template <int VW>
 __global__ __launch_bounds__(kNormMaxThreads) void combine_norm_kernel(int K, int L, const float* __restrict__ ws,
                                                                        float* __restrict__ z,
                                                                        const void* __restrict__ gamma, int gamma_bf16,
                                                                        float eps, int out_bf16,
                                                                        void* __restrict__ out) {
+  typedef typename Vec<VW>::T V;
   __shared__ float s_part[kNormMaxThreads / 64];
   const int t = blockIdx.x;
-  const int step = 2 * blockDim.x;
+  const int step = VW * blockDim.x;
   float* zrow = z + (size_t)t * L;
   const float* src = ws + (size_t)t * K * L;
-  auto combine = [&](int c) {
-    float2 v = *reinterpret_cast<const float2*>(src + c);
+  auto combine = [&](int c) __attribute__((always_inline)) {
+    V v = *reinterpret_cast<const V*>(src + c);
     for (int k0 = 1; k0 < K; k0 += 16) {
-      float2 u[16];
+      V u[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j)
-        if (k0 + j < K) u[j] = *reinterpret_cast<const float2*>(src + (size_t)(k0 + j) * L + c);
+        if (k0 + j < K) u[j] = *reinterpret_cast<const V*>(src + (size_t)(k0 + j) * L + c);
 #pragma unroll
       for (int j = 0; j < 16; ++j)
-        if (k0 + j < K) {
-          v.x += u[j].x;
-          v.y += u[j].y;
-        }
+        if (k0 + j < K) Vec<VW>::add(v, u[j]);
     }
-    *reinterpret_cast<float2*>(zrow + c) = v;
+    *reinterpret_cast<V*>(zrow + c) = v;
     return v;
   };
-  float2 keep[kNormKeep];
+  V keep[kNormKeep];
   float ss = 0.0f;
 #pragma unroll
   for (int it = 0; it < kNormKeep; ++it) {
-    const int c = 2 * threadIdx.x + step * it;
-    keep[it] = c < L ? combine(c) : make_float2(0.0f, 0.0f);
-    if (c < L) ss = sq_acc(ss, keep[it]);
+    const int c = VW * threadIdx.x + step * it;
+    keep[it] = c < L ? combine(c) : Vec<VW>::zero();
+    if (c < L) ss = sq_acc<VW>(ss, keep[it]);
   }
-  for (int c = 2 * threadIdx.x + step * kNormKeep; c < L; c += step) ss = sq_acc(ss, combine(c));
+  for (int c = VW * threadIdx.x + step * kNormKeep; c < L; c += step) ss = sq_acc<VW>(ss, combine(c));
   const float tot = block_sum(ss, s_part);
   const float r = 1.0f / sqrtf(tot / (float)L + eps);
 #pragma unroll
   for (int it = 0; it < kNormKeep; ++it) {
-    const int c = 2 * threadIdx.x + step * it;
-    if (c < L) store_norm2(out, out_bf16, (size_t)t * L + c, keep[it], r, gamma, gamma_bf16, c);
+    const int c = VW * threadIdx.x + step * it;
+    if (c < L) store_norm<VW>(out, out_bf16, (size_t)t * L + c, keep[it], r, gamma, gamma_bf16, c);
   }
-  for (int c = 2 * threadIdx.x + step * kNormKeep; c < L; c += step)
-    store_norm2(out, out_bf16, (size_t)t * L + c, *reinterpret_cast<const float2*>(zrow + c), r, gamma, gamma_bf16,
-                c);
+  for (int c = VW * threadIdx.x + step * kNormKeep; c < L; c += step)
+    store_norm<VW>(out, out_bf16, (size_t)t * L + c, *reinterpret_cast<const V*>(zrow + c), r, gamma, gamma_bf16, c);
 }
 
 hipError_t launch_combine_norm(int T, int K, int L, const float* ws, float* z, const void* gamma, float eps, Elt elt,
                                void* out, hipStream_t stream) {
-  if (L % 2 != 0) return hipErrorInvalidValue;
+  const int vw = norm_vw(T);
+  if (L % vw != 0) return hipErrorInvalidValue;
   const int bf = elt == Elt::BF16 ? 1 : 0;
-  hipLaunchKernelGGL(combine_norm_kernel, dim3(T), dim3(norm_threads(L)), 0, stream, K, L, ws, z, gamma, bf, eps, bf,
-                     out);
+  const dim3 grid(T), block(norm_threads(T, L));
+  if (vw == 2)
+    hipLaunchKernelGGL(combine_norm_kernel<2>, grid, block, 0, stream, K, L, ws, z, gamma, bf, eps, bf, out);
+  else
+    hipLaunchKernelGGL(combine_norm_kernel<4>, grid, block, 0, stream, K, L, ws, z, gamma, bf, eps, bf, out);
   return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm(int T, int L, const float* z, const void* gamma, float eps, Elt elt, void* out,
                           hipStream_t stream) {
-  if (L % 2 != 0) return hipErrorInvalidValue;
+  const int vw = norm_vw(T);
+  if (L % vw != 0) return hipErrorInvalidValue;
   const int bf = elt == Elt::BF16 ? 1 : 0;
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(norm_threads(L)), 0, stream, L, z, gamma, bf, eps, bf, out);
+  const dim3 grid(T), block(norm_threads(T, L));
+  if (vw == 2)
+    hipLaunchKernelGGL(rmsnorm_kernel<2>, grid, block, 0, stream, L, z, gamma, bf, eps, bf, out);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<4>, grid, block, 0, stream, L, z, gamma, bf, eps, bf, out);
   return hipGetLastError();
 }
 

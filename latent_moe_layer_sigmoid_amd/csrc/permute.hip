@@ -257,10 +257,17 @@ __global__ __launch_bounds__(PB) void permute_scan_kernel(int nblk, int E, int t
   int* s_scr = s_cnt + E;     // [2 * PW]
   for (int e = threadIdx.x; e < E; e += PB) {
     int run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      const int c = block_counts[(size_t)b * E + e];
-      block_counts[(size_t)b * E + e] = run;
-      run += c;
+    for (int b0 = 0; b0 < nblk; b0 += 16) {   // the counts of 16 blocks are requested together
+      int c[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (b0 + j < nblk) c[j] = block_counts[(size_t)(b0 + j) * E + e];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (b0 + j < nblk) {
+          block_counts[(size_t)(b0 + j) * E + e] = run;
+          run += c[j];
+        }
     }
     s_cnt[e] = run;
   }

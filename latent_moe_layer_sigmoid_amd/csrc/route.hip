@@ -52,8 +52,8 @@ __global__ __launch_bounds__(256) void route_renorm_kernel(int T, int E, int K, 
 }
 
 // Grouped top-k: one wavefront per token. The bias-corrected scores go to this wavefront's
-// LDS row; lane g < n_group takes the two largest of group g (its score is their fp32
-// sum), ranks it against the other groups (ties -> lower group) and a ballot gives the
+// LDS row; the lanes of group g find its two largest scores (the group score is their fp32
+// sum); lane g ranks group g against the other groups (ties -> lower group) and a ballot gives the
 // wave-uniform mask of the topk_group kept groups; then the single-group routine runs
 // with the other groups' experts left out.
 template <int KPL, int NP>
@@ -74,10 +74,16 @@ __global__ __launch_bounds__(256) void route_grouped_kernel(int T, int E, int K,
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const int gs = E / n_group;
-  if (lane < n_group) {
-    float t1 = -INFINITY, t2 = -INFINITY;
-    for (int i = 0; i < gs; ++i) {
-      const float v = kap[lane * gs + i];
+  // lpg lanes per group (a power of two): each takes every lpg-th score of its group, then
+  // the partial (largest, second largest) pairs merge by butterfly inside the group. The
+  // two largest values of a group do not depend on the order they are met in.
+  int lpg = 1;
+  while (lpg * 2 * n_group <= 64) lpg *= 2;
+  const int g = lane / lpg, sub = lane % lpg;
+  float t1 = -INFINITY, t2 = -INFINITY;
+  if (g < n_group) {
+    for (int i = sub; i < gs; i += lpg) {
+      const float v = kap[g * gs + i];
       if (v > t1) {
         t2 = t1;
         t1 = v;
@@ -85,8 +91,14 @@ __global__ __launch_bounds__(256) void route_grouped_kernel(int T, int E, int K,
         t2 = v;
       }
     }
-    gsc[lane] = gs > 1 ? t1 + t2 : t1;
   }
+  for (int off = 1; off < lpg; off <<= 1) {
+    const float u1 = __shfl_xor(t1, off, WAVE), u2 = __shfl_xor(t2, off, WAVE);
+    const float n2 = fmaxf(fminf(t1, u1), fmaxf(t2, u2));
+    t1 = fmaxf(t1, u1);
+    t2 = n2;
+  }
+  if (g < n_group && sub == 0) gsc[g] = gs > 1 ? t1 + t2 : t1;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
