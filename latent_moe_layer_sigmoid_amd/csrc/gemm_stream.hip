@@ -45,15 +45,21 @@ LMOE_DEV Chunk load_chunk_a(rsrc_t r, uint32_t voff, uint32_t soff) {
 
 // Weights are in the packed layout (see lmoe_pack_weights): the 16 rows x 256 bytes of
 // one (row group, chunk) form a 4 KB block whose piece q is the 1 KB at q * 1024 + 16 * l
-// for lane l. Every load instruction reads 1 KB contiguous.
+// for lane l. Every load instruction reads 1 KB contiguous. POL is the cache policy: when
+// each weight byte is read once in the launch the loads carry the non-temporal hint (the
+// decode layer step measured about 5% faster with it); when several row tiles re-read the
+// same weights they keep the default, so that the re-reads can hit the caches.
+template <int POL>
 LMOE_DEV Chunk load_chunk_w(rsrc_t r, uint32_t voff, uint32_t soff) {
   Chunk c;
-  c.v[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-  c.v[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 1024, soff, 0));
-  c.v[2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 2048, soff, 0));
-  c.v[3] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 3072, soff, 0));
+  c.v[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POL));
+  c.v[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 1024, soff, POL));
+  c.v[2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 2048, soff, POL));
+  c.v[3] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 3072, soff, POL));
   return c;
 }
+constexpr int kPolDefault = 0;
+constexpr int kPolStream = 2;   // nt
 
 template <Elt ELT>
 struct EltTraits;
@@ -109,7 +115,7 @@ LMOE_DEV float load_elt(Elt elt, const void* base, size_t idx) {
 // nbw consecutive column blocks of its row tile; its ring runs on across block boundaries
 // (the next block's first chunks are requested while the current block finishes), and
 // each block's epilogue runs as soon as its last chunk has been consumed.
-template <Elt ELT, int NT, bool DUAL, int D, bool MB>
+template <Elt ELT, int NT, bool DUAL, int D, bool MB, int POL>
 __global__ __launch_bounds__(512) void stream_gemm_kernel(const StreamGemm g, int groups_total, int nbw, int nch0,
                                                           int nch1) {
   static_assert(!(MB && DUAL), "several blocks per wave: single phase only");
@@ -187,10 +193,10 @@ __global__ __launch_bounds__(512) void stream_gemm_kernel(const StreamGemm g, in
   if (v0 < v1) {   // first weight chunk (phase 0 unless the range starts in phase 1)
     if (!DUAL || v0 < nch0) {
 #pragma unroll
-      for (int j = 0; j < NT; ++j) b[0][j] = load_chunk_w(w_rs, b_off[j], (uint32_t)v0 * 4096u);
+      for (int j = 0; j < NT; ++j) b[0][j] = load_chunk_w<POL>(w_rs, b_off[j], (uint32_t)v0 * 4096u);
     } else {
 #pragma unroll
-      for (int j = 0; j < NT; ++j) b[0][j] = load_chunk_w(w1_rs, b1_off[j], (uint32_t)(v0 - nch0) * 4096u);
+      for (int j = 0; j < NT; ++j) b[0][j] = load_chunk_w<POL>(w1_rs, b1_off[j], (uint32_t)(v0 - nch0) * 4096u);
     }
   }
 
@@ -276,7 +282,7 @@ __global__ __launch_bounds__(512) void stream_gemm_kernel(const StreamGemm g, in
     ca = load_chunk_a(p1 ? a1_rs : a_rs, p1 ? a1_off : a_off, c * CB);
 #pragma unroll
     for (int j = 0; j < NT; ++j)
-      cb[j] = load_chunk_w(p1 ? w1_rs : w_rs, p1 ? b1_off[j] : b_off[j], c * 4096u + ib * bstride);
+      cb[j] = load_chunk_w<POL>(p1 ? w1_rs : w_rs, p1 ? b1_off[j] : b_off[j], c * 4096u + ib * bstride);
   };
   auto issue = [&](int v, Chunk& ca, Chunk (&cb)[NT]) __attribute__((always_inline)) {
     const bool p1 = DUAL && v >= nch0;
@@ -390,19 +396,28 @@ constexpr int depth_of() {
   return 2;
 }
 
+template <Elt ELT, int NT, int POL>
+static void launch_pol(bool dual, int nbw, dim3 grid, dim3 block, size_t lds, hipStream_t stream, const StreamGemm& g,
+                       int groups_total, int nch0, int nch1) {
+  constexpr int D = depth_of<NT>();
+  if (dual)
+    hipLaunchKernelGGL((stream_gemm_kernel<ELT, NT, true, D, false, POL>), grid, block, lds, stream, g, groups_total,
+                       1, nch0, nch1);
+  else if (nbw > 1)
+    hipLaunchKernelGGL((stream_gemm_kernel<ELT, NT, false, D, true, POL>), grid, block, lds, stream, g, groups_total,
+                       nbw, nch0, nch1);
+  else
+    hipLaunchKernelGGL((stream_gemm_kernel<ELT, NT, false, D, false, POL>), grid, block, lds, stream, g, groups_total,
+                       1, nch0, nch1);
+}
+
 template <Elt ELT, int NT>
 static void launch_nt(bool dual, int nbw, dim3 grid, dim3 block, size_t lds, hipStream_t stream, const StreamGemm& g,
                       int groups_total, int nch0, int nch1) {
-  constexpr int D = depth_of<NT>();
-  if (dual)
-    hipLaunchKernelGGL((stream_gemm_kernel<ELT, NT, true, D, false>), grid, block, lds, stream, g, groups_total, 1,
-                       nch0, nch1);
-  else if (nbw > 1)
-    hipLaunchKernelGGL((stream_gemm_kernel<ELT, NT, false, D, true>), grid, block, lds, stream, g, groups_total, nbw,
-                       nch0, nch1);
+  if (g.weights_once)
+    launch_pol<ELT, NT, kPolStream>(dual, nbw, grid, block, lds, stream, g, groups_total, nch0, nch1);
   else
-    hipLaunchKernelGGL((stream_gemm_kernel<ELT, NT, false, D, false>), grid, block, lds, stream, g, groups_total, 1,
-                       nch0, nch1);
+    launch_pol<ELT, NT, kPolDefault>(dual, nbw, grid, block, lds, stream, g, groups_total, nch0, nch1);
 }
 
 // Waves a launch aims for (8 per CU). More, thinner waves measured slower: each wave
@@ -412,6 +427,7 @@ constexpr long kTargetWaves = 2048;
 template <Elt ELT>
 static hipError_t launch_elt(StreamGemm g, int live, hipStream_t stream) {
   using TR = EltTraits<ELT>;
+  if (!g.row_to_pair) g.weights_once = g.M <= 16;   // dense: one row tile reads every weight
   const bool dual = g.nseg == 1 && g.seg[0].epi == Epi::ADD2;
   const int nch0 = g.Kd / TR::KCH;
   const int nch1 = dual ? g.Kd1 / TR::KCH : 0;

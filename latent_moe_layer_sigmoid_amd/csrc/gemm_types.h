@@ -68,6 +68,9 @@ struct StreamGemm {
   // the slices in order and applies the epilogues. ksplit <= 1: no split.
   float* part;
   int ksplit;
+  // every weight row is read by a single 16-row tile of this launch (dense M <= 16, or
+  // grouped with at most 16 tokens): the stream kernel then loads weights non-temporally
+  int weights_once;
 };
 
 }  // namespace lmoe

@@ -328,6 +328,7 @@ lmoe_status lmoe_fc1_situ(int T, int E, int K, int in_dim, int d, int tile_m, lm
   if (!a || !w1 || !act) return LMOE_ERR_INVALID_ARG;
   if (!fits32(T, in_dim, a_dtype) || !fits32(2L * d, in_dim, w_dtype)) return LMOE_ERR_UNSUPPORTED;
   StreamGemm g{};
+  g.weights_once = T <= 16;   // an expert then holds at most 16 rows: one row tile
   g.a = a;
   g.a_bytes = (uint32_t)((long)T * in_dim * esize_of(a_dtype));
   g.lda = in_dim;
@@ -416,6 +417,7 @@ static lmoe_status fc2_combine_impl(int T, int E, int K, int d, int out_dim, int
   const long act_rows = dense ? T : rows_cap;
   if (!fits32(act_rows, d, act_dtype) || !fits32(out_dim, d, w_dtype)) return LMOE_ERR_UNSUPPORTED;
   StreamGemm g{};
+  g.weights_once = T <= 16;   // an expert then holds at most 16 rows: one row tile
   g.a = act;
   g.a_bytes = (uint32_t)(act_rows * d * esize_of(act_dtype));
   g.lda = d;
