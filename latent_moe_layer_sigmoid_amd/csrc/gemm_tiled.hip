@@ -3,8 +3,10 @@
 // FC1 / FC2 over tiles of 128 expert rows.
 //
 // Workgroup tile: 128 rows x 512 weight rows, 256 threads = 4 wavefronts side by side,
-// each owning all 128 rows x its own 128 weight rows as 8 x 8 v_mfma_f32_16x16x32_bf16
-// tiles (256 fp32 accumulators per lane; one wavefront per SIMD). A SituGLU wavefront
+// each owning all 128 rows x its own 128 weight rows as 4 x 4 v_mfma_f32_32x32x16_bf16
+// tiles (256 fp32 accumulators per lane; one wavefront per SIMD). The 32 x 32 form issues
+// half as many MFMAs per K step as 16 x 16 tiles for the same work (measured: 2170 instead
+// of 2280 cycles per K step on the 8192-row dense shapes). A SituGLU wavefront
 // takes 64 gate rows and the matching 64 up rows. Per 32-wide K step the workgroup needs
 // 8 KB of activations and 32 KB of weights for 1024 MFMA cycles per SIMD (about 40 bytes
 // per clock per CU), and each wavefront reads 16 KB of operands from LDS.
@@ -12,11 +14,16 @@
 // Operands reach LDS by direct buffer-to-LDS loads (buffer_load_dwordx4 ... lds) in the
 // packed MFMA order the weights already have in HBM: for each 16-row group and 32-wide K
 // step, a 1 KB block holding lane l = 16g + r's 16 bytes (row r, K 8g .. 8g + 7) at 16 l.
-// Every MFMA operand is then one conflict-free ds_read_b128, and the weights are copied
+// A 32 x 32 x 16 operand (row l % 32, K 8 (l / 32) .. + 7 of one half step) is then one
+// conflict-free ds_read_b128 from two neighbouring blocks, and the weights are copied
 // block for block. LDS is a ring of NSLOT 40 KB K steps, NSLOT - 1 of them in flight
 // while one is computed; the operands of step c + 1 are read from LDS into registers
 // while the MFMAs of step c run. Workgroups are ordered so that the 32 running on one XCD
 // cover 8 row tiles x 4 weight blocks, which share operands in that XCD's L2.
+//
+// The epilogue goes through LDS 64 rows at a time; the pair ids of the tile's rows are
+// requested before the K loop and the combine weights and in-place addends in batches, so
+// that no output row waits on a dependent global load of its own.
 //
 // Epilogues: plain store, SituGLU (vLLM PR 50088, commit 2), weighted per-pair store for
 // the combine (TensorRT-LLM PR 20541, "Commit 1": finalize), and the in-place add of the
@@ -144,6 +151,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     a_off[h] = (uint32_t)arow * (uint32_t)(g.lda * 2) + g4 * 16;
   }
+  // pair of the output rows row0 + lane and row0 + 64 + lane (-1: padding or past M), read
+  // by the epilogue; requested here so that its latency hides behind the K loop
+  int rp[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = row0 + 64 * h + lane;
+    rp[h] = grouped ? g.row_to_pair[row] : (row < g.M ? row : -1);
+  }
 
   // ---- weight row groups of this wavefront (its own 8 groups; SituGLU: 4 gate + 4 up)
   const uint32_t w_bytes = __builtin_amdgcn_readfirstlane((uint32_t)sg.n_total * (uint32_t)(g.Kd * 2));
@@ -164,25 +179,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int j = 0; j < 8; ++j)
       to_lds(w_rs, base + B_OFF + (8 * wave + j) * 1024, b_off[j], (uint32_t)(c + k0) * 1024u);
   };
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)smem + lane * 16;
+  // 32 x 32 x 16 operand of lane l: row l % 32 of a 32-row tile (16-row block (l / 16) & 1),
+  // K 8 (l / 32) .. + 7 of the half step h: K group 2 h + l / 32 of that block
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)smem + ((lane >> 4) & 1) * 1024 + (lane >> 5) * 256 + (lane & 15) * 16;
   auto read = [&](int c, Frag& f) {
     const uint32_t base = lds0 + (uint32_t)(c % NSLOT) * SLOT;
     const uint32_t bbase = base + B_OFF + wave * 8192;
-    static_for<8>([&](auto i) { f.a[i] = lds_read16<int(i) * 1024>(base); });
-    static_for<8>([&](auto j) { f.b[j] = lds_read16<int(j) * 1024>(bbase); });
+    static_for<8>([&](auto i) { f.a[i] = lds_read16<(int(i) >> 1) * 2048 + (int(i) & 1) * 512>(base); });
+    static_for<8>([&](auto j) { f.b[j] = lds_read16<(int(j) >> 1) * 2048 + (int(j) & 1) * 512>(bbase); });
   };
 
-  floatx4 acc[8][8];
+  floatx16 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
 
   auto mma = [&](const Frag& f) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[2 * i + h], f.b[2 * j + h], acc[i][j], 0, 0, 0);
   };
 
   // ---- prologue: steps 0 .. NSLOT-1 in flight; step 0 in registers
@@ -238,12 +258,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   float* red = reinterpret_cast<float*>(smem) + wave * (64 * RS);
   const float inv_b = 1.0f / g.beta;
   const float inv_lb = g.lbeta > 0.0f ? 1.0f / g.lbeta : 0.0f;
+  // combine weights of this lane's two rows, requested once for the whole epilogue
+  float rw[2] = {1.0f, 1.0f};
+  if ((sg.epi == Epi::PAIR || sg.epi == Epi::TOKEN) && g.pair_w) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) rw[h] = rp[h] >= 0 ? g.pair_w[rp[h]] : 0.0f;
+  }
   static_for<2>([&](auto h) {
     __builtin_amdgcn_sched_barrier(0);
-    static_for<4>([&](auto ii) {
-      static_for<8>([&](auto j) {
-        static_for<4>([&](auto rr) {
-          red[(16 * ii + 4 * g4 + rr) * RS + 16 * j + m] = acc[4 * int(h) + int(ii)][int(j)][int(rr)];
+    // accumulator tile (i, j) register rr: row 32 i + 8 (rr / 4) + 4 (lane / 32) + rr % 4,
+    // column 32 j + lane % 32 of the wavefront's 128 x 128 block
+    static_for<2>([&](auto ii) {
+      static_for<4>([&](auto j) {
+        static_for<16>([&](auto rr) {
+          red[(32 * ii + 8 * (int(rr) >> 2) + 4 * (lane >> 5) + (int(rr) & 3)) * RS + 32 * j + (lane & 31)] =
+              acc[2 * int(h) + int(ii)][int(j)][int(rr)];
         });
       });
     });
@@ -280,9 +309,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       // 16 lanes per row (4 outputs each): gate columns c .. c + 3, up columns 64 + c ..
       const int q = lane & 15;
       const int col = 256 * nb + 64 * wave + 4 * q;
-      for (int r = lane >> 4; r < 64; r += 4) {
+#pragma unroll 4
+      for (int it = 0; it < 16; ++it) {
+        const int r = 4 * it + (lane >> 4);
         const int row = rbase + r;
-        const int pair = grouped ? g.row_to_pair[row] : (row < g.M ? row : -1);
+        const int pair = __shfl(rp[h], r, WAVE);
         const floatx4 gv = *reinterpret_cast<const floatx4*>(red + r * RS + 4 * q);
         const floatx4 uv = *reinterpret_cast<const floatx4*>(red + r * RS + 64 + 4 * q);
         if (pair < 0 || col >= sg.n_out) continue;
@@ -299,38 +330,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
       }
     } else {
-      // 32 lanes per row (4 columns each)
+      // 32 lanes per row (4 columns each), 32 rows per batch; an in-place addend is
+      // requested for the whole batch before the batch's stores (each element is read and
+      // written by the same lane, so this is safe when `add` is the output)
       const int q = lane & 31;
       const int col = TILE_N * nb + 128 * wave + 4 * q;
-      for (int r = lane >> 5; r < 64; r += 2) {
-        const int row = rbase + r;
-        const int pair = grouped ? g.row_to_pair[row] : (row < g.M ? row : -1);
-        floatx4 v = *reinterpret_cast<const floatx4*>(red + r * RS + 4 * q);
-        if (pair < 0 || col >= sg.n_out) continue;
-        size_t idx = (size_t)row * sg.ldo + col;
-        if (sg.epi == Epi::PAIR || sg.epi == Epi::TOKEN) {
-          const float wgt = g.pair_w ? g.pair_w[pair] : 1.0f;
-          v *= wgt;
-          if (sg.epi == Epi::PAIR) {
-            *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(sg.out) + (size_t)pair * sg.ldo + col) = v;
-            continue;
-          }
-          idx = (size_t)(pair / g.topk) * sg.ldo + col;
-        } else if (sg.epi == Epi::ADD && g.add != nullptr) {
-          if (sg.out_elt == Elt::F32) {
-            v += *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(g.add) + idx);
-          } else {
-            const uint2 a = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(g.add) + idx);
-            v += floatx4{bf16_to_f32((uint16_t)a.x), bf16_to_f32((uint16_t)(a.x >> 16)), bf16_to_f32((uint16_t)a.y),
-                         bf16_to_f32((uint16_t)(a.y >> 16))};
+      const bool add = sg.epi == Epi::ADD && g.add != nullptr;
+      for (int b = 0; b < 2; ++b) {
+        floatx4 av[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int row = rbase + 32 * b + 2 * u + (lane >> 5);
+          av[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+          if (add && row < g.M && col < sg.n_out) {
+            const size_t idx = (size_t)row * sg.ldo + col;
+            if (sg.out_elt == Elt::F32) {
+              av[u] = *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(g.add) + idx);
+            } else {
+              const uint2 a = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(g.add) + idx);
+              av[u] = floatx4{__uint_as_float(a.x << 16), __uint_as_float(a.x & 0xFFFF0000u),
+                              __uint_as_float(a.y << 16), __uint_as_float(a.y & 0xFFFF0000u)};
+            }
           }
         }
-        if (sg.out_elt == Elt::F32) {
-          *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(sg.out) + idx) = v;
-        } else {
-          const uint32_t lo = f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-          const uint32_t hi = f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(sg.out) + idx) = make_uint2(lo, hi);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int r = 32 * b + 2 * u + (lane >> 5);
+          const int row = rbase + r;
+          const int pair = grouped ? __shfl(rp[h], r, WAVE) : (row < g.M ? row : -1);
+          const float wgt = __shfl(rw[h], r, WAVE);   // cross-lane reads before any lane leaves
+          floatx4 v = *reinterpret_cast<const floatx4*>(red + r * RS + 4 * q);
+          if (pair < 0 || col >= sg.n_out) continue;
+          size_t idx = (size_t)row * sg.ldo + col;
+          if (sg.epi == Epi::PAIR || sg.epi == Epi::TOKEN) {
+            v *= wgt;
+            if (sg.epi == Epi::PAIR) {
+              *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(sg.out) + (size_t)pair * sg.ldo + col) = v;
+              continue;
+            }
+            idx = (size_t)(pair / g.topk) * sg.ldo + col;
+          } else if (add) {
+            v += av[u];
+          }
+          if (sg.out_elt == Elt::F32) {
+            *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(sg.out) + idx) = v;
+          } else {
+            const uint32_t lo = f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+            const uint32_t hi = f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(sg.out) + idx) = make_uint2(lo, hi);
+          }
         }
       }
     }

@@ -31,7 +31,10 @@ LMOE_DEV void cas_desc(uint64_t& a, uint64_t& b) {
 }
 
 // Batcher's odd-even merge sort of N (a power of two) keys, descending; fully unrolled.
-template <int N>
+// Keys from index LIVE on are padding holding 0, below every real key: a descending
+// compare-exchange leaves the smaller key at the higher index, so such a slot only ever
+// meets real keys as the higher index and keeps its 0; those comparators are left out.
+template <int N, int LIVE = N>
 LMOE_DEV void sort_desc(uint64_t* k) {
 #pragma unroll
   for (int p = 1; p < N; p <<= 1)
@@ -41,7 +44,7 @@ LMOE_DEV void sort_desc(uint64_t* k) {
       for (int j = q % p; j + q < N; j += 2 * q)
 #pragma unroll
         for (int i = 0; i < q; ++i)
-          if (i + j + q < N && (i + j) / (2 * p) == (i + j + q) / (2 * p)) cas_desc(k[i + j], k[i + j + q]);
+          if (i + j + q < LIVE && (i + j) / (2 * p) == (i + j + q) / (2 * p)) cas_desc(k[i + j], k[i + j + q]);
 }
 
 LMOE_DEV float score_of(float logit) { return __builtin_amdgcn_rcpf(1.0f + __expf(-logit)); }
@@ -83,12 +86,10 @@ LMOE_DEV void route_token(int t, int E, int K, const float* __restrict__ logits,
     lg[j] = row[e];
     bs[j] = (METHOD == 0 && bias) ? bias[e] : 0.0f;
   }
-  f32v vlg;
   uint64_t key[NP];
 #pragma unroll
   for (int j = 0; j < NP; ++j) {
     const int e = lane + 64 * j;
-    vlg[j] = j < KPL ? lg[j] : 0.0f;
     key[j] = 0;   // below every real key; never selected since K <= the competing experts
     const bool competes = e < E && (group_size <= 0 || ((keep_groups >> (e / max(group_size, 1))) & 1ull));
     if (j < KPL && competes) {
@@ -96,12 +97,14 @@ LMOE_DEV void route_token(int t, int E, int K, const float* __restrict__ logits,
       key[j] = ((uint64_t)orderable(kap) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
     }
   }
-  sort_desc<NP>(key);
+  sort_desc<NP, KPL>(key);
   u32v vh, vl;
+  f32v vlg;
 #pragma unroll
   for (int j = 0; j < NP; ++j) {
     vh[j] = (uint32_t)(key[j] >> 32);
     vl[j] = (uint32_t)key[j];
+    vlg[j] = j < KPL ? lg[j] : 0.0f;
   }
 
   uint32_t hh = vh[0], ll = vl[0];   // this lane's current head key
