@@ -171,23 +171,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     b_off[j] = (uint32_t)n16 * (uint32_t)(g.Kd * 32) + lane * 16;   // past the matrix: zeros
   }
 
-  auto issue = [&](int c) {
+  // copy k of step c: k = 0, 1 this wavefront's two activation row groups, 2 .. 9 its
+  // eight weight row groups
+  auto issue_one = [&](int c, int k) __attribute__((always_inline)) {
     char* base = smem + (c % NSLOT) * SLOT;
+    if (k < 2)
+      to_lds(a_rs, base + (2 * wave + k) * 1024, a_off[k], (uint32_t)(c + k0) * 64u);
+    else
+      to_lds(w_rs, base + B_OFF + (8 * wave + k - 2) * 1024, b_off[k - 2], (uint32_t)(c + k0) * 1024u);
+  };
+  auto issue = [&](int c) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) to_lds(a_rs, base + (2 * wave + h) * 1024, a_off[h], (uint32_t)(c + k0) * 64u);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      to_lds(w_rs, base + B_OFF + (8 * wave + j) * 1024, b_off[j], (uint32_t)(c + k0) * 1024u);
+    for (int k = 0; k < LOADS_PER_STEP; ++k) issue_one(c, k);
   };
   // 32 x 32 x 16 operand of lane l: row l % 32 of a 32-row tile (16-row block (l / 16) & 1),
   // K 8 (l / 32) .. + 7 of the half step h: K group 2 h + l / 32 of that block
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)smem + ((lane >> 4) & 1) * 1024 + (lane >> 5) * 256 + (lane & 15) * 16;
-  auto read = [&](int c, Frag& f) {
-    const uint32_t base = lds0 + (uint32_t)(c % NSLOT) * SLOT;
-    const uint32_t bbase = base + B_OFF + wave * 8192;
-    static_for<8>([&](auto i) { f.a[i] = lds_read16<(int(i) >> 1) * 2048 + (int(i) & 1) * 512>(base); });
-    static_for<8>([&](auto j) { f.b[j] = lds_read16<(int(j) >> 1) * 2048 + (int(j) & 1) * 512>(bbase); });
+  // fragment K (a compile-time 0 .. 15) of step c: 0 .. 7 activation tile K / 2, half step
+  // K % 2; 8 .. 15 the same for the weights
+  auto read_one = [&](int c, Frag& f, auto K) __attribute__((always_inline)) {
+    constexpr int k = decltype(K)::value, q = k & 7;
+    const uint32_t base = lds0 + (uint32_t)(c % NSLOT) * SLOT + (k < 8 ? 0 : B_OFF + wave * 8192);
+    const bf16x8_t v = lds_read16<(q >> 1) * 2048 + (q & 1) * 512>(base);
+    if constexpr (k < 8)
+      f.a[q] = v;
+    else
+      f.b[q] = v;
   };
+  auto read = [&](int c, Frag& f) { static_for<16>([&](auto k) { read_one(c, f, k); }); };
 
   floatx16 acc[4][4];
 #pragma unroll
@@ -242,7 +253,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     __builtin_amdgcn_sched_barrier(0);
     if (c + NSLOT < nch) issue(c + NSLOT);
   };
+  // Steps whose copy c + NSLOT exists: the fragment reads follow the first 16 MFMAs one by
+  // one and the 10 copies every third MFMA, each pinned in place. One wavefront per SIMD
+  // has nothing to issue while it waits for the address unit to take a copy; placed
+  // between MFMAs, the wait overlaps the MFMA already running (measured on the 8192-row
+  // dense shapes: 1140-1570 cycles per K step instead of 2180; reads and copies in a
+  // block each, or left to the scheduler, 1400-1800).
+  auto step_il = [&](int c, Frag& cur, Frag& nxt) __attribute__((always_inline)) {
+    wait_steps(NSLOT - 2);
+    lds_barrier();
+    static_for<32>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      constexpr int h = i >> 4, ti = (i >> 2) & 3, tj = i & 3;
+      acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[2 * ti + h], cur.b[2 * tj + h], acc[ti][tj], 0, 0, 0);
+      if constexpr (i < 16) read_one(c + 1, nxt, std::integral_constant<int, i>{});
+      if constexpr (i % 3 == 2 && i / 3 < LOADS_PER_STEP) issue_one(c + NSLOT, i / 3);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
   int c = 0;
+  for (; c + 1 + NSLOT < nch; c += 2) {
+    step_il(c, f0, f1);
+    step_il(c + 1, f1, f0);
+  }
   for (; c + 1 < nch; c += 2) {
     step(c, f0, f1);
     step(c + 1, f1, f0);
