@@ -51,11 +51,15 @@ LMOE_DEV void to_lds(rsrc_t r, char* lds, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
 }
 
-LMOE_DEV void store_out(Elt elt, void* base, size_t idx, float v) {
-  if (elt == Elt::F32)
-    reinterpret_cast<float*>(base)[idx] = v;
-  else
-    reinterpret_cast<uint16_t*>(base)[idx] = f32_to_bf16(v);
+// four consecutive outputs as fp32 (16 bytes) or bf16 (8 bytes)
+LMOE_DEV void store4(Elt elt, void* base, size_t idx, floatx4 v) {
+  if (elt == Elt::F32) {
+    *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(base) + idx) = v;
+  } else {
+    const uint32_t lo = f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    const uint32_t hi = f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + idx) = make_uint2(lo, hi);
+  }
 }
 
 // A wave-uniform copy of a pointer / value (kept in scalar registers, so that buffer
@@ -93,6 +97,7 @@ struct Frag {
   bf16x8_t a[8], b[8];
 };
 
+template <bool ADD_PRE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void tiled_gemm_kernel(
     const StreamGemm g, int blocks_total, int m_tiles, int nch_total) {
   __shared__ __attribute__((aligned(1024))) char smem[NSLOT * SLOT];
@@ -100,18 +105,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 15, g4 = lane >> 4;
 
-  // ---- tile of this workgroup: XCD-contiguous logical ids, then row-tile groups of 8;
-  // with split-K the K slice is the outermost index
+  // ---- tile of this workgroup. Logical ids come in groups of GROUP_M row tiles x all
+  // weight blocks (one group shares its operands in one L2); the groups are dealt to the
+  // 8 XCDs in turn (workgroup b runs on XCD b % 8), so that the tiles of a grouped launch
+  // that hold rows, which are the first ones, spread over all XCDs. With split-K the K
+  // slice is the outermost index.
   const int G = m_tiles * blocks_total;
   const int ksplit = g.ksplit > 1 ? g.ksplit : 1;
-  const int GK8 = (G * ksplit + 7) & ~7;
-  const int lid_k = (int)(blockIdx.x & 7) * (GK8 >> 3) + (int)(blockIdx.x >> 3);
+  const int per_group = GROUP_M * blocks_total;
+  const int j = (int)(blockIdx.x >> 3);
+  const int lid_k = ((j / per_group) * 8 + (int)(blockIdx.x & 7)) * per_group + j % per_group;
   if (lid_k >= G * ksplit) return;
   const int ks = lid_k / G;
   const int lid = lid_k - ks * G;
   const int k0 = (int)((long)nch_total * ks / ksplit);                 // this slice's K steps
   const int nch = (int)((long)nch_total * (ks + 1) / ksplit) - k0;
-  const int per_group = GROUP_M * blocks_total;
   const int grp = lid / per_group;
   const int first_m = grp * GROUP_M;
   const int gm = min(GROUP_M, m_tiles - first_m);
@@ -283,10 +291,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   if (c < nch) step(c, f0, f1);
 
   // ---- epilogue, 64 rows at a time through this wavefront's own LDS region (every
-  // wavefront is past its last LDS read and every buffer-to-LDS load has landed).
-  // Accumulator tile (i, j) element rr is row 16 i + 4 g4 + rr, column 16 j + m of the
-  // wavefront's 128 x 128 block; it is written to LDS as fp32 [64][RS], then read back as
-  // 4 consecutive columns per lane so that the outputs leave as contiguous row segments.
+  // wavefront is past its last LDS read and every buffer-to-LDS load has landed): the
+  // accumulators of 64 rows are written to LDS as fp32 [64][RS], then read back as 4
+  // consecutive columns per lane so that the outputs leave as contiguous row segments.
   constexpr int RS = 132;                          // row stride (floats), padded against bank conflicts
   float* red = reinterpret_cast<float*>(smem) + wave * (64 * RS);
   const float inv_b = 1.0f / g.beta;
@@ -297,10 +304,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int h = 0; h < 2; ++h) rw[h] = rp[h] >= 0 ? g.pair_w[rp[h]] : 0.0f;
   }
-  static_for<2>([&](auto h) {
+  // rows of the tile up to the last one holding a pair (dense: the last one below M);
+  // the loops below skip whole batches of rows past it
+  const uint64_t m0 = __ballot(rp[0] >= 0), m1 = __ballot(rp[1] >= 0);
+  const int nv = m1 ? 128 - __builtin_clzll(m1) : (m0 ? 64 - __builtin_clzll(m0) : 0);
+  const int nv_half[2] = {min(nv, 64), max(nv - 64, 0)};
+  // accumulator tile (i, j) register rr: row 32 i + 8 (rr / 4) + 4 (lane / 32) + rr % 4,
+  // column 32 j + lane % 32 of the wavefront's 128 x 128 block; half h = rows 64 h ..
+  auto acc_to_lds = [&](auto h) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
-    // accumulator tile (i, j) register rr: row 32 i + 8 (rr / 4) + 4 (lane / 32) + rr % 4,
-    // column 32 j + lane % 32 of the wavefront's 128 x 128 block
     static_for<2>([&](auto ii) {
       static_for<4>([&](auto j) {
         static_for<16>([&](auto rr) {
@@ -310,112 +322,183 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       });
     });
     __builtin_amdgcn_sched_barrier(0);
-    const int rbase = row0 + 64 * h;
-    if (ksplit > 1) {
-      // raw fp32 partial sums of this K slice: 32 lanes per row, 4 weight-row columns each
-      int pbase = 0, ptot = 0;
+  };
+
+  if (ksplit > 1) {
+    // raw fp32 partial sums of this K slice: 32 lanes per row, 4 weight-row columns each
+    int pbase = 0, ptot = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (i < g.nseg) {
-          if (i < s) pbase += g.seg[i].n_total;
-          ptot += g.seg[i].n_total;
-        }
+    for (int i = 0; i < 4; ++i) {
+      if (i < g.nseg) {
+        if (i < s) pbase += g.seg[i].n_total;
+        ptot += g.seg[i].n_total;
       }
-      const int q = lane & 31;
-      int pcol, valid;
-      if (situ) {
-        const int c = 4 * q;   // LDS columns 0..63: gate, 64..127: up
-        const int oc = 256 * nb + 64 * wave + (c & 63);
-        valid = oc < sg.n_out;
-        pcol = (c < 64 ? 0 : sg.n_out) + oc;
-      } else {
-        pcol = TILE_N * nb + 128 * wave + 4 * q;
-        valid = pcol < sg.n_out;
-      }
-      float* dst = g.part + (size_t)ks * g.M * ptot + pbase + pcol;
+    }
+    const int q = lane & 31;
+    int pcol, valid;
+    if (situ) {
+      const int c = 4 * q;   // LDS columns 0..63: gate, 64..127: up
+      const int oc = 256 * nb + 64 * wave + (c & 63);
+      valid = oc < sg.n_out;
+      pcol = (c < 64 ? 0 : sg.n_out) + oc;
+    } else {
+      pcol = TILE_N * nb + 128 * wave + 4 * q;
+      valid = pcol < sg.n_out;
+    }
+    float* dst = g.part + (size_t)ks * g.M * ptot + pbase + pcol;
+    static_for<2>([&](auto h) {
+      acc_to_lds(h);
+      const int rbase = row0 + 64 * h;
       for (int r = lane >> 5; r < 64; r += 2) {
         const int row = rbase + r;
         const floatx4 v = *reinterpret_cast<const floatx4*>(red + r * RS + 4 * q);
         if (row < g.M && valid) *reinterpret_cast<floatx4*>(dst + (size_t)row * ptot) = v;
       }
-    } else if (situ) {
-      // 16 lanes per row (4 outputs each): gate columns c .. c + 3, up columns 64 + c ..
-      const int q = lane & 15;
-      const int col = 256 * nb + 64 * wave + 4 * q;
-#pragma unroll 4
-      for (int it = 0; it < 16; ++it) {
-        const int r = 4 * it + (lane >> 4);
-        const int row = rbase + r;
-        const int pair = __shfl(rp[h], r, WAVE);
-        const floatx4 gv = *reinterpret_cast<const floatx4*>(red + r * RS + 4 * q);
-        const floatx4 uv = *reinterpret_cast<const floatx4*>(red + r * RS + 64 + 4 * q);
-        if (pair < 0 || col >= sg.n_out) continue;
-        float v[4];
+    });
+    return;
+  }
+
+  // The output loops, specialised on the epilogue and the output type (both uniform in a
+  // workgroup) so that they hold no per-row branches on them: in each batch of rows, the
+  // LDS reads, row ids and combine weights are all requested before the first store, so
+  // that no read waits behind a store or a branch; batches past the last row holding a
+  // pair are skipped. The batch loops are not unrolled: the epilogue runs once per
+  // workgroup, so its code is fetched cold, and a compact loop keeps that fetch short.
+  auto epilogue = [&](auto EP, auto F32OUT) __attribute__((always_inline)) {
+    constexpr Epi ep = decltype(EP)::value;
+    constexpr Elt oe = decltype(F32OUT)::value ? Elt::F32 : Elt::BF16;
+    constexpr bool add_pre = ep == Epi::ADD && oe == Elt::BF16;
+#pragma unroll 1
+    for (int h = 0; h < 2; ++h) {
+      const int nvh = h ? nv_half[1] : nv_half[0];
+      if (nvh == 0) break;
+      const int rbase = row0 + 64 * h;
+      const int rph = h ? rp[1] : rp[0];
+      [[maybe_unused]] const float rwh = h ? rw[1] : rw[0];
+      // in-place addends (bf16) of every row of this half that this lane stores, requested
+      // before its stores: vector-memory stores and loads share one in-order counter, so a
+      // load issued after a store would wait for it (each element is read and written by
+      // the same lane, so `add` may be the output)
+      [[maybe_unused]] uint2 addv[add_pre ? 4 : 1][8];
+      if constexpr (add_pre) {
+        const int col = TILE_N * nb + 128 * wave + 4 * (lane & 31);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = situ_f(gv[k], uv[k], g.beta, inv_b, g.lbeta, inv_lb);
-        const size_t idx = (size_t)row * sg.ldo + col;
-        if (sg.out_elt == Elt::F32) {
-          *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(sg.out) + idx) = floatx4{v[0], v[1], v[2], v[3]};
-        } else {
-          const uint32_t lo = f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-          const uint32_t hi = f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(sg.out) + idx) = make_uint2(lo, hi);
-        }
+        for (int bt = 0; bt < 4; ++bt)
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int r = 16 * bt + 2 * u + (lane >> 5);
+            addv[bt][u] = make_uint2(0u, 0u);
+            if (g.add != nullptr && r < nvh && rbase + r < g.M && col < sg.n_out)
+              addv[bt][u] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(g.add) +
+                                                            (size_t)(rbase + r) * sg.ldo + col);
+          }
       }
-    } else {
-      // 32 lanes per row (4 columns each), 32 rows per batch; an in-place addend is
-      // requested for the whole batch before the batch's stores (each element is read and
-      // written by the same lane, so this is safe when `add` is the output)
-      const int q = lane & 31;
-      const int col = TILE_N * nb + 128 * wave + 4 * q;
-      const bool add = sg.epi == Epi::ADD && g.add != nullptr;
-      for (int b = 0; b < 2; ++b) {
-        floatx4 av[16];
+      if (h == 0)
+        acc_to_lds(std::integral_constant<int, 0>{});
+      else
+        acc_to_lds(std::integral_constant<int, 1>{});
+      if constexpr (ep == Epi::SITU) {
+        // 16 lanes per row (4 outputs each): gate columns c .. c + 3, up columns 64 + c ..;
+        // batches of 32 rows, 8 per lane
+        const int q = lane & 15;
+        const int col = 256 * nb + 64 * wave + 4 * q;
+        const bool col_ok = col < sg.n_out;
+#pragma unroll 1
+        for (int r0 = 0; r0 < nvh; r0 += 32) {
+          floatx4 gv[8], uv[8];
+          int pr[8];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const int row = rbase + 32 * b + 2 * u + (lane >> 5);
-          av[u] = floatx4{0.f, 0.f, 0.f, 0.f};
-          if (add && row < g.M && col < sg.n_out) {
-            const size_t idx = (size_t)row * sg.ldo + col;
-            if (sg.out_elt == Elt::F32) {
-              av[u] = *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(g.add) + idx);
-            } else {
-              const uint2 a = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(g.add) + idx);
-              av[u] = floatx4{__uint_as_float(a.x << 16), __uint_as_float(a.x & 0xFFFF0000u),
-                              __uint_as_float(a.y << 16), __uint_as_float(a.y & 0xFFFF0000u)};
-            }
+          for (int u = 0; u < 8; ++u) {
+            const int r = r0 + 4 * u + (lane >> 4);
+            pr[u] = __shfl(rph, r, WAVE);
+            gv[u] = *reinterpret_cast<const floatx4*>(red + r * RS + 4 * q);
+            uv[u] = *reinterpret_cast<const floatx4*>(red + r * RS + 64 + 4 * q);
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            if (pr[u] < 0 || !col_ok) continue;
+            floatx4 v;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[k] = situ_f(gv[u][k], uv[u][k], g.beta, inv_b, g.lbeta, inv_lb);
+            store4(oe, sg.out, (size_t)(rbase + r0 + 4 * u + (lane >> 4)) * sg.ldo + col, v);
           }
         }
+      } else {
+        // 32 lanes per row (4 columns each), batches of 16 rows, 8 per lane
+        const int q = lane & 31;
+        const int col = TILE_N * nb + 128 * wave + 4 * q;
+        const bool col_ok = col < sg.n_out;
+        auto batch = [&](int r0, auto BT) __attribute__((always_inline)) {
+          floatx4 v[8];
+          int pr[8];
+          [[maybe_unused]] float wt[8];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const int r = 32 * b + 2 * u + (lane >> 5);
-          const int row = rbase + r;
-          const int pair = grouped ? __shfl(rp[h], r, WAVE) : (row < g.M ? row : -1);
-          const float wgt = __shfl(rw[h], r, WAVE);   // cross-lane reads before any lane leaves
-          floatx4 v = *reinterpret_cast<const floatx4*>(red + r * RS + 4 * q);
-          if (pair < 0 || col >= sg.n_out) continue;
-          size_t idx = (size_t)row * sg.ldo + col;
-          if (sg.epi == Epi::PAIR || sg.epi == Epi::TOKEN) {
-            v *= wgt;
-            if (sg.epi == Epi::PAIR) {
-              *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(sg.out) + (size_t)pair * sg.ldo + col) = v;
-              continue;
+          for (int u = 0; u < 8; ++u) {
+            const int r = r0 + 2 * u + (lane >> 5);
+            pr[u] = __shfl(rph, r, WAVE);
+            if constexpr (ep == Epi::PAIR || ep == Epi::TOKEN) wt[u] = __shfl(rwh, r, WAVE);
+            v[u] = *reinterpret_cast<const floatx4*>(red + r * RS + 4 * q);
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            if (pr[u] < 0 || !col_ok) continue;
+            const size_t idx = (size_t)(rbase + r0 + 2 * u + (lane >> 5)) * sg.ldo + col;
+            if constexpr (ep == Epi::PAIR) {
+              *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(sg.out) + (size_t)pr[u] * sg.ldo + col) =
+                  v[u] * wt[u];
+            } else if constexpr (ep == Epi::TOKEN) {
+              store4(oe, sg.out, (size_t)(pr[u] / g.topk) * sg.ldo + col, v[u] * wt[u]);
+            } else if constexpr (ep == Epi::ADD) {
+              if constexpr (add_pre) {
+                const uint2 a = addv[decltype(BT)::value][u];
+                v[u] += floatx4{__uint_as_float(a.x << 16), __uint_as_float(a.x & 0xFFFF0000u),
+                                __uint_as_float(a.y << 16), __uint_as_float(a.y & 0xFFFF0000u)};
+              } else if (g.add != nullptr) {
+                v[u] += *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(g.add) + idx);
+              }
+              store4(oe, sg.out, idx, v[u]);
+            } else {
+              store4(oe, sg.out, idx, v[u]);
             }
-            idx = (size_t)(pair / g.topk) * sg.ldo + col;
-          } else if (add) {
-            v += av[u];
           }
-          if (sg.out_elt == Elt::F32) {
-            *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(sg.out) + idx) = v;
-          } else {
-            const uint32_t lo = f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-            const uint32_t hi = f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(sg.out) + idx) = make_uint2(lo, hi);
-          }
+        };
+        if constexpr (add_pre) {
+          // the addends sit in registers per batch: batches unrolled
+          static_for<4>([&](auto bt) {
+            if (16 * int(bt) < nvh) batch(16 * int(bt), bt);
+          });
+        } else {
+#pragma unroll 1
+          for (int r0 = 0; r0 < nvh; r0 += 16) batch(r0, std::integral_constant<int, 0>{});
         }
       }
     }
-  });
+  };
+  using F32_ = std::true_type;
+  using BF16_ = std::false_type;
+  const bool f32out = sg.out_elt == Elt::F32;
+  if constexpr (ADD_PRE) {
+    epilogue(std::integral_constant<Epi, Epi::ADD>{}, BF16_{});
+  } else if (sg.epi == Epi::SITU) {
+    if (f32out)
+      epilogue(std::integral_constant<Epi, Epi::SITU>{}, F32_{});
+    else
+      epilogue(std::integral_constant<Epi, Epi::SITU>{}, BF16_{});
+  } else if (sg.epi == Epi::PAIR) {
+    epilogue(std::integral_constant<Epi, Epi::PAIR>{}, F32_{});
+  } else if (sg.epi == Epi::TOKEN) {
+    if (f32out)
+      epilogue(std::integral_constant<Epi, Epi::TOKEN>{}, F32_{});
+    else
+      epilogue(std::integral_constant<Epi, Epi::TOKEN>{}, BF16_{});
+  } else if (sg.epi == Epi::ADD) {
+    epilogue(std::integral_constant<Epi, Epi::ADD>{}, F32_{});   // bf16 outputs take the ADD_PRE instance
+  } else {
+    if (f32out)
+      epilogue(std::integral_constant<Epi, Epi::STORE>{}, F32_{});
+    else
+      epilogue(std::integral_constant<Epi, Epi::STORE>{}, BF16_{});
+  }
 }
 
 static int tiled_blocks(StreamGemm& g) {
@@ -493,9 +576,16 @@ hipError_t launch_tiled_gemm(StreamGemm g, hipStream_t stream) {
   const int b0 = tiled_blocks(g);
   if (g.ksplit < 2 || !g.part || g.row_to_pair) g.ksplit = 1;
   const int m_tiles = (g.M + TILE_M - 1) / TILE_M;
-  const int G = m_tiles * b0;
-  const unsigned GK8 = (unsigned)((G * g.ksplit + 7) & ~7);
-  hipLaunchKernelGGL(tiled_gemm_kernel, dim3(GK8), dim3(256), 0, stream, g, b0, m_tiles, nch);
+  // whole rounds of 8 groups (one per XCD); the ids past the tiles return at once
+  const long per_group = (long)GROUP_M * b0;
+  const long groups = ((long)m_tiles * b0 * g.ksplit + per_group - 1) / per_group;
+  const unsigned grid = (unsigned)(((groups + 7) / 8) * 8 * per_group);
+  const bool add_pre = g.nseg == 1 && g.seg[0].epi == Epi::ADD && g.add != nullptr && g.seg[0].out_elt == Elt::BF16 &&
+                       g.ksplit == 1;
+  if (add_pre)
+    hipLaunchKernelGGL(tiled_gemm_kernel<true>, dim3(grid), dim3(256), 0, stream, g, b0, m_tiles, nch);
+  else
+    hipLaunchKernelGGL(tiled_gemm_kernel<false>, dim3(grid), dim3(256), 0, stream, g, b0, m_tiles, nch);
   if (g.ksplit > 1) {
     int ptot = 0, wmax = 0;
     for (int i = 0; i < g.nseg; ++i) {
