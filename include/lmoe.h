@@ -290,14 +290,17 @@ lmoe_status lmoe_tail(int T, int L, int H, const float* latent, const void* gamm
                       const void* w_up, const void* shared, lmoe_dtype io_dtype, void* out,
                       void* norm_out, hipStream_t stream);
 
-/* The tail with the shared expert's FC2 folded into the up projection, in two launches
- * ([P3] _shard_up_proj_tail: hidden += latent @ up_proj^T
- * accumulated into the shared output; [P1] commit 6: the up projection folds in the
- * shared-expert add):
+/* The tail with the shared expert's FC2 folded into the up projection ([P3]
+ * _shard_up_proj_tail: hidden += latent @ up_proj^T accumulated into the shared output;
+ * [P1] commit 6: the up projection folds in the shared-expert add):
  *   norm_out = RMSNorm(latent; gamma, eps)                        (as lmoe_tail)
- *   out[t, :] = round(round(shared_act[t, :] @ w_s2^T) + norm_out[t, :] @ w_up^T)
- * where round() rounds to io_dtype: the shared-expert output is rounded exactly as if
- * it had been stored, then added in fp32. shared_act [T, I] is the shared expert's
+ *   T < 256 (or F32):  out[t, :] = round(round(shared_act[t, :] @ w_s2^T) + norm_out[t, :] @ w_up^T)
+ *   T >= 256, BF16:    out[t, :] = round(shared_act[t, :] @ w_s2^T + norm_out[t, :] @ w_up^T)
+ * where round() rounds to io_dtype. With few tokens the shared-expert output is rounded
+ * exactly as if it had been stored, then added in fp32; with many, both products are
+ * summed in one set of fp32 accumulators (one GEMM over both K ranges), which differs
+ * from the first form by at most half a unit in the last place of the shared output
+ * before the final rounding. shared_act [T, I] is the shared expert's
  * SituGLU activation, w_s2 [H, I] and w_up [H, L] packed weights. out must not alias
  * shared_act or norm_out. latent NULL: norm_out already holds the normalized latent.
  * L % 128 and I % 128 == 0 (BF16; 64 for F32), H % 16 == 0. */

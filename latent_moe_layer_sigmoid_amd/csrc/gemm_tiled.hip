@@ -97,7 +97,7 @@ struct Frag {
   bf16x8_t a[8], b[8];
 };
 
-template <bool ADD_PRE>
+template <bool ADD_PRE, bool DUAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void tiled_gemm_kernel(
     const StreamGemm g, int blocks_total, int m_tiles, int nch_total) {
   __shared__ __attribute__((aligned(1024))) char smem[NSLOT * SLOT];
@@ -106,15 +106,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int m = lane & 15, g4 = lane >> 4;
 
   // ---- tile of this workgroup. Logical ids come in groups of GROUP_M row tiles x all
-  // weight blocks (one group shares its operands in one L2); the groups are dealt to the
-  // 8 XCDs in turn (workgroup b runs on XCD b % 8), so that the tiles of a grouped launch
-  // that hold rows, which are the first ones, spread over all XCDs. With split-K the K
+  // weight blocks (one group shares its operands in one L2; workgroup b runs on XCD
+  // b % 8). Dense launches give each XCD an equal run of consecutive ids. Grouped launches
+  // deal whole groups to the XCDs in turn: their tiles that hold rows come first, and the
+  // rest return at once, so equal runs would leave the last XCDs idle. With split-K the K
   // slice is the outermost index.
   const int G = m_tiles * blocks_total;
   const int ksplit = g.ksplit > 1 ? g.ksplit : 1;
   const int per_group = GROUP_M * blocks_total;
   const int j = (int)(blockIdx.x >> 3);
-  const int lid_k = ((j / per_group) * 8 + (int)(blockIdx.x & 7)) * per_group + j % per_group;
+  const int lid_k = g.row_to_pair != nullptr
+                        ? ((j / per_group) * 8 + (int)(blockIdx.x & 7)) * per_group + j % per_group
+                        : (int)(blockIdx.x & 7) * (int)(gridDim.x >> 3) + j;
   if (lid_k >= G * ksplit) return;
   const int ks = lid_k / G;
   const int lid = lid_k - ks * G;
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 
   // ---- activation rows this wavefront copies (row groups 2*wave, 2*wave + 1)
-  const rsrc_t a_rs = make_rsrc(uniform_ptr(g.a), __builtin_amdgcn_readfirstlane(g.a_bytes));
+  rsrc_t a_rs = make_rsrc(uniform_ptr(g.a), __builtin_amdgcn_readfirstlane(g.a_bytes));
   uint32_t a_off[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -170,7 +173,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   // ---- weight row groups of this wavefront (its own 8 groups; SituGLU: 4 gate + 4 up)
   const uint32_t w_bytes = __builtin_amdgcn_readfirstlane((uint32_t)sg.n_total * (uint32_t)(g.Kd * 2));
-  const rsrc_t w_rs = make_rsrc(uniform_ptr(reinterpret_cast<const char*>(sg.w) + (size_t)e * w_bytes), w_bytes);
+  rsrc_t w_rs = make_rsrc(uniform_ptr(reinterpret_cast<const char*>(sg.w) + (size_t)e * w_bytes), w_bytes);
   uint32_t b_off[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -179,16 +182,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     b_off[j] = (uint32_t)n16 * (uint32_t)(g.Kd * 32) + lane * 16;   // past the matrix: zeros
   }
 
+  // Two K phases (DUAL, dense, one plain segment): steps 0 .. nch0 - 1 multiply `a` by the
+  // segment's weights, the rest `a1` by `w1`, accumulating into the same fp32 tiles, so
+  // that the result is round(a w^T + a1 w1^T). The copies run ahead of the MFMAs, so the
+  // operands switch when the first copy of step nch0 is issued.
+  const int nch0 = DUAL ? g.Kd / 32 : nch_total;
+  int kb = 0;                              // first step of the phase being copied
+  auto to_phase1 = [&]() __attribute__((always_inline)) {
+    a_rs = make_rsrc(uniform_ptr(g.a1), __builtin_amdgcn_readfirstlane(g.a1_bytes));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int arow = min(row0 + 16 * (2 * wave + h) + m, g.M - 1);
+      a_off[h] = (uint32_t)arow * (uint32_t)(g.lda1 * 2) + g4 * 16;
+    }
+    const uint32_t w1_bytes = __builtin_amdgcn_readfirstlane((uint32_t)sg.n_total * (uint32_t)(g.Kd1 * 2));
+    w_rs = make_rsrc(uniform_ptr(g.w1), w1_bytes);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      b_off[j] = (uint32_t)(nb * 32 + 8 * wave + j) * (uint32_t)(g.Kd1 * 32) + lane * 16;
+    kb = nch0;
+  };
   // copy k of step c: k = 0, 1 this wavefront's two activation row groups, 2 .. 9 its
   // eight weight row groups
   auto issue_one = [&](int c, int k) __attribute__((always_inline)) {
     char* base = smem + (c % NSLOT) * SLOT;
     if (k < 2)
-      to_lds(a_rs, base + (2 * wave + k) * 1024, a_off[k], (uint32_t)(c + k0) * 64u);
+      to_lds(a_rs, base + (2 * wave + k) * 1024, a_off[k], (uint32_t)(c + k0 - kb) * 64u);
     else
-      to_lds(w_rs, base + B_OFF + (8 * wave + k - 2) * 1024, b_off[k - 2], (uint32_t)(c + k0) * 1024u);
+      to_lds(w_rs, base + B_OFF + (8 * wave + k - 2) * 1024, b_off[k - 2], (uint32_t)(c + k0 - kb) * 1024u);
   };
   auto issue = [&](int c) {
+    if constexpr (DUAL)
+      if (c == nch0) to_phase1();
 #pragma unroll
     for (int k = 0; k < LOADS_PER_STEP; ++k) issue_one(c, k);
   };
@@ -270,6 +295,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   auto step_il = [&](int c, Frag& cur, Frag& nxt) __attribute__((always_inline)) {
     wait_steps(NSLOT - 2);
     lds_barrier();
+    if constexpr (DUAL)
+      if (c + NSLOT == nch0) to_phase1();
     static_for<32>([&](auto I) __attribute__((always_inline)) {
       constexpr int i = decltype(I)::value;
       constexpr int h = i >> 4, ti = (i >> 2) & 3, tj = i & 3;
@@ -479,6 +506,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const bool f32out = sg.out_elt == Elt::F32;
   if constexpr (ADD_PRE) {
     epilogue(std::integral_constant<Epi, Epi::ADD>{}, BF16_{});
+  } else if constexpr (DUAL) {
+    if (f32out)
+      epilogue(std::integral_constant<Epi, Epi::STORE>{}, F32_{});
+    else
+      epilogue(std::integral_constant<Epi, Epi::STORE>{}, BF16_{});
   } else if (sg.epi == Epi::SITU) {
     if (f32out)
       epilogue(std::integral_constant<Epi, Epi::SITU>{}, F32_{});
@@ -571,21 +603,35 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const StreamGemm g, 
   }
 }
 
+// Two K phases in one launch (sums of both products in one set of fp32 accumulators):
+// dense, one plain-store segment.
+bool tiled_dual_ok(const StreamGemm& g) {
+  return g.a1 != nullptr && g.w1 != nullptr && g.row_to_pair == nullptr && g.nseg == 1 && g.seg[0].epi == Epi::STORE &&
+         g.Kd % 32 == 0 && g.Kd1 % 32 == 0;
+}
+
 hipError_t launch_tiled_gemm(StreamGemm g, hipStream_t stream) {
-  const int nch = g.Kd / 32;
+  // two K phases: dense, one plain-store segment (see the kernel)
+  const bool dual = tiled_dual_ok(g);
+  if (dual) g.ksplit = 1;
+  const int nch = g.Kd / 32 + (dual ? g.Kd1 / 32 : 0);
   const int b0 = tiled_blocks(g);
   if (g.ksplit < 2 || !g.part || g.row_to_pair) g.ksplit = 1;
   const int m_tiles = (g.M + TILE_M - 1) / TILE_M;
-  // whole rounds of 8 groups (one per XCD); the ids past the tiles return at once
+  // a multiple of 8 workgroups (dense) or whole rounds of 8 groups (grouped); the ids past
+  // the tiles return at once
+  const long n = (long)m_tiles * b0 * g.ksplit;
   const long per_group = (long)GROUP_M * b0;
-  const long groups = ((long)m_tiles * b0 * g.ksplit + per_group - 1) / per_group;
-  const unsigned grid = (unsigned)(((groups + 7) / 8) * 8 * per_group);
+  const unsigned grid = g.row_to_pair ? (unsigned)(((n + per_group - 1) / per_group + 7) / 8 * 8 * per_group)
+                                      : (unsigned)((n + 7) & ~7L);
   const bool add_pre = g.nseg == 1 && g.seg[0].epi == Epi::ADD && g.add != nullptr && g.seg[0].out_elt == Elt::BF16 &&
                        g.ksplit == 1;
-  if (add_pre)
-    hipLaunchKernelGGL(tiled_gemm_kernel<true>, dim3(grid), dim3(256), 0, stream, g, b0, m_tiles, nch);
+  if (dual)
+    hipLaunchKernelGGL((tiled_gemm_kernel<false, true>), dim3(grid), dim3(256), 0, stream, g, b0, m_tiles, nch);
+  else if (add_pre)
+    hipLaunchKernelGGL((tiled_gemm_kernel<true, false>), dim3(grid), dim3(256), 0, stream, g, b0, m_tiles, nch);
   else
-    hipLaunchKernelGGL(tiled_gemm_kernel<false>, dim3(grid), dim3(256), 0, stream, g, b0, m_tiles, nch);
+    hipLaunchKernelGGL((tiled_gemm_kernel<false, false>), dim3(grid), dim3(256), 0, stream, g, b0, m_tiles, nch);
   if (g.ksplit > 1) {
     int ptot = 0, wmax = 0;
     for (int i = 0; i < g.nseg; ++i) {

@@ -12,6 +12,7 @@ namespace lmoe {
 hipError_t launch_stream_gemm(StreamGemm g, Elt elt, int live_tiles, hipStream_t stream);
 // LDS-tiled bf16 GEMM: 128-row tiles (dense rows, or grouped tiles with tile_m == 128); Kd % 128 == 0.
 hipError_t launch_tiled_gemm(StreamGemm g, hipStream_t stream);
+bool tiled_dual_ok(const StreamGemm& g);
 // Split-K factor the tiled kernel would use for dense g (1: none) and the fp32 workspace
 // bytes it then needs.
 int tiled_splitk(const StreamGemm& g);

@@ -508,25 +508,25 @@ lmoe_status lmoe_tail_shared(int T, int L, int H, int I, const float* latent, co
     if (err != hipSuccess) return LMOE_ERR_HIP;
   }
   if (use_tiled_dense(T, io_dtype)) {
-    // token-heavy: out = shared-expert FC2 (stored, rounded), then out += up projection in place
+    // token-heavy: one tiled GEMM with two K phases, out = round(shared_act w_s2^T +
+    // norm_out w_up^T): the shared-expert FC2 and the up projection accumulate into the
+    // same fp32 tiles (the shared output is not rounded on its own here)
     StreamGemm g{};
     g.a = shared_act;
     g.a_bytes = (uint32_t)((long)T * I * esize_of(io_dtype));
     g.lda = I;
     g.Kd = I;
+    g.a1 = norm_out;
+    g.a1_bytes = (uint32_t)((long)T * L * esize_of(io_dtype));
+    g.lda1 = L;
+    g.Kd1 = L;
+    g.w1 = w_up;
     g.M = T;
     g.topk = 1;
     g.beta = 1.0f;
     g.nseg = 1;
     g.seg[0] = Seg{w_s2, H, H, Epi::STORE, elt_of(io_dtype), out, H, 0, 0};
-    err = launch_tiled_gemm(g, stream);
-    if (err != hipSuccess) return LMOE_ERR_HIP;
-    g.a = norm_out;
-    g.a_bytes = (uint32_t)((long)T * L * esize_of(io_dtype));
-    g.lda = L;
-    g.Kd = L;
-    g.add = out;
-    g.seg[0] = Seg{w_up, H, H, Epi::ADD, elt_of(io_dtype), out, H, 0, 0};
+    if (!tiled_dual_ok(g)) return LMOE_ERR_UNSUPPORTED;
     return hip_status(launch_tiled_gemm(g, stream));
   }
   StreamGemm g{};

@@ -50,7 +50,7 @@ class LatentMoELayer:
     device (lmoe_pack_weights) when the layer is built."""
 
     def __init__(self, shape: LayerShape, weights: dict, device="cuda", fused=True, shared_stream=False,
-                 router_stream=False):
+                 router_stream=False, fold_shared_fc2=None):
         B.lib()   # fail loudly now if the library is missing
         self.s = shape
         # fused: the hidden-input projections share one launch (lmoe_linear_multi) and the
@@ -66,6 +66,10 @@ class LatentMoELayer:
         # router stream while the main stream computes the latent down projection
         # (TensorRT-LLM PR 20541, "Commit 2": router stream, shared stream, main stream).
         self.router_stream = router_stream
+        # fold_shared_fc2 (with a second stream): the side stream runs only the shared FC1
+        # and the tail computes the shared FC2 and the up projection in one call
+        # (lmoe_tail_shared); None: fold when the token count takes the tiled GEMMs
+        self.fold_shared_fc2 = fold_shared_fc2
         self.device = torch.device(device)
         # extra streams at the default priority
         self._side = torch.cuda.Stream(self.device) if self.shared_stream else None
@@ -255,7 +259,9 @@ class LatentMoELayer:
         """Main stream: router GEMM + down projection (one launch), routing, permutation,
         experts, then RMSNorm + up projection with the shared add. Side stream: the shared
         expert (FC1 + SituGLU, FC2), started once the main stream reaches this call and
-        joined by an event before the tail. With the router stream, the router GEMM,
+        joined by an event before the tail; when folded (fold_shared_fc2), the side stream
+        runs only the FC1 and the tail computes the shared FC2 and the up projection in one
+        call. With the router stream, the router GEMM,
         routing and permutation run there and the main stream computes the down projection
         meanwhile, then waits for the routing before the experts."""
         s, w = self.s, self.w
@@ -268,10 +274,12 @@ class LatentMoELayer:
         side.wait_event(start)            # X is ready and the previous call's tail has read sh
         if not torch.cuda.is_current_stream_capturing():
             X.record_stream(side)
+        fold = self.fold_shared_fc2 if self.fold_shared_fc2 is not None else (T >= 256 and s.dtype == "bf16")
         B.lmoe_fc1_situ(T, 1, 1, s.H, s.I, 16, dt, X, None, None, None, dt, w["W_s1"], None, s.beta,
                         s.linear_beta, dt, b["act_s"], None, T, side)
-        B.lmoe_fc2_combine(T, 1, 1, s.I, s.H, 16, dt, b["act_s"], None, None, None, dt, w["W_s2"], None, None,
-                           dt, b["sh"], T, None, 0, side)
+        if not fold:
+            B.lmoe_fc2_combine(T, 1, 1, s.I, s.H, 16, dt, b["act_s"], None, None, None, dt, w["W_s2"], None, None,
+                               dt, b["sh"], T, None, 0, side)
         shared_done = torch.cuda.Event()
         shared_done.record(side)
         if self.router_stream:
@@ -295,7 +303,11 @@ class LatentMoELayer:
             self._routed(X, b, main, mark, norm=True)
         main.wait_event(shared_done)
         mark("tail")
-        B.lmoe_tail(T, s.L, s.H, None, w["gamma"], s.eps, w["W_up"], b["sh"], dt, b["out"], b["n"], main)
+        if fold:
+            B.lmoe_tail_shared(T, s.L, s.H, s.I, None, w["gamma"], s.eps, w["W_up"], b["act_s"], w["W_s2"], dt,
+                               b["out"], b["n"], main)
+        else:
+            B.lmoe_tail(T, s.L, s.H, None, w["gamma"], s.eps, w["W_up"], b["sh"], dt, b["out"], b["n"], main)
         mark(None)
         return b["out"]
 
