@@ -5,9 +5,11 @@ grouped FC1 + SituGLU, grouped FC2 + combine, shared expert, RMSNorm + up projec
 with the shared add) over one batch of seeded synthetic tokens already resident in HBM.
 
 Prints one JSON line: layer tokens/s of the decode-shape layer (T=8, H=7168, L=2048,
-E=896, top-16, d=512, shared I=4096, bf16), routing us/call at T=1024, the HBM
-roofline fraction of the dominant kernel (grouped FC1 + SituGLU, timed with HIP events
-on its launch stream) and the CPU oracle timed on a bounded sample of the same work.
+E=896, top-16, d=512, shared I=4096, bf16), routing us/call at T=1024, the roofline
+fraction of the dominant kernel (grouped FC1 + SituGLU, timed with HIP events on its
+launch stream; HBM-bound for the weight-streaming kernels of decode and MX experts,
+MFMA-bound for the tiled kernel of prefill) and the CPU oracle timed on a bounded sample
+of the same work.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_bf16]
                        [--no-cpu-baseline]
@@ -50,6 +52,28 @@ def fc1_bytes(cfg, n_touched, rows):
         w = n_touched * 2 * cfg.d * cfg.L * (0.5 + 1 / 32)
         return int(w + cfg.T * cfg.L * (1 + 1 / 32) + rows * cfg.d * (1 + 1 / 32))
     return n_touched * 2 * cfg.d * cfg.L * 2 + cfg.T * cfg.L * 2 + rows * cfg.d * 2
+
+
+def fc1_roofline(cfg, n_touched, rows, pairs, fc1_ms):
+    """Roofline of the grouped FC1 + SituGLU launch for the workload's kernel: the
+    weight-streaming GEMM (decode, MX experts) is bound by HBM, its algorithmic bytes per
+    launch from fc1_bytes; the LDS-tiled MFMA GEMM (128-row expert tiles, prefill) is bound
+    by the bf16 matrix cores, its algorithmic work 2 * pairs * 2d * L flops (the token-expert
+    pairs, not the padded rows it also computes)."""
+    if cfg.experts != "mx" and cfg.tile_m == 128:
+        flops = 2 * pairs * 2 * cfg.d * cfg.L
+        achieved = flops / (fc1_ms * 1e-3) / 1e12
+        return {"kernel": "grouped FC1 + SituGLU (tiled_gemm_kernel, 128 x 512 tiles, SituGLU epilogue)",
+                "bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": flops,
+                "executed_rows": rows, "avg_ms": round(fc1_ms, 5), "n_touched_experts": n_touched}
+    fb = fc1_bytes(cfg, n_touched, rows)
+    achieved = fb / (fc1_ms * 1e-3) / 1e9
+    kern = ("stream_gemm_mx_kernel, MXFP8 x MXFP4 scaled MFMA" if cfg.experts == "mx"
+            else "stream_gemm_kernel, SituGLU epilogue")
+    return {"kernel": f"grouped FC1 + SituGLU ({kern})", "bound": "hbm", "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": fb, "avg_ms": round(fc1_ms, 5), "n_touched_experts": n_touched}
 
 
 def fc1_traffic(cfg, seed):
@@ -238,9 +262,9 @@ def main():
     counts = b["counts"].cpu()
     n_touched = int((counts > 0).sum())
     rows = int(b["tile_offsets"][-1].item())
-    fb = fc1_bytes(cfg, n_touched, rows)
     fc1_ms = dur["fc1"]
-    achieved = fb / (fc1_ms * 1e-3) / 1e9
+    roof = fc1_roofline(cfg, n_touched, rows, cfg.T * cfg.K, fc1_ms)
+    roof["traffic"] = fc1_traffic(cfg, args.seed)
     lb = layer_bytes(cfg, n_touched)
     log(f"n_touched={n_touched} rows={rows} fc1={fc1_ms * 1e3:.1f}us step={ms_per_step * 1e3:.1f}us "
         f"layer bytes={lb / 1e6:.1f}MB")
@@ -267,10 +291,7 @@ def main():
                                f"shared I={cfg.I} experts={cfg.experts} tile_m={cfg.tile_m}",
                    "tokens_per_step": cfg.T, "seed": args.seed, "schedule": args.schedule,
                    "launch": "hip_graph" if args.graph else "eager"},
-        "roofline": {"kernel": "grouped FC1 + SituGLU (stream_gemm_kernel, SituGLU epilogue)",
-                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": fc1_traffic(cfg, args.seed),
-                     "algorithmic_bytes": fb, "avg_ms": round(fc1_ms, 5), "n_touched_experts": n_touched},
+        "roofline": roof,
         "layer_hbm": {"algorithmic_bytes": lb, "achieved_GBs": round(lb / (ms_per_step * 1e-3) / 1e9, 1),
                       "frac": round(lb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "route_us_per_call": round(route_us, 3),
