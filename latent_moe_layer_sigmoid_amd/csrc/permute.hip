@@ -8,7 +8,9 @@
 // (one ballot per bit), the rank inside the wave is the popcount of matching lower
 // lanes, and the per-wave counts in LDS give the offset of each earlier wave.
 //   1 block  : one fused kernel (count, scan, rank, scatter).
-//   >1 blocks: count per block -> one-block scan over (expert, block) -> rank + scatter.
+//   >1 blocks: count per block (and -1 into every row of row_to_pair) -> one-block scan of
+//              the expert totals -> per block: its base in each expert (the counts of the
+//              blocks before it), rank + scatter.
 // Threads of a workgroup share data through LDS only, so its barriers order LDS alone (the
 // global outputs are read by later launches).
 // Decode-sized batches (T <= 16 tokens, T*K <= 1024 pairs) can also run routing and the
@@ -70,12 +72,12 @@ LMOE_DEV int block_exclusive_scan(int v, int* s_wave, int* total) {
 }
 
 // Scan of counts over experts (each thread owns a contiguous range of experts), writing
-// offsets, tile_offsets, pad rows and the tile -> expert map. s_cnt holds counts[E].
-// While every padded row index fits in 16 bits, the two sums (pairs and padded rows)
-// share one scan as the halves of a 32-bit value.
+// offsets, tile_offsets, the tile -> expert map and, with fill_pad, -1 into the pad rows.
+// s_cnt holds counts[E]. While every padded row index fits in 16 bits, the two sums
+// (pairs and padded rows) share one scan as the halves of a 32-bit value.
 LMOE_DEV void scan_experts(const int* s_cnt, int E, int tile_m, int max_tiles, int32_t* counts,
                            int32_t* offsets, int32_t* tile_offsets, int32_t* row_to_pair,
-                           int32_t* tile_expert, int* s_scratch, int* s_tile_off) {
+                           int32_t* tile_expert, int* s_scratch, int* s_tile_off, bool fill_pad = true) {
   const int per = (E + PB - 1) / PB;
   const int e0 = threadIdx.x * per, e1 = min(E, e0 + per);
   const int tsh = __builtin_ctz(tile_m);   // tile_m is a power of two
@@ -105,7 +107,8 @@ LMOE_DEV void scan_experts(const int* s_cnt, int E, int tile_m, int max_tiles, i
     offsets[e] = c_pre;
     tile_offsets[e] = p_pre;
     if (s_tile_off) s_tile_off[e] = p_pre;
-    for (int r = p_pre + c; r < p_pre + pc; ++r) row_to_pair[r] = -1;
+    if (fill_pad)
+      for (int r = p_pre + c; r < p_pre + pc; ++r) row_to_pair[r] = -1;
     for (int tt = p_pre >> tsh; tt < (p_pre + pc) >> tsh; ++tt) tile_expert[tt] = e;
     c_pre += c;
     p_pre += pc;
@@ -237,8 +240,11 @@ hipError_t launch_route_permute(int T, int E, int K, const float* logits, const 
 
 // ---- several blocks ------------------------------------------------------------------------
 __global__ __launch_bounds__(PB) void permute_count_kernel(int npairs, int E, const int32_t* __restrict__ ids,
-                                                           int32_t* __restrict__ block_counts) {
+                                                           int32_t* __restrict__ block_counts,
+                                                           int32_t* __restrict__ row_to_pair, int rows_cap) {
   extern __shared__ int s_cnt[];
+  // every row starts as padding; the scatter kernel (a later launch) writes the pairs
+  for (int r = blockIdx.x * PB + threadIdx.x; r < rows_cap; r += gridDim.x * PB) row_to_pair[r] = -1;
   for (int e = threadIdx.x; e < E; e += PB) s_cnt[e] = 0;
   lds_sync();
   const int p = blockIdx.x * PB + threadIdx.x;
@@ -247,43 +253,47 @@ __global__ __launch_bounds__(PB) void permute_count_kernel(int npairs, int E, co
   for (int e = threadIdx.x; e < E; e += PB) block_counts[(size_t)blockIdx.x * E + e] = s_cnt[e];
 }
 
-// One block: per expert, exclusive scan over blocks (in place), then the expert scan.
+// Sum over blocks [0, nb) of expert e's block counts; 32 counts requested together.
+LMOE_DEV int sum_block_counts(const int32_t* __restrict__ block_counts, int E, int e, int nb) {
+  int run = 0;
+  for (int b0 = 0; b0 < nb; b0 += 32) {
+    int c[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) c[j] = b0 + j < nb ? block_counts[(size_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) run += c[j];
+  }
+  return run;
+}
+
+// One block: the expert totals (sums over blocks), then the expert scan (the pad rows are
+// already -1).
 __global__ __launch_bounds__(PB) void permute_scan_kernel(int nblk, int E, int tile_m, int max_tiles,
-                                                          int32_t* __restrict__ block_counts, int32_t* counts,
+                                                          const int32_t* __restrict__ block_counts, int32_t* counts,
                                                           int32_t* offsets, int32_t* tile_offsets,
                                                           int32_t* row_to_pair, int32_t* tile_expert) {
   extern __shared__ int smem[];
   int* s_cnt = smem;          // [E]
   int* s_scr = s_cnt + E;     // [2 * PW]
-  for (int e = threadIdx.x; e < E; e += PB) {
-    int run = 0;
-    for (int b0 = 0; b0 < nblk; b0 += 16) {   // the counts of 16 blocks are requested together
-      int c[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (b0 + j < nblk) c[j] = block_counts[(size_t)(b0 + j) * E + e];
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (b0 + j < nblk) {
-          block_counts[(size_t)(b0 + j) * E + e] = run;
-          run += c[j];
-        }
-    }
-    s_cnt[e] = run;
-  }
+  for (int e = threadIdx.x; e < E; e += PB) s_cnt[e] = sum_block_counts(block_counts, E, e, nblk);
   lds_sync();
   scan_experts(s_cnt, E, tile_m, max_tiles, counts, offsets, tile_offsets, row_to_pair, tile_expert,
-               s_scr, nullptr);
+               s_scr, nullptr, false);
 }
 
 __global__ __launch_bounds__(PB) void permute_scatter_kernel(int npairs, int E, const int32_t* __restrict__ ids,
-                                                             const int32_t* __restrict__ block_base,
+                                                             const int32_t* __restrict__ block_counts,
                                                              const int32_t* __restrict__ tile_offsets,
                                                              int32_t* row_to_pair, int32_t* pair_to_row) {
-  extern __shared__ unsigned short s_wcnt[];   // [PW * E]
-  const int32_t* bb = block_base + (size_t)blockIdx.x * E;
-  rank_scatter(ids, npairs, E, id_bits(E), blockIdx.x * PB, s_wcnt,
-               [&](int e) { return tile_offsets[e] + bb[e]; }, row_to_pair, pair_to_row);
+  extern __shared__ int s_base[];                                           // [E]
+  unsigned short* s_wcnt = reinterpret_cast<unsigned short*>(s_base + E);   // [PW * E]
+  // first row of this block's pairs in each expert: the expert's first row plus the pairs
+  // of the blocks before this one
+  for (int e = threadIdx.x; e < E; e += PB)
+    s_base[e] = tile_offsets[e] + sum_block_counts(block_counts, E, e, blockIdx.x);
+  lds_sync();
+  rank_scatter(ids, npairs, E, id_bits(E), blockIdx.x * PB, s_wcnt, [&](int e) { return s_base[e]; },
+               row_to_pair, pair_to_row);
 }
 
 size_t permute_workspace_bytes(int npairs, int E) {
@@ -303,11 +313,12 @@ hipError_t launch_permute(int npairs, int E, int tile_m, int max_tiles, const in
   }
   int32_t* block_counts = (int32_t*)workspace;
   hipLaunchKernelGGL(permute_count_kernel, dim3(nblk), dim3(PB), (size_t)E * sizeof(int), stream, npairs, E,
-                     ids, block_counts);
+                     ids, block_counts, row_to_pair, max_tiles * tile_m);
   hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(PB), (size_t)(E + 2 * PW) * sizeof(int), stream, nblk, E,
                      tile_m, max_tiles, block_counts, counts, offsets, tile_offsets, row_to_pair, tile_expert);
-  hipLaunchKernelGGL(permute_scatter_kernel, dim3(nblk), dim3(PB), (size_t)PW * E * sizeof(unsigned short),
-                     stream, npairs, E, ids, block_counts, tile_offsets, row_to_pair, pair_to_row);
+  hipLaunchKernelGGL(permute_scatter_kernel, dim3(nblk), dim3(PB),
+                     (size_t)E * sizeof(int) + (size_t)PW * E * sizeof(unsigned short), stream, npairs, E, ids,
+                     block_counts, tile_offsets, row_to_pair, pair_to_row);
   return hipGetLastError();
 }
 

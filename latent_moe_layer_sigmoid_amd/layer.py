@@ -183,6 +183,15 @@ class LatentMoELayer:
         mark(None)
         return b["out"]
 
+    def folds_shared_fc2(self, T):
+        """True when a forward pass over T tokens with the shared-expert stream computes the
+        shared FC2 inside the tail (the shared output b["sh"] is then not written)."""
+        if not self.shared_stream:
+            return False
+        if self.fold_shared_fc2 is not None:
+            return self.fold_shared_fc2
+        return T >= 256 and self.s.dtype == "bf16"
+
     def capture(self, X):
         """A HIP graph of one forward pass on the static input X (same buffers as
         forward(X)); graph.replay() reruns the whole layer, reading X's current contents.
@@ -274,7 +283,7 @@ class LatentMoELayer:
         side.wait_event(start)            # X is ready and the previous call's tail has read sh
         if not torch.cuda.is_current_stream_capturing():
             X.record_stream(side)
-        fold = self.fold_shared_fc2 if self.fold_shared_fc2 is not None else (T >= 256 and s.dtype == "bf16")
+        fold = self.folds_shared_fc2(T)
         B.lmoe_fc1_situ(T, 1, 1, s.H, s.I, 16, dt, X, None, None, None, dt, w["W_s1"], None, s.beta,
                         s.linear_beta, dt, b["act_s"], None, T, side)
         if not fold:
