@@ -308,6 +308,20 @@ lmoe_status lmoe_tail_shared(int T, int L, int H, int I, const float* latent, co
                              const void* w_up, const void* shared_act, const void* w_s2, lmoe_dtype io_dtype,
                              void* out, void* norm_out, hipStream_t stream);
 
+/* lmoe_tail_shared with a caller-provided fp32 workspace for split-K: with T >= 256 (BF16)
+ * and too few 128 x 512 output tiles to fill the CUs (for example T = 1024, H = 7168), the
+ * K range of both phases together is cut into slices computed by separate workgroups into
+ * `workspace`, and a second kernel adds the slices in fixed order and rounds (results are
+ * reproducible; they may differ in the last bits from the unsplit call).
+ * lmoe_tail_shared_workspace_bytes returns the bytes needed for the same shapes (0: no
+ * split, workspace unused). workspace NULL: no split; non-NULL but smaller than needed:
+ * LMOE_ERR_WORKSPACE. Everything else as lmoe_tail_shared. */
+size_t lmoe_tail_shared_workspace_bytes(int T, int L, int H, int I, lmoe_dtype io_dtype);
+lmoe_status lmoe_tail_shared_ws(int T, int L, int H, int I, const float* latent, const void* gamma, float eps,
+                                const void* w_up, const void* shared_act, const void* w_s2, lmoe_dtype io_dtype,
+                                void* out, void* norm_out, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
 /* Masked SituGLU over the batched [E, T_max, 2d] expert layout ([P1] commit 2:
  * masked_situ_and_mul reads expert_num_tokens and leaves padded rows untouched).
  *   For e < E and r < clamp(expert_num_tokens[e], 0, T_max):

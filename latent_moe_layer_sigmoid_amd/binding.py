@@ -55,6 +55,8 @@ SIGNATURES = [
                                    _i, _p, _p]),
     ("lmoe_tail", _i, [_i, _i, _i, _p, _p, _f, _p, _p, _i, _p, _p, _p]),
     ("lmoe_tail_shared", _i, [_i, _i, _i, _i, _p, _p, _f, _p, _p, _p, _i, _p, _p, _p]),
+    ("lmoe_tail_shared_workspace_bytes", _z, [_i, _i, _i, _i, _i]),
+    ("lmoe_tail_shared_ws", _i, [_i, _i, _i, _i, _p, _p, _f, _p, _p, _p, _i, _p, _p, _p, _z, _p]),
     ("lmoe_situ_masked", _i, [_i, _i, _i, _i, _p, _p, _f, _f, _p, _p]),
 ]
 
@@ -263,6 +265,18 @@ def lmoe_tail_shared(T, L, H, I, latent, gamma, eps, w_up, shared_act, w_s2, io_
     _check("lmoe_tail_shared", lib().lmoe_tail_shared(T, L, H, I, _ptr(latent), _ptr(gamma), float(eps), _ptr(w_up),
                                                       _ptr(shared_act), _ptr(w_s2), io_dtype, _ptr(out),
                                                       _ptr(norm_out), _stream(stream)))
+
+
+def lmoe_tail_shared_workspace_bytes(T, L, H, I, io_dtype):
+    return int(lib().lmoe_tail_shared_workspace_bytes(T, L, H, I, io_dtype))
+
+
+def lmoe_tail_shared_ws(T, L, H, I, latent, gamma, eps, w_up, shared_act, w_s2, io_dtype, out, norm_out, workspace,
+                        workspace_bytes, stream=None):
+    _check("lmoe_tail_shared_ws", lib().lmoe_tail_shared_ws(T, L, H, I, _ptr(latent), _ptr(gamma), float(eps),
+                                                            _ptr(w_up), _ptr(shared_act), _ptr(w_s2), io_dtype,
+                                                            _ptr(out), _ptr(norm_out), _ptr(workspace),
+                                                            int(workspace_bytes), _stream(stream)))
 
 
 def lmoe_situ_masked(E, T_max, d, dtype, inp, expert_num_tokens, beta, linear_beta, out, stream=None):

@@ -202,6 +202,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       b_off[j] = (uint32_t)(nb * 32 + 8 * wave + j) * (uint32_t)(g.Kd1 * 32) + lane * 16;
     kb = nch0;
   };
+  // a split-K slice that starts in the second phase copies its operands from the start
+  if constexpr (DUAL)
+    if (k0 >= nch0) to_phase1();
   // copy k of step c: k = 0, 1 this wavefront's two activation row groups, 2 .. 9 its
   // eight weight row groups
   auto issue_one = [&](int c, int k) __attribute__((always_inline)) {
@@ -213,7 +216,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
   auto issue = [&](int c) {
     if constexpr (DUAL)
-      if (c == nch0) to_phase1();
+      if (c + k0 == nch0) to_phase1();
 #pragma unroll
     for (int k = 0; k < LOADS_PER_STEP; ++k) issue_one(c, k);
   };
@@ -296,7 +299,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     wait_steps(NSLOT - 2);
     lds_barrier();
     if constexpr (DUAL)
-      if (c + NSLOT == nch0) to_phase1();
+      if (c + NSLOT + k0 == nch0) to_phase1();
     static_for<32>([&](auto I) __attribute__((always_inline)) {
       constexpr int i = decltype(I)::value;
       constexpr int h = i >> 4, ti = (i >> 2) & 3, tj = i & 3;
@@ -551,7 +554,7 @@ int tiled_splitk(const StreamGemm& g0) {
   StreamGemm g = g0;
   const int G = ((g.M + TILE_M - 1) / TILE_M) * tiled_blocks(g);
   int k = 256 / (G > 0 ? G : 1);
-  k = min(k, (g.Kd / 32) / 16);
+  k = min(k, ((g.Kd + (tiled_dual_ok(g) ? g.Kd1 : 0)) / 32) / 16);
   k = min(k, 8);
   return k < 2 ? 1 : k;
 }
@@ -604,16 +607,16 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const StreamGemm g, 
 }
 
 // Two K phases in one launch (sums of both products in one set of fp32 accumulators):
-// dense, one plain-store segment.
+// dense, one plain-store segment, a second phase (Kd1 > 0: a1 and w1 are its operands).
 bool tiled_dual_ok(const StreamGemm& g) {
-  return g.a1 != nullptr && g.w1 != nullptr && g.row_to_pair == nullptr && g.nseg == 1 && g.seg[0].epi == Epi::STORE &&
-         g.Kd % 32 == 0 && g.Kd1 % 32 == 0;
+  return g.Kd1 > 0 && g.row_to_pair == nullptr && g.nseg == 1 && g.seg[0].epi == Epi::STORE && g.Kd % 32 == 0 &&
+         g.Kd1 % 32 == 0;
 }
 
 hipError_t launch_tiled_gemm(StreamGemm g, hipStream_t stream) {
-  // two K phases: dense, one plain-store segment (see the kernel)
+  // two K phases: dense, one plain-store segment (see the kernel); split-K slices cut the
+  // steps of both phases together
   const bool dual = tiled_dual_ok(g);
-  if (dual) g.ksplit = 1;
   const int nch = g.Kd / 32 + (dual ? g.Kd1 / 32 : 0);
   const int b0 = tiled_blocks(g);
   if (g.ksplit < 2 || !g.part || g.row_to_pair) g.ksplit = 1;

@@ -491,9 +491,32 @@ lmoe_status lmoe_tail(int T, int L, int H, const float* latent, const void* gamm
   return hip_status(run_gemm(g, io_dtype, use_tiled_dense(T, io_dtype), (T + 15) / 16, stream));
 }
 
-lmoe_status lmoe_tail_shared(int T, int L, int H, int I, const float* latent, const void* gamma, float eps,
-                             const void* w_up, const void* shared_act, const void* w_s2, lmoe_dtype io_dtype,
-                             void* out, void* norm_out, hipStream_t stream) {
+// The tiled two-phase GEMM of the token-heavy tail: out = shared_act @ w_s2^T +
+// norm_out @ w_up^T, one set of fp32 accumulators.
+static StreamGemm tail_shared_gemm(int T, int L, int H, int I, const void* w_up, const void* shared_act,
+                                   const void* w_s2, lmoe_dtype io_dtype, void* out, const void* norm_out) {
+  StreamGemm g{};
+  g.a = shared_act;
+  g.a_bytes = (uint32_t)((long)T * I * esize_of(io_dtype));
+  g.lda = I;
+  g.Kd = I;
+  g.a1 = norm_out;
+  g.a1_bytes = (uint32_t)((long)T * L * esize_of(io_dtype));
+  g.lda1 = L;
+  g.Kd1 = L;
+  g.w1 = w_up;
+  g.M = T;
+  g.topk = 1;
+  g.beta = 1.0f;
+  g.nseg = 1;
+  g.seg[0] = Seg{w_s2, H, H, Epi::STORE, elt_of(io_dtype), out, H, 0, 0};
+  return g;
+}
+
+static lmoe_status tail_shared_impl(int T, int L, int H, int I, const float* latent, const void* gamma, float eps,
+                                    const void* w_up, const void* shared_act, const void* w_s2,
+                                    lmoe_dtype io_dtype, void* out, void* norm_out, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
   if (T < 0 || L <= 0 || H <= 0 || I <= 0) return LMOE_ERR_INVALID_ARG;
   if (!dense_elt(io_dtype) || !(eps >= 0.0f) || !isfinite(eps)) return LMOE_ERR_INVALID_ARG;
   if (L % kchunk_of(io_dtype) != 0 || I % kchunk_of(io_dtype) != 0 || H % 16 != 0) return LMOE_ERR_UNSUPPORTED;
@@ -510,23 +533,18 @@ lmoe_status lmoe_tail_shared(int T, int L, int H, int I, const float* latent, co
   if (use_tiled_dense(T, io_dtype)) {
     // token-heavy: one tiled GEMM with two K phases, out = round(shared_act w_s2^T +
     // norm_out w_up^T): the shared-expert FC2 and the up projection accumulate into the
-    // same fp32 tiles (the shared output is not rounded on its own here)
-    StreamGemm g{};
-    g.a = shared_act;
-    g.a_bytes = (uint32_t)((long)T * I * esize_of(io_dtype));
-    g.lda = I;
-    g.Kd = I;
-    g.a1 = norm_out;
-    g.a1_bytes = (uint32_t)((long)T * L * esize_of(io_dtype));
-    g.lda1 = L;
-    g.Kd1 = L;
-    g.w1 = w_up;
-    g.M = T;
-    g.topk = 1;
-    g.beta = 1.0f;
-    g.nseg = 1;
-    g.seg[0] = Seg{w_s2, H, H, Epi::STORE, elt_of(io_dtype), out, H, 0, 0};
+    // same fp32 tiles (the shared output is not rounded on its own here); with a
+    // workspace, split-K when the tiles alone would leave CUs idle
+    StreamGemm g = tail_shared_gemm(T, L, H, I, w_up, shared_act, w_s2, io_dtype, out, norm_out);
     if (!tiled_dual_ok(g)) return LMOE_ERR_UNSUPPORTED;
+    if (workspace) {
+      const int k = tiled_splitk(g);
+      if (k > 1) {
+        if (workspace_bytes < tiled_splitk_bytes(g, k)) return LMOE_ERR_WORKSPACE;
+        g.part = static_cast<float*>(workspace);
+        g.ksplit = k;
+      }
+    }
     return hip_status(launch_tiled_gemm(g, stream));
   }
   StreamGemm g{};
@@ -545,6 +563,28 @@ lmoe_status lmoe_tail_shared(int T, int L, int H, int I, const float* latent, co
   g.nseg = 1;
   g.seg[0] = Seg{w_s2, H, H, Epi::ADD2, elt_of(io_dtype), out, H, 0, 0};
   return hip_status(launch_stream_gemm(g, elt_of(io_dtype), (T + 15) / 16, stream));
+}
+
+lmoe_status lmoe_tail_shared(int T, int L, int H, int I, const float* latent, const void* gamma, float eps,
+                             const void* w_up, const void* shared_act, const void* w_s2, lmoe_dtype io_dtype,
+                             void* out, void* norm_out, hipStream_t stream) {
+  return tail_shared_impl(T, L, H, I, latent, gamma, eps, w_up, shared_act, w_s2, io_dtype, out, norm_out, nullptr,
+                          0, stream);
+}
+
+size_t lmoe_tail_shared_workspace_bytes(int T, int L, int H, int I, lmoe_dtype io_dtype) {
+  if (T <= 0 || L <= 0 || H <= 0 || I <= 0 || !dense_elt(io_dtype) || !use_tiled_dense(T, io_dtype)) return 0;
+  if (L % kchunk_of(io_dtype) != 0 || I % kchunk_of(io_dtype) != 0 || H % 16 != 0) return 0;
+  const StreamGemm g = tail_shared_gemm(T, L, H, I, nullptr, nullptr, nullptr, io_dtype, nullptr, nullptr);
+  return tiled_splitk_bytes(g, tiled_splitk(g));
+}
+
+lmoe_status lmoe_tail_shared_ws(int T, int L, int H, int I, const float* latent, const void* gamma, float eps,
+                                const void* w_up, const void* shared_act, const void* w_s2, lmoe_dtype io_dtype,
+                                void* out, void* norm_out, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  return tail_shared_impl(T, L, H, I, latent, gamma, eps, w_up, shared_act, w_s2, io_dtype, out, norm_out,
+                          workspace, workspace_bytes, stream);
 }
 
 lmoe_status lmoe_situ_masked(int E, int T_max, int d, lmoe_dtype dtype, const void* in,

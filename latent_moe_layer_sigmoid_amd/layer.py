@@ -126,6 +126,10 @@ class LatentMoELayer:
         fws = max(fw2, fw3)
         b["front_ws"] = torch.empty(max(fws // 4, 1), dtype=torch.float32, device=dev) if fws else None
         b["front_ws_bytes"] = fws
+        # split-K workspace of the fused tail (shared FC2 + up projection)
+        tws = B.lmoe_tail_shared_workspace_bytes(T, s.L, s.H, s.I, dtl)
+        b["tail_ws"] = torch.empty(max(tws // 4, 1), dtype=torch.float32, device=dev) if tws else None
+        b["tail_ws_bytes"] = tws
         if s.experts == "mx":
             b["xq"] = torch.empty(T, s.L, dtype=torch.uint8, device=dev)
             b["xs"] = torch.empty(T, s.L // 32, dtype=torch.uint8, device=dev)
@@ -167,8 +171,8 @@ class LatentMoELayer:
         if self.fused:
             # shared expert's FC2 folded into the up projection: one GEMM over both K ranges
             mark("tail")
-            B.lmoe_tail_shared(T, s.L, s.H, s.I, None, w["gamma"], s.eps, w["W_up"], b["act_s"], w["W_s2"], dt,
-                               b["out"], b["n"], stream)
+            B.lmoe_tail_shared_ws(T, s.L, s.H, s.I, None, w["gamma"], s.eps, w["W_up"], b["act_s"], w["W_s2"], dt,
+                                  b["out"], b["n"], b["tail_ws"], b["tail_ws_bytes"], stream)
         else:
             # shared expert (dense mode: E = K = 1)
             mark("shared_fc1")
@@ -313,8 +317,8 @@ class LatentMoELayer:
         main.wait_event(shared_done)
         mark("tail")
         if fold:
-            B.lmoe_tail_shared(T, s.L, s.H, s.I, None, w["gamma"], s.eps, w["W_up"], b["act_s"], w["W_s2"], dt,
-                               b["out"], b["n"], main)
+            B.lmoe_tail_shared_ws(T, s.L, s.H, s.I, None, w["gamma"], s.eps, w["W_up"], b["act_s"], w["W_s2"], dt,
+                                  b["out"], b["n"], b["tail_ws"], b["tail_ws_bytes"], main)
         else:
             B.lmoe_tail(T, s.L, s.H, None, w["gamma"], s.eps, w["W_up"], b["sh"], dt, b["out"], b["n"], main)
         mark(None)

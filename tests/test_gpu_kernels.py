@@ -732,6 +732,41 @@ def test_tail_shared_matches_oracle(B, T, L, H, I, dt):
     assert norm_err(f64(out), rout) <= 1e-2
 
 
+@pytest.mark.parametrize("T,L,H,I", [(1024, 2048, 7168, 4096), (300, 512, 400, 1280), (300, 512, 400, 1536)])
+def test_tail_shared_split_k_matches_oracle(B, T, L, H, I):
+    # the token-heavy fused tail with too few output tiles for the CUs: split-K slices over
+    # both K phases, against the oracle and against the unsplit call. Slices of 32-wide
+    # steps: 192 in 2 (the phase boundary at step 128 inside the second slice), 56 in 3
+    # (boundary 40 inside the third), 64 in 4 (boundary 48 at the start of the fourth)
+    rng = np.random.default_rng(T + 7 * L + I)
+    td = torch.bfloat16
+    z = torch.from_numpy(rng.standard_normal((T, L)) * 0.3).float()
+    gamma = torch.from_numpy(rng.uniform(0.9, 1.1, L)).to(td)
+    Wup = torch.from_numpy(rng.standard_normal((H, L)) / math.sqrt(L)).to(td)
+    a_s = torch.from_numpy(rng.standard_normal((T, I))).to(td)
+    Ws2 = torch.from_numpy(rng.standard_normal((H, I)) / math.sqrt(I)).to(td)
+    wsb = B.lmoe_tail_shared_workspace_bytes(T, L, H, I, B.LMOE_BF16)
+    assert wsb > 0              # 8 x 14 or 3 x 1 tiles on 256 CUs: split
+    ws = torch.empty(max(wsb // 4, 1), dtype=torch.float32, device=DEV)
+    args = (T, L, H, I, z.to(DEV), gamma.to(DEV), 1e-6, B.packed(Wup.to(DEV)), a_s.to(DEV), B.packed(Ws2.to(DEV)),
+            B.LMOE_BF16)
+    out, n = torch.empty(T, H, dtype=td, device=DEV), torch.empty(T, L, dtype=td, device=DEV)
+    B.lmoe_tail_shared_ws(*args, out, n, ws, wsb)
+    out1, n1 = torch.empty(T, H, dtype=td, device=DEV), torch.empty(T, L, dtype=td, device=DEV)
+    B.lmoe_tail_shared(*args, out1, n1)
+    if wsb > 0:
+        with pytest.raises(B.LmoeError) as ei:
+            B.lmoe_tail_shared_ws(*args, out1, n1, ws, wsb - 4)
+        assert ei.value.status == B.LMOE_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    sel = np.arange(T) if T <= 300 else np.array([0, 1, 511, 1022, 1023])
+    sh = oracle.round_to(oracle.linear(f64(a_s)[sel], f64(Ws2)), "bf16")
+    rn, rout = oracle.tail(f64(z)[sel], f64(gamma), 1e-6, f64(Wup), sh, "bf16")
+    assert norm_err(f64(n)[sel], rn) <= 1e-2
+    assert norm_err(f64(out)[sel], rout) <= 1e-2
+    assert norm_err(f64(out), f64(out1)) <= 1e-2
+
+
 # ------------------------------------------------------------------------------- tail
 
 @pytest.mark.parametrize("T,L,H,dt,alias", [(8, 2048, 7168, "bf16", False), (4, 128, 256, "f32", True),
