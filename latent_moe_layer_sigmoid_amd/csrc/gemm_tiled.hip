@@ -2,28 +2,31 @@
 // the prefill-sized projections of the hidden input, the tail, and the grouped expert
 // FC1 / FC2 over tiles of 128 expert rows.
 //
-// Workgroup tile: 128 rows x 512 weight rows, 256 threads = 4 wavefronts side by side,
-// each owning all 128 rows x its own 128 weight rows as 4 x 4 v_mfma_f32_32x32x16_bf16
-// tiles (256 fp32 accumulators per lane; one wavefront per SIMD). The 32 x 32 form issues
-// half as many MFMAs per K step as 16 x 16 tiles for the same work (measured: 2170 instead
-// of 2280 cycles per K step on the 8192-row dense shapes). A SituGLU wavefront
-// takes 64 gate rows and the matching 64 up rows. Per 32-wide K step the workgroup needs
-// 8 KB of activations and 32 KB of weights for 1024 MFMA cycles per SIMD (about 40 bytes
-// per clock per CU), and each wavefront reads 16 KB of operands from LDS.
+// Workgroup tile: 128 rows x 512 weight rows, 512 threads = 8 wavefronts, two per SIMD:
+// wavefront w owns rows 64 (w / 4) .. + 63 x weight rows 128 (w % 4) .. + 127 as 2 x 4
+// v_mfma_f32_32x32x16_bf16 tiles (128 fp32 accumulators per lane). With two wavefronts per
+// SIMD, one's waits (for a buffer-to-LDS copy to be taken, for LDS) overlap the other's
+// MFMAs; against four wavefronts of 256 accumulators the epilogue halves and the K loop
+// stays where it was, held by the rate at which a CU pulls operands into LDS (40 KB per
+// step in about 1800 cycles). A SituGLU column block holds 64 gate rows and the matching
+// 64 up rows. Per 32-wide K step the workgroup needs 8 KB of activations and 32 KB of
+// weights for 1024 MFMA cycles per SIMD, and each wavefront reads 12 KB of operands from
+// LDS.
 //
 // Operands reach LDS by direct buffer-to-LDS loads (buffer_load_dwordx4 ... lds) in the
 // packed MFMA order the weights already have in HBM: for each 16-row group and 32-wide K
 // step, a 1 KB block holding lane l = 16g + r's 16 bytes (row r, K 8g .. 8g + 7) at 16 l.
 // A 32 x 32 x 16 operand (row l % 32, K 8 (l / 32) .. + 7 of one half step) is then one
 // conflict-free ds_read_b128 from two neighbouring blocks, and the weights are copied
-// block for block. LDS is a ring of NSLOT 40 KB K steps, NSLOT - 1 of them in flight
-// while one is computed; the operands of step c + 1 are read from LDS into registers
-// while the MFMAs of step c run. Workgroups are ordered so that the 32 running on one XCD
-// cover 8 row tiles x 4 weight blocks, which share operands in that XCD's L2.
+// block for block; each wavefront copies one activation block and four weight blocks per
+// step. LDS is a ring of NSLOT 40 KB K steps, NSLOT - 1 of them in flight while one is
+// computed; the operands of step c + 1 are read from LDS into registers while the MFMAs of
+// step c run. Groups of 8 row tiles x all weight blocks share their operands in one XCD's
+// L2.
 //
-// The epilogue goes through LDS 64 rows at a time; the pair ids of the tile's rows are
-// requested before the K loop and the combine weights and in-place addends in batches, so
-// that no output row waits on a dependent global load of its own.
+// The epilogue goes through LDS 32 rows per wavefront at a time; the pair ids of the
+// tile's rows are requested before the K loop and the combine weights and in-place
+// addends before the stores, so that no output row waits on a dependent global load.
 //
 // Epilogues: plain store, SituGLU (vLLM PR 50088, commit 2), weighted per-pair store for
 // the combine (TensorRT-LLM PR 20541, "Commit 1": finalize), and the in-place add of the
@@ -40,7 +43,7 @@ constexpr int TILE_N = 512;           // weight rows per workgroup (SituGLU: 256
 constexpr int NSLOT = 4;              // LDS ring of K steps
 constexpr int SLOT = 40960;           // bytes per K step: A 8 x 1 KB + B 32 x 1 KB
 constexpr int B_OFF = 8192;
-constexpr int LOADS_PER_STEP = 10;    // per wavefront: 2 A blocks + 8 B blocks
+constexpr int LOADS_PER_STEP = 5;     // per wavefront: 1 A block + 4 B blocks
 constexpr int GROUP_M = 8;            // row tiles per swizzle group
 
 // s_waitcnt immediates (gfx9 encoding): vm = vector-memory count (6 bits), lgkm = LDS
@@ -94,15 +97,17 @@ LMOE_DEV void lds_barrier() {
 }
 
 struct Frag {
-  bf16x8_t a[8], b[8];
+  bf16x8_t a[4], b[8];
 };
 
 template <bool ADD_PRE, bool DUAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void tiled_gemm_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void tiled_gemm_kernel(
     const StreamGemm g, int blocks_total, int m_tiles, int nch_total) {
   __shared__ __attribute__((aligned(1024))) char smem[NSLOT * SLOT];
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // 0 .. 7
+  const int cb = wave & 3;     // the wavefront's 128 weight rows (column block of the tile)
+  const int rh = wave >> 2;    // the wavefront's 64 rows of the tile
   const int m = lane & 15, g4 = lane >> 4;
 
   // ---- tile of this workgroup. Logical ids come in groups of GROUP_M row tiles x all
@@ -145,12 +150,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if (e < 0) return;
   }
 
-  // ---- activation rows this wavefront copies (row groups 2*wave, 2*wave + 1)
+  // ---- activation rows this wavefront copies (row group `wave` of the tile's 8)
   rsrc_t a_rs = make_rsrc(uniform_ptr(g.a), __builtin_amdgcn_readfirstlane(g.a_bytes));
-  uint32_t a_off[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int row = row0 + 16 * (2 * wave + h) + m;
+  uint32_t a_off;
+  {
+    const int row = row0 + 16 * wave + m;
     int arow;
     if (grouped) {
       int p = g.row_to_pair[row];
@@ -160,27 +164,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     } else {
       arow = min(row, g.M - 1);
     }
-    a_off[h] = (uint32_t)arow * (uint32_t)(g.lda * 2) + g4 * 16;
+    a_off = (uint32_t)arow * (uint32_t)(g.lda * 2) + g4 * 16;
   }
-  // pair of the output rows row0 + lane and row0 + 64 + lane (-1: padding or past M), read
-  // by the epilogue; requested here so that its latency hides behind the K loop
-  int rp[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int row = row0 + 64 * h + lane;
-    rp[h] = grouped ? g.row_to_pair[row] : (row < g.M ? row : -1);
+  // pair of the output row row0 + 64 rh + lane (-1: padding or past M), read by the
+  // epilogue; requested here so that its latency hides behind the K loop
+  int rp;
+  {
+    const int row = row0 + 64 * rh + lane;
+    rp = grouped ? g.row_to_pair[row] : (row < g.M ? row : -1);
   }
 
-  // ---- weight row groups of this wavefront (its own 8 groups; SituGLU: 4 gate + 4 up)
+  // ---- weight row groups this wavefront copies: LDS blocks 4 wave .. 4 wave + 3 of the
+  // 32 (block q holds row group q % 8 of column block q / 8; SituGLU: 4 gate + 4 up)
   const uint32_t w_bytes = __builtin_amdgcn_readfirstlane((uint32_t)sg.n_total * (uint32_t)(g.Kd * 2));
   rsrc_t w_rs = make_rsrc(uniform_ptr(reinterpret_cast<const char*>(sg.w) + (size_t)e * w_bytes), w_bytes);
-  uint32_t b_off[8];
+  auto n16_of = [&](int q) __attribute__((always_inline)) {
+    const int cw = q >> 3, j = q & 7;
+    return situ ? (j < 4 ? nb * 16 + 4 * cw + j : sg.n_out / 16 + nb * 16 + 4 * cw + (j - 4))
+                : nb * 32 + 8 * cw + j;
+  };
+  uint32_t b_off[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int n16 = situ ? (j < 4 ? nb * 16 + 4 * wave + j : sg.n_out / 16 + nb * 16 + 4 * wave + (j - 4))
-                         : nb * 32 + 8 * wave + j;
-    b_off[j] = (uint32_t)n16 * (uint32_t)(g.Kd * 32) + lane * 16;   // past the matrix: zeros
-  }
+  for (int j = 0; j < 4; ++j)
+    b_off[j] = (uint32_t)n16_of(4 * wave + j) * (uint32_t)(g.Kd * 32) + lane * 16;   // past the matrix: zeros
 
   // Two K phases (DUAL, dense, one plain segment): steps 0 .. nch0 - 1 multiply `a` by the
   // segment's weights, the rest `a1` by `w1`, accumulating into the same fp32 tiles, so
@@ -190,29 +196,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   int kb = 0;                              // first step of the phase being copied
   auto to_phase1 = [&]() __attribute__((always_inline)) {
     a_rs = make_rsrc(uniform_ptr(g.a1), __builtin_amdgcn_readfirstlane(g.a1_bytes));
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int arow = min(row0 + 16 * (2 * wave + h) + m, g.M - 1);
-      a_off[h] = (uint32_t)arow * (uint32_t)(g.lda1 * 2) + g4 * 16;
-    }
+    a_off = (uint32_t)min(row0 + 16 * wave + m, g.M - 1) * (uint32_t)(g.lda1 * 2) + g4 * 16;
     const uint32_t w1_bytes = __builtin_amdgcn_readfirstlane((uint32_t)sg.n_total * (uint32_t)(g.Kd1 * 2));
     w_rs = make_rsrc(uniform_ptr(g.w1), w1_bytes);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      b_off[j] = (uint32_t)(nb * 32 + 8 * wave + j) * (uint32_t)(g.Kd1 * 32) + lane * 16;
+    for (int j = 0; j < 4; ++j) b_off[j] = (uint32_t)n16_of(4 * wave + j) * (uint32_t)(g.Kd1 * 32) + lane * 16;
     kb = nch0;
   };
   // a split-K slice that starts in the second phase copies its operands from the start
   if constexpr (DUAL)
     if (k0 >= nch0) to_phase1();
-  // copy k of step c: k = 0, 1 this wavefront's two activation row groups, 2 .. 9 its
-  // eight weight row groups
+  // copy k of step c: k = 0 this wavefront's activation row group, 1 .. 4 its four weight
+  // row groups
   auto issue_one = [&](int c, int k) __attribute__((always_inline)) {
     char* base = smem + (c % NSLOT) * SLOT;
-    if (k < 2)
-      to_lds(a_rs, base + (2 * wave + k) * 1024, a_off[k], (uint32_t)(c + k0 - kb) * 64u);
+    if (k < 1)
+      to_lds(a_rs, base + wave * 1024, a_off, (uint32_t)(c + k0 - kb) * 64u);
     else
-      to_lds(w_rs, base + B_OFF + (8 * wave + k - 2) * 1024, b_off[k - 2], (uint32_t)(c + k0 - kb) * 1024u);
+      to_lds(w_rs, base + B_OFF + (4 * wave + k - 1) * 1024, b_off[k - 1], (uint32_t)(c + k0 - kb) * 1024u);
   };
   auto issue = [&](int c) {
     if constexpr (DUAL)
@@ -223,22 +224,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // 32 x 32 x 16 operand of lane l: row l % 32 of a 32-row tile (16-row block (l / 16) & 1),
   // K 8 (l / 32) .. + 7 of the half step h: K group 2 h + l / 32 of that block
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)smem + ((lane >> 4) & 1) * 1024 + (lane >> 5) * 256 + (lane & 15) * 16;
-  // fragment K (a compile-time 0 .. 15) of step c: 0 .. 7 activation tile K / 2, half step
-  // K % 2; 8 .. 15 the same for the weights
+  // fragment K (a compile-time 0 .. 11) of step c: 0 .. 3 activation tile K / 2 of the
+  // wavefront's two (32-row tiles 2 rh, 2 rh + 1), half step K % 2; 4 .. 11 weight tile
+  // (K - 4) / 2 of its column block, half step K % 2
+  const uint32_t lds_a = lds0 + (uint32_t)rh * 4096;
+  const uint32_t lds_b = lds0 + B_OFF + (uint32_t)cb * 8192;
   auto read_one = [&](int c, Frag& f, auto K) __attribute__((always_inline)) {
-    constexpr int k = decltype(K)::value, q = k & 7;
-    const uint32_t base = lds0 + (uint32_t)(c % NSLOT) * SLOT + (k < 8 ? 0 : B_OFF + wave * 8192);
-    const bf16x8_t v = lds_read16<(q >> 1) * 2048 + (q & 1) * 512>(base);
-    if constexpr (k < 8)
-      f.a[q] = v;
-    else
-      f.b[q] = v;
+    constexpr int k = decltype(K)::value;
+    if constexpr (k < 4) {
+      f.a[k] = lds_read16<(k >> 1) * 2048 + (k & 1) * 512>(lds_a + (uint32_t)(c % NSLOT) * SLOT);
+    } else {
+      constexpr int q = k - 4;
+      f.b[q] = lds_read16<(q >> 1) * 2048 + (q & 1) * 512>(lds_b + (uint32_t)(c % NSLOT) * SLOT);
+    }
   };
-  auto read = [&](int c, Frag& f) { static_for<16>([&](auto k) { read_one(c, f, k); }); };
+  auto read = [&](int c, Frag& f) { static_for<12>([&](auto k) { read_one(c, f, k); }); };
 
-  floatx16 acc[4][4];
+  floatx16 acc[2][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
 
@@ -246,7 +250,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[2 * i + h], f.b[2 * j + h], acc[i][j], 0, 0, 0);
@@ -289,23 +293,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     __builtin_amdgcn_sched_barrier(0);
     if (c + NSLOT < nch) issue(c + NSLOT);
   };
-  // Steps whose copy c + NSLOT exists: the fragment reads follow the first 16 MFMAs one by
-  // one and the 10 copies every third MFMA, each pinned in place. One wavefront per SIMD
-  // has nothing to issue while it waits for the address unit to take a copy; placed
-  // between MFMAs, the wait overlaps the MFMA already running (measured on the 8192-row
-  // dense shapes: 1140-1570 cycles per K step instead of 2180; reads and copies in a
-  // block each, or left to the scheduler, 1400-1800).
+  // Steps whose copy c + NSLOT exists: the fragment reads follow the first 12 MFMAs one by
+  // one and the 5 copies every third MFMA, each pinned in place, so that a wait for the
+  // address unit to take a copy overlaps the MFMA already running (and the other
+  // wavefront of the SIMD).
   auto step_il = [&](int c, Frag& cur, Frag& nxt) __attribute__((always_inline)) {
     wait_steps(NSLOT - 2);
     lds_barrier();
     if constexpr (DUAL)
       if (c + NSLOT + k0 == nch0) to_phase1();
-    static_for<32>([&](auto I) __attribute__((always_inline)) {
+    static_for<16>([&](auto I) __attribute__((always_inline)) {
       constexpr int i = decltype(I)::value;
-      constexpr int h = i >> 4, ti = (i >> 2) & 3, tj = i & 3;
+      constexpr int h = i >> 3, ti = (i >> 2) & 1, tj = i & 3;
       acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[2 * ti + h], cur.b[2 * tj + h], acc[ti][tj], 0, 0, 0);
-      if constexpr (i < 16) read_one(c + 1, nxt, std::integral_constant<int, i>{});
-      if constexpr (i % 3 == 2 && i / 3 < LOADS_PER_STEP) issue_one(c + NSLOT, i / 3);
+      if constexpr (i < 12) read_one(c + 1, nxt, std::integral_constant<int, i>{});
+      if constexpr (i % 3 == 1 && i / 3 < LOADS_PER_STEP) issue_one(c + NSLOT, i / 3);
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -320,35 +322,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   if (c < nch) step(c, f0, f1);
 
-  // ---- epilogue, 64 rows at a time through this wavefront's own LDS region (every
+  // ---- epilogue, 32 rows at a time through this wavefront's own LDS region (every
   // wavefront is past its last LDS read and every buffer-to-LDS load has landed): the
-  // accumulators of 64 rows are written to LDS as fp32 [64][RS], then read back as 4
+  // accumulators of 32 rows are written to LDS as fp32 [32][RS], then read back as 4
   // consecutive columns per lane so that the outputs leave as contiguous row segments.
   constexpr int RS = 132;                          // row stride (floats), padded against bank conflicts
-  float* red = reinterpret_cast<float*>(smem) + wave * (64 * RS);
+  float* red = reinterpret_cast<float*>(smem) + wave * (32 * RS);
   const float inv_b = 1.0f / g.beta;
   const float inv_lb = g.lbeta > 0.0f ? 1.0f / g.lbeta : 0.0f;
-  // combine weights of this lane's two rows, requested once for the whole epilogue
-  float rw[2] = {1.0f, 1.0f};
-  if ((sg.epi == Epi::PAIR || sg.epi == Epi::TOKEN) && g.pair_w) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) rw[h] = rp[h] >= 0 ? g.pair_w[rp[h]] : 0.0f;
-  }
-  // rows of the tile up to the last one holding a pair (dense: the last one below M);
-  // the loops below skip whole batches of rows past it
-  const uint64_t m0 = __ballot(rp[0] >= 0), m1 = __ballot(rp[1] >= 0);
-  const int nv = m1 ? 128 - __builtin_clzll(m1) : (m0 ? 64 - __builtin_clzll(m0) : 0);
-  const int nv_half[2] = {min(nv, 64), max(nv - 64, 0)};
-  // accumulator tile (i, j) register rr: row 32 i + 8 (rr / 4) + 4 (lane / 32) + rr % 4,
-  // column 32 j + lane % 32 of the wavefront's 128 x 128 block; half h = rows 64 h ..
-  auto acc_to_lds = [&](auto h) __attribute__((always_inline)) {
+  // combine weight of this lane's row, requested once for the whole epilogue
+  float rw = 1.0f;
+  if ((sg.epi == Epi::PAIR || sg.epi == Epi::TOKEN) && g.pair_w) rw = rp >= 0 ? g.pair_w[rp] : 0.0f;
+  // rows of the wavefront's 64 up to the last one holding a pair (dense: the last one below
+  // M); the loops below skip whole batches of rows past it
+  const uint64_t mv = __ballot(rp >= 0);
+  const int nv = mv ? 64 - __builtin_clzll(mv) : 0;
+  const int nvq[2] = {min(nv, 32), max(nv - 32, 0)};
+  const int rbase0 = row0 + 64 * rh;
+  // accumulator tile (t, j) register rr: row 8 (rr / 4) + 4 (lane / 32) + rr % 4 of the
+  // wavefront's 32-row tile t, column 32 j + lane % 32 of its 128 columns
+  auto acc_to_lds = [&](auto T) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
-    static_for<2>([&](auto ii) {
-      static_for<4>([&](auto j) {
-        static_for<16>([&](auto rr) {
-          red[(32 * ii + 8 * (int(rr) >> 2) + 4 * (lane >> 5) + (int(rr) & 3)) * RS + 32 * j + (lane & 31)] =
-              acc[2 * int(h) + int(ii)][int(j)][int(rr)];
-        });
+    static_for<4>([&](auto j) {
+      static_for<16>([&](auto rr) {
+        red[(8 * (int(rr) >> 2) + 4 * (lane >> 5) + (int(rr) & 3)) * RS + 32 * j + (lane & 31)] =
+            acc[int(T)][int(j)][int(rr)];
       });
     });
     __builtin_amdgcn_sched_barrier(0);
@@ -368,18 +366,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     int pcol, valid;
     if (situ) {
       const int c = 4 * q;   // LDS columns 0..63: gate, 64..127: up
-      const int oc = 256 * nb + 64 * wave + (c & 63);
+      const int oc = 256 * nb + 64 * cb + (c & 63);
       valid = oc < sg.n_out;
       pcol = (c < 64 ? 0 : sg.n_out) + oc;
     } else {
-      pcol = TILE_N * nb + 128 * wave + 4 * q;
+      pcol = TILE_N * nb + 128 * cb + 4 * q;
       valid = pcol < sg.n_out;
     }
     float* dst = g.part + (size_t)ks * g.M * ptot + pbase + pcol;
-    static_for<2>([&](auto h) {
-      acc_to_lds(h);
-      const int rbase = row0 + 64 * h;
-      for (int r = lane >> 5; r < 64; r += 2) {
+    static_for<2>([&](auto t) {
+      acc_to_lds(t);
+      const int rbase = rbase0 + 32 * int(t);
+      for (int r = lane >> 5; r < 32; r += 2) {
         const int row = rbase + r;
         const floatx4 v = *reinterpret_cast<const floatx4*>(red + r * RS + 4 * q);
         if (row < g.M && valid) *reinterpret_cast<floatx4*>(dst + (size_t)row * ptot) = v;
@@ -392,71 +390,66 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // workgroup) so that they hold no per-row branches on them: in each batch of rows, the
   // LDS reads, row ids and combine weights are all requested before the first store, so
   // that no read waits behind a store or a branch; batches past the last row holding a
-  // pair are skipped. The batch loops are not unrolled: the epilogue runs once per
-  // workgroup, so its code is fetched cold, and a compact loop keeps that fetch short.
+  // pair are skipped. The loop over the two 32-row tiles is not unrolled: the epilogue runs
+  // once per workgroup, so its code is fetched cold, and a compact loop keeps that short.
   auto epilogue = [&](auto EP, auto F32OUT) __attribute__((always_inline)) {
     constexpr Epi ep = decltype(EP)::value;
     constexpr Elt oe = decltype(F32OUT)::value ? Elt::F32 : Elt::BF16;
     constexpr bool add_pre = ep == Epi::ADD && oe == Elt::BF16;
 #pragma unroll 1
-    for (int h = 0; h < 2; ++h) {
-      const int nvh = h ? nv_half[1] : nv_half[0];
-      if (nvh == 0) break;
-      const int rbase = row0 + 64 * h;
-      const int rph = h ? rp[1] : rp[0];
-      [[maybe_unused]] const float rwh = h ? rw[1] : rw[0];
-      // in-place addends (bf16) of every row of this half that this lane stores, requested
+    for (int t = 0; t < 2; ++t) {
+      const int nvt = t ? nvq[1] : nvq[0];
+      if (nvt == 0) break;
+      const int rbase = rbase0 + 32 * t;
+      // in-place addends (bf16) of every row of this tile that this lane stores, requested
       // before its stores: vector-memory stores and loads share one in-order counter, so a
       // load issued after a store would wait for it (each element is read and written by
       // the same lane, so `add` may be the output)
-      [[maybe_unused]] uint2 addv[add_pre ? 4 : 1][8];
+      [[maybe_unused]] uint2 addv[add_pre ? 2 : 1][8];
       if constexpr (add_pre) {
-        const int col = TILE_N * nb + 128 * wave + 4 * (lane & 31);
+        const int col = TILE_N * nb + 128 * cb + 4 * (lane & 31);
 #pragma unroll
-        for (int bt = 0; bt < 4; ++bt)
+        for (int bt = 0; bt < 2; ++bt)
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
             const int r = 16 * bt + 2 * u + (lane >> 5);
             addv[bt][u] = make_uint2(0u, 0u);
-            if (g.add != nullptr && r < nvh && rbase + r < g.M && col < sg.n_out)
+            if (g.add != nullptr && r < nvt && rbase + r < g.M && col < sg.n_out)
               addv[bt][u] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(g.add) +
                                                             (size_t)(rbase + r) * sg.ldo + col);
           }
       }
-      if (h == 0)
+      if (t == 0)
         acc_to_lds(std::integral_constant<int, 0>{});
       else
         acc_to_lds(std::integral_constant<int, 1>{});
       if constexpr (ep == Epi::SITU) {
         // 16 lanes per row (4 outputs each): gate columns c .. c + 3, up columns 64 + c ..;
-        // batches of 32 rows, 8 per lane
+        // one batch of 32 rows, 8 per lane
         const int q = lane & 15;
-        const int col = 256 * nb + 64 * wave + 4 * q;
+        const int col = 256 * nb + 64 * cb + 4 * q;
         const bool col_ok = col < sg.n_out;
-#pragma unroll 1
-        for (int r0 = 0; r0 < nvh; r0 += 32) {
-          floatx4 gv[8], uv[8];
-          int pr[8];
+        floatx4 gv[8], uv[8];
+        int pr[8];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int r = r0 + 4 * u + (lane >> 4);
-            pr[u] = __shfl(rph, r, WAVE);
-            gv[u] = *reinterpret_cast<const floatx4*>(red + r * RS + 4 * q);
-            uv[u] = *reinterpret_cast<const floatx4*>(red + r * RS + 64 + 4 * q);
-          }
+        for (int u = 0; u < 8; ++u) {
+          const int r = 4 * u + (lane >> 4);
+          pr[u] = __shfl(rp, 32 * t + r, WAVE);
+          gv[u] = *reinterpret_cast<const floatx4*>(red + r * RS + 4 * q);
+          uv[u] = *reinterpret_cast<const floatx4*>(red + r * RS + 64 + 4 * q);
+        }
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            if (pr[u] < 0 || !col_ok) continue;
-            floatx4 v;
+        for (int u = 0; u < 8; ++u) {
+          if (pr[u] < 0 || !col_ok) continue;
+          floatx4 v;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) v[k] = situ_f(gv[u][k], uv[u][k], g.beta, inv_b, g.lbeta, inv_lb);
-            store4(oe, sg.out, (size_t)(rbase + r0 + 4 * u + (lane >> 4)) * sg.ldo + col, v);
-          }
+          for (int k = 0; k < 4; ++k) v[k] = situ_f(gv[u][k], uv[u][k], g.beta, inv_b, g.lbeta, inv_lb);
+          store4(oe, sg.out, (size_t)(rbase + 4 * u + (lane >> 4)) * sg.ldo + col, v);
         }
       } else {
         // 32 lanes per row (4 columns each), batches of 16 rows, 8 per lane
         const int q = lane & 31;
-        const int col = TILE_N * nb + 128 * wave + 4 * q;
+        const int col = TILE_N * nb + 128 * cb + 4 * q;
         const bool col_ok = col < sg.n_out;
         auto batch = [&](int r0, auto BT) __attribute__((always_inline)) {
           floatx4 v[8];
@@ -465,8 +458,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
             const int r = r0 + 2 * u + (lane >> 5);
-            pr[u] = __shfl(rph, r, WAVE);
-            if constexpr (ep == Epi::PAIR || ep == Epi::TOKEN) wt[u] = __shfl(rwh, r, WAVE);
+            pr[u] = __shfl(rp, 32 * t + r, WAVE);
+            if constexpr (ep == Epi::PAIR || ep == Epi::TOKEN) wt[u] = __shfl(rw, 32 * t + r, WAVE);
             v[u] = *reinterpret_cast<const floatx4*>(red + r * RS + 4 * q);
           }
 #pragma unroll
@@ -494,12 +487,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         };
         if constexpr (add_pre) {
           // the addends sit in registers per batch: batches unrolled
-          static_for<4>([&](auto bt) {
-            if (16 * int(bt) < nvh) batch(16 * int(bt), bt);
+          static_for<2>([&](auto bt) {
+            if (16 * int(bt) < nvt) batch(16 * int(bt), bt);
           });
         } else {
 #pragma unroll 1
-          for (int r0 = 0; r0 < nvh; r0 += 16) batch(r0, std::integral_constant<int, 0>{});
+          for (int r0 = 0; r0 < nvt; r0 += 16) batch(r0, std::integral_constant<int, 0>{});
         }
       }
     }
@@ -630,11 +623,11 @@ hipError_t launch_tiled_gemm(StreamGemm g, hipStream_t stream) {
   const bool add_pre = g.nseg == 1 && g.seg[0].epi == Epi::ADD && g.add != nullptr && g.seg[0].out_elt == Elt::BF16 &&
                        g.ksplit == 1;
   if (dual)
-    hipLaunchKernelGGL((tiled_gemm_kernel<false, true>), dim3(grid), dim3(256), 0, stream, g, b0, m_tiles, nch);
+    hipLaunchKernelGGL((tiled_gemm_kernel<false, true>), dim3(grid), dim3(512), 0, stream, g, b0, m_tiles, nch);
   else if (add_pre)
-    hipLaunchKernelGGL((tiled_gemm_kernel<true, false>), dim3(grid), dim3(256), 0, stream, g, b0, m_tiles, nch);
+    hipLaunchKernelGGL((tiled_gemm_kernel<true, false>), dim3(grid), dim3(512), 0, stream, g, b0, m_tiles, nch);
   else
-    hipLaunchKernelGGL((tiled_gemm_kernel<false, false>), dim3(grid), dim3(256), 0, stream, g, b0, m_tiles, nch);
+    hipLaunchKernelGGL((tiled_gemm_kernel<false, false>), dim3(grid), dim3(512), 0, stream, g, b0, m_tiles, nch);
   if (g.ksplit > 1) {
     int ptot = 0, wmax = 0;
     for (int i = 0; i < g.nseg; ++i) {
