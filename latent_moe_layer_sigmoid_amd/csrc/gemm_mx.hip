@@ -35,10 +35,27 @@ struct MxStep {
 };
 
 template <int NT, int R>
-__global__ __launch_bounds__(64) void stream_gemm_mx_kernel(const StreamGemm g, int blocks_total, int nsteps) {
+__global__ __launch_bounds__(256) void stream_gemm_mx_kernel(const StreamGemm g, int blocks_total, int nsteps,
+                                                             int grouped_waves) {
   const int lane = threadIdx.x & 63;
-  const int mt = blockIdx.x / blocks_total;
-  const int nb = blockIdx.x - mt * blocks_total;
+  int mt, nb;
+  if (grouped_waves) {
+    // A workgroup's 4 wavefronts take 4 neighbouring column blocks of one row tile, so they
+    // request the same activation rows on one CU; the workgroups of a row tile run on one
+    // XCD (workgroup b runs on XCD b % 8), consecutive row tiles on the XCDs in turn, so
+    // that each tile's activation rows cross into one L2 only and the tiles holding rows
+    // (the first ones) spread over all XCDs.
+    const int nwb = (blocks_total + 3) / 4;
+    const int j = (int)(blockIdx.x >> 3);
+    const int lid = ((j / nwb) * 8 + (int)(blockIdx.x & 7)) * nwb + j % nwb;
+    mt = lid / nwb;
+    nb = (lid - mt * nwb) * 4 + (int)(threadIdx.x >> 6);
+    if (nb >= blocks_total) return;
+  } else {
+    // one wavefront per workgroup, column blocks of a row tile consecutive
+    mt = blockIdx.x / blocks_total;
+    nb = blockIdx.x - mt * blocks_total;
+  }
   const int row0 = mt * 16 * R;   // R row groups of 16 share every weight fragment
   if (row0 >= g.M) return;
   const Seg sg = g.seg[0];
@@ -216,12 +233,20 @@ hipError_t launch_stream_gemm_mx(StreamGemm g, int live, hipStream_t stream) {
   g.seg[0].blocks = blocks;
   g.seg[0].block0 = 0;
   g.nseg = 1;
+  // FC1 (long K: 64 KB of activation rows per 32-row tile): workgroups of 4 wavefronts
+  // (4 column blocks of one row tile), whole rounds of 8 row tiles (one per XCD), the ids
+  // past the tiles returning at once. FC2 (K = d: 16 KB per tile) measured faster with one
+  // wavefront per workgroup.
+  const bool grouped_waves = g.seg[0].epi == Epi::SITU_MX;
+  const unsigned grid = grouped_waves ? (unsigned)(((m_tiles + 7) / 8) * 8 * ((blocks + 3) / 4))
+                                      : (unsigned)(m_tiles * blocks);
+  const unsigned threads = grouped_waves ? 256 : 64;
   if (R == 2)
-    hipLaunchKernelGGL((stream_gemm_mx_kernel<NT, 2>), dim3((unsigned)(m_tiles * blocks)), dim3(64), 0, stream, g,
-                       blocks, nsteps);
+    hipLaunchKernelGGL((stream_gemm_mx_kernel<NT, 2>), dim3(grid), dim3(threads), 0, stream, g, blocks, nsteps,
+                       (int)grouped_waves);
   else
-    hipLaunchKernelGGL((stream_gemm_mx_kernel<NT, 1>), dim3((unsigned)(m_tiles * blocks)), dim3(64), 0, stream, g,
-                       blocks, nsteps);
+    hipLaunchKernelGGL((stream_gemm_mx_kernel<NT, 1>), dim3(grid), dim3(threads), 0, stream, g, blocks, nsteps,
+                       (int)grouped_waves);
   return hipGetLastError();
 }
 
