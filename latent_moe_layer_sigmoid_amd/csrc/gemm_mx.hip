@@ -72,6 +72,14 @@ __global__ __launch_bounds__(256) void stream_gemm_mx_kernel(const StreamGemm g,
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int i = 0; i < 4; ++i) pair_o[r][i] = g.row_to_pair[row0 + 16 * r + 4 * g4 + i];
+  // combine weights of the lane's output rows (FC2), requested now so that their latency
+  // hides behind the K loop
+  float pw[R][4];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      pw[r][i] = (!situ && g.pair_w != nullptr && pair_o[r][i] >= 0) ? g.pair_w[pair_o[r][i]] : 1.0f;
 
   // weight tiles (packed codes and scales of expert e)
   const int half = NT / 2;
@@ -203,7 +211,7 @@ __global__ __launch_bounds__(256) void stream_gemm_mx_kernel(const StreamGemm g,
       for (int i = 0; i < 4; ++i) {
         const int pair = pair_o[r][i];
         if (pair < 0) continue;
-        const float wgt = g.pair_w ? g.pair_w[pair] : 1.0f;
+        const float wgt = pw[r][i];
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
           const int col = nb * NT * 16 + j * 16 + m;

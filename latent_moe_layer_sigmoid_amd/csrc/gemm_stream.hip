@@ -222,6 +222,36 @@ __global__ __launch_bounds__(512) void stream_gemm_kernel(const StreamGemm g, in
     a1_off = (uint32_t)arow * (uint32_t)(g.lda1 * TR::BYTES) + g4 * 16;
   }
 
+  // ---- epilogue operands, requested now so that their latency hides behind the K loop
+  // (loaded in the epilogue, each would wait behind every load still in flight): the
+  // combine weights of the lane's four rows (PAIR / TOKEN; four-tile waves, the grouped
+  // FC2's shape) and the in-place addends (ADD; one-tile waves, the up projection's shape;
+  // the lane reads the elements it writes). Other widths load them in the epilogue: the
+  // registers held through the K loop would cost them a wave per SIMD.
+  constexpr bool PW_PRE = NT == 4;
+  float pw[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+  if constexpr (PW_PRE) {
+    if ((sg.epi == Epi::PAIR || sg.epi == Epi::TOKEN) && g.pair_w != nullptr) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int orow = row0 + 4 * g4 + i;
+        const int pair = grouped ? pair_o[i] : (orow < g.M ? orow : -1);
+        if (pair >= 0) pw[i] = g.pair_w[pair];
+      }
+    }
+  }
+  constexpr bool ADD_PRE_OK = NT == 1 && !DUAL && !MB;
+  const bool add_pre = ADD_PRE_OK && sg.epi == Epi::ADD && g.add != nullptr;
+  float addv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (ADD_PRE_OK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int orow = row0 + 4 * g4 + i;
+      const int col = nb * 16 + m;
+      if (add_pre && orow < g.M && col < sg.n_out) addv[i] = load_elt(sg.out_elt, g.add, (size_t)orow * sg.ldo + col);
+    }
+  }
+
   floatx4 acc[NACC];
 #pragma unroll
   for (int j = 0; j < NACC; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -258,14 +288,14 @@ __global__ __launch_bounds__(512) void stream_gemm_kernel(const StreamGemm g, in
           if (sg.epi == Epi::STORE) {
             store_elt(sg.out_elt, sg.out, (size_t)orow * sg.ldo + col, v);
           } else if (sg.epi == Epi::PAIR) {
-            const float wgt = g.pair_w ? g.pair_w[pair] : 1.0f;
+            const float wgt = PW_PRE ? pw[i] : (g.pair_w ? g.pair_w[pair] : 1.0f);
             reinterpret_cast<float*>(sg.out)[(size_t)pair * sg.ldo + col] = wgt * v;
           } else if (sg.epi == Epi::TOKEN) {
-            const float wgt = g.pair_w ? g.pair_w[pair] : 1.0f;
+            const float wgt = PW_PRE ? pw[i] : (g.pair_w ? g.pair_w[pair] : 1.0f);
             store_elt(sg.out_elt, sg.out, (size_t)(pair / g.topk) * sg.ldo + col, wgt * v);
           } else if (sg.epi == Epi::ADD) {
             const size_t idx = (size_t)orow * sg.ldo + col;
-            const float add = g.add ? load_elt(sg.out_elt, g.add, idx) : 0.0f;
+            const float add = add_pre ? addv[i] : (g.add ? load_elt(sg.out_elt, g.add, idx) : 0.0f);
             store_elt(sg.out_elt, sg.out, idx, add + v);
           } else if (DUAL) {   // ADD2: the first phase's result rounded to the output type, plus the second's
             if (sg.out_elt == Elt::BF16) v = bf16_to_f32(f32_to_bf16(v));
