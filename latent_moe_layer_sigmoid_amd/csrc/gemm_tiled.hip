@@ -24,6 +24,11 @@
 // step c run. Groups of 8 row tiles x all weight blocks share their operands in one XCD's
 // L2.
 //
+// A wavefront computes only those of its two 32-row tiles that hold a row to store: the
+// padding at the end of an expert's last tile (and, in the dense launches that need no
+// tail or add, rows past M) takes no MFMAs and no fragment reads, while the copies, waits
+// and barriers stay those of every other wavefront.
+//
 // The epilogue goes through LDS 32 rows per wavefront at a time; the pair ids of the
 // tile's rows are requested before the K loop and the combine weights and in-place
 // addends before the stores, so that no output row waits on a dependent global load.
@@ -229,16 +234,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // (K - 4) / 2 of its column block, half step K % 2
   const uint32_t lds_a = lds0 + (uint32_t)rh * 4096;
   const uint32_t lds_b = lds0 + B_OFF + (uint32_t)cb * 8192;
-  auto read_one = [&](int c, Frag& f, auto K) __attribute__((always_inline)) {
+  // NA (compile time): how many of the wavefront's two 32-row tiles it computes; the
+  // fragments of the others are not read
+  auto read_one = [&](int c, Frag& f, auto K, auto NA) __attribute__((always_inline)) {
     constexpr int k = decltype(K)::value;
+    constexpr int na = decltype(NA)::value;
     if constexpr (k < 4) {
-      f.a[k] = lds_read16<(k >> 1) * 2048 + (k & 1) * 512>(lds_a + (uint32_t)(c % NSLOT) * SLOT);
-    } else {
+      if constexpr ((k >> 1) < na)
+        f.a[k] = lds_read16<(k >> 1) * 2048 + (k & 1) * 512>(lds_a + (uint32_t)(c % NSLOT) * SLOT);
+    } else if constexpr (na > 0) {
       constexpr int q = k - 4;
       f.b[q] = lds_read16<(q >> 1) * 2048 + (q & 1) * 512>(lds_b + (uint32_t)(c % NSLOT) * SLOT);
     }
   };
-  auto read = [&](int c, Frag& f) { static_for<12>([&](auto k) { read_one(c, f, k); }); };
+  auto read = [&](int c, Frag& f, auto NA) { static_for<12>([&](auto k) { read_one(c, f, k, NA); }); };
 
   floatx16 acc[2][4];
 #pragma unroll
@@ -246,11 +255,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
 
-  auto mma = [&](const Frag& f) {
+  auto mma = [&](const Frag& f, auto NA) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < decltype(NA)::value; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[2 * i + h], f.b[2 * j + h], acc[i][j], 0, 0, 0);
@@ -273,23 +282,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   wait_steps(min(nch, NSLOT) - 1);
   lds_barrier();
-  Frag f0, f1;
-  read(0, f0);
+  // The wavefront's 32-row tiles that hold a row to store (padding rows and rows past M
+  // come last in a tile): only those are computed, and a wavefront with none only copies.
+  // Its row ids were requested before the copies, so they have landed by now.
+  const uint64_t mv = __ballot(rp >= 0);
+  const int nv = mv ? 64 - __builtin_clzll(mv) : 0;
+  const int n_act = __builtin_amdgcn_readfirstlane((nv + 31) >> 5);
 
   // ---- main loop, two steps per trip so that the register fragments alternate.
   // Step c: wait until step c + 1 has landed (this wavefront's loads, then the barrier for
   // the others) and this wavefront's reads of step c (slot c % NSLOT) are done; after the
   // barrier every wavefront is done with that slot, and step c + NSLOT goes into it. Then
   // read step c + 1 into registers while the MFMAs of step c run.
-  auto step = [&](int c, Frag& cur, Frag& nxt) {
+  auto step = [&](int c, Frag& cur, Frag& nxt, auto NA) {
     // issued so far: steps up to min(c + NSLOT - 1, nch - 1)
     wait_steps(min(c + NSLOT - 1, nch - 1) - (c + 1));
     lds_barrier();                        // nothing moves across the waits and the barrier
     // fragment reads, then the MFMAs, then the copies of step c + NSLOT: a wavefront's
     // buffer-to-LDS copies can hold up its in-order issue (measured: placed before the
     // MFMAs they cost about 3% more per step than placed after them)
-    if (c + 1 < nch) read(c + 1, nxt);
-    mma(cur);
+    if (c + 1 < nch) read(c + 1, nxt, NA);
+    mma(cur, NA);
     __builtin_amdgcn_sched_barrier(0);
     if (c + NSLOT < nch) issue(c + NSLOT);
   };
@@ -297,7 +310,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // one and the 5 copies every third MFMA, each pinned in place, so that a wait for the
   // address unit to take a copy overlaps the MFMA already running (and the other
   // wavefront of the SIMD).
-  auto step_il = [&](int c, Frag& cur, Frag& nxt) __attribute__((always_inline)) {
+  auto step_il = [&](int c, Frag& cur, Frag& nxt, auto NA) __attribute__((always_inline)) {
     wait_steps(NSLOT - 2);
     lds_barrier();
     if constexpr (DUAL)
@@ -305,22 +318,35 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     static_for<16>([&](auto I) __attribute__((always_inline)) {
       constexpr int i = decltype(I)::value;
       constexpr int h = i >> 3, ti = (i >> 2) & 1, tj = i & 3;
-      acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[2 * ti + h], cur.b[2 * tj + h], acc[ti][tj], 0, 0, 0);
-      if constexpr (i < 12) read_one(c + 1, nxt, std::integral_constant<int, i>{});
+      if constexpr (ti < decltype(NA)::value)
+        acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[2 * ti + h], cur.b[2 * tj + h], acc[ti][tj], 0, 0, 0);
+      if constexpr (i < 12) read_one(c + 1, nxt, std::integral_constant<int, i>{}, NA);
       if constexpr (i % 3 == 1 && i / 3 < LOADS_PER_STEP) issue_one(c + NSLOT, i / 3);
       __builtin_amdgcn_sched_barrier(0);
     });
   };
-  int c = 0;
-  for (; c + 1 + NSLOT < nch; c += 2) {
-    step_il(c, f0, f1);
-    step_il(c + 1, f1, f0);
-  }
-  for (; c + 1 < nch; c += 2) {
-    step(c, f0, f1);
-    step(c + 1, f1, f0);
-  }
-  if (c < nch) step(c, f0, f1);
+  auto k_loop = [&](auto NA) __attribute__((always_inline)) {
+    Frag f0, f1;
+    read(0, f0, NA);
+    int c = 0;
+    for (; c + 1 + NSLOT < nch; c += 2) {
+      step_il(c, f0, f1, NA);
+      step_il(c + 1, f1, f0, NA);
+    }
+    for (; c + 1 < nch; c += 2) {
+      step(c, f0, f1, NA);
+      step(c + 1, f1, f0, NA);
+    }
+    if (c < nch) step(c, f0, f1, NA);
+  };
+  // (the dense-only variants, the tail and the in-place add, compute every tile: only
+  // their last row tile can hold rows past M)
+  if (DUAL || ADD_PRE || n_act == 2)
+    k_loop(std::integral_constant<int, 2>{});
+  else if (n_act == 1)
+    k_loop(std::integral_constant<int, 1>{});
+  else
+    k_loop(std::integral_constant<int, 0>{});
 
   // ---- epilogue, 32 rows at a time through this wavefront's own LDS region (every
   // wavefront is past its last LDS read and every buffer-to-LDS load has landed): the
@@ -333,10 +359,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // combine weight of this lane's row, requested once for the whole epilogue
   float rw = 1.0f;
   if ((sg.epi == Epi::PAIR || sg.epi == Epi::TOKEN) && g.pair_w) rw = rp >= 0 ? g.pair_w[rp] : 0.0f;
-  // rows of the wavefront's 64 up to the last one holding a pair (dense: the last one below
-  // M); the loops below skip whole batches of rows past it
-  const uint64_t mv = __ballot(rp >= 0);
-  const int nv = mv ? 64 - __builtin_clzll(mv) : 0;
+  // rows of the wavefront's 64 up to the last one holding a pair (nv, dense: the last one
+  // below M); the loops below skip whole batches of rows past it
   const int nvq[2] = {min(nv, 32), max(nv - 32, 0)};
   const int rbase0 = row0 + 64 * rh;
   // accumulator tile (t, j) register rr: row 8 (rr / 4) + 4 (lane / 32) + rr % 4 of the
