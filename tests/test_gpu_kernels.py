@@ -391,10 +391,11 @@ def test_linear_matches_oracle(B, M, N, Kd, dt, yt):
 
 # -------------------------------------------------------------------- grouped expert GEMMs
 
-def _expert_case(B, T, E, K, L, d, tile_m, dt, seed):
+def _expert_case(B, T, E, K, L, d, tile_m, dt, seed, ids=None):
     rng = np.random.default_rng(seed)
     td = torch.bfloat16 if dt == "bf16" else torch.float32
-    ids = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    if ids is None:
+        ids = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
     w = rng.random((T, K)).astype(np.float32) + 0.1
     x = torch.from_numpy(rng.standard_normal((T, L))).to(td)
     W1 = torch.from_numpy(rng.standard_normal((E, 2 * d, L)) / math.sqrt(L)).to(td)
@@ -415,7 +416,24 @@ def _expert_case(B, T, E, K, L, d, tile_m, dt, seed):
                                                  (256, 64, 8, 2048, 128, 16, "bf16"),
                                                  (256, 128, 8, 256, 512, 16, "bf16")])
 def test_fc1_fc2_grouped_match_oracle(B, T, E, K, L, d, tile_m, dt):
-    c = _expert_case(B, T, E, K, L, d, tile_m, dt, seed=T + E)
+    _check_fc1_fc2(B, _expert_case(B, T, E, K, L, d, tile_m, dt, seed=T + E), T, E, K, L, d, tile_m, dt)
+
+
+def test_fc1_fc2_tiled_padding_quarters(B):
+    """128-row expert tiles whose last rows are padding: expert counts on both sides of
+    every 32-row boundary, so that a tile's wavefronts compute two, one or none of their
+    32-row quarters; two experts receive no pair."""
+    counts = [1, 31, 32, 33, 63, 64, 65, 95, 0, 96, 97, 127, 128, 129, 160, 200, 256, 0]
+    E, K, L, d, tile_m = len(counts), 1, 256, 128, 128
+    ids = np.repeat(np.arange(E, dtype=np.int32), counts)
+    np.random.default_rng(5).shuffle(ids)
+    T = len(ids)
+    c = _expert_case(B, T, E, K, L, d, tile_m, "bf16", seed=17, ids=ids.reshape(T, K))
+    assert np.array_equal(np.diff(c["perm"]["offsets"]), counts)
+    _check_fc1_fc2(B, c, T, E, K, L, d, tile_m, "bf16")
+
+
+def _check_fc1_fc2(B, c, T, E, K, L, d, tile_m, dt):
     ldt = B.LMOE_BF16 if dt == "bf16" else B.LMOE_F32
     rc = c["rc"]
     sentinel = -12288.0   # exact in bf16 and fp32
@@ -655,7 +673,9 @@ def test_dense_mode_shared_expert(B, dt):
     assert norm_err(f64(sh), ref) <= 1e-2
 
 
-@pytest.mark.parametrize("M,Kd,dt", [(8, 7168, "bf16"), (3, 256, "f32"), (37, 384, "bf16"), (260, 512, "bf16")])
+# M = 260, 300, 340, 480: the last 128-row tile holds 4, 44, 84 and 96 rows
+@pytest.mark.parametrize("M,Kd,dt", [(8, 7168, "bf16"), (3, 256, "f32"), (37, 384, "bf16"), (260, 512, "bf16"),
+                                     (300, 256, "bf16"), (340, 512, "bf16"), (480, 256, "bf16")])
 def test_linear_multi_matches_oracle(B, M, Kd, dt):
     rng = np.random.default_rng(M + Kd)
     td = torch.bfloat16 if dt == "bf16" else torch.float32
