@@ -13,7 +13,8 @@
 //
 // Grouped expert tiles of 16 rows (or 32 when the permutation's tile is a multiple of 32:
 // two row groups then share every weight fragment, halving weight traffic per row), one
-// wavefront per (tile, column block), NT tiles of 16 columns per wave. A pipeline step is
+// wavefront per (tile, column block) in FC1 and per (tile, two neighbouring column blocks)
+// in FC2, NT tiles of 16 columns per block. A pipeline step is
 // 256 K elements = two scaled MFMAs per row group: per lane 2 x 32 fp8 bytes of each
 // activation row (row-major) and, per weight tile, 2 x 16 bytes of packed e2m1 codes (one
 // contiguous 1 KB per wave-wide load; layout written by lmoe_pack_mxfp4_weights) plus one
@@ -26,6 +27,10 @@
 
 namespace lmoe {
 
+// column blocks an FC2 wavefront walks (measured at T = 1024, d = 512, L = 2048: FC2 +
+// combine 183 / 167 / 169 / 179 us for 1 / 2 / 4 / 8)
+constexpr int MX_FC2_BLOCKS_PER_WAVE = 2;
+
 template <int NT, int R>
 struct MxStep {
   uint4 a[R][4];     // A codes of row group r: MFMA u uses a[r][2u] (K 16g..) and a[r][2u+1] (K 64+16g..)
@@ -34,9 +39,12 @@ struct MxStep {
   uint32_t sb[NT];   // B scales of the stage: byte q = 2h + u
 };
 
-template <int NT, int R>
-__global__ __launch_bounds__(256) void stream_gemm_mx_kernel(const StreamGemm g, int blocks_total, int nsteps,
-                                                             int grouped_waves) {
+// WALK (FC2 only): each wavefront walks blocks_per_wave column blocks, storing a block's
+// products while the next block's first step loads; a kernel of its own, so that the
+// registers of the SituGLU epilogue do not count against it.
+template <int NT, int R, bool WALK>
+__device__ __forceinline__ void mx_gemm_body(const StreamGemm& g, int blocks_total, int nsteps, int grouped_waves,
+                                             int blocks_per_wave) {
   const int lane = threadIdx.x & 63;
   int mt, nb;
   if (grouped_waves) {
@@ -52,10 +60,13 @@ __global__ __launch_bounds__(256) void stream_gemm_mx_kernel(const StreamGemm g,
     nb = (lid - mt * nwb) * 4 + (int)(threadIdx.x >> 6);
     if (nb >= blocks_total) return;
   } else {
-    // one wavefront per workgroup, column blocks of a row tile consecutive
-    mt = blockIdx.x / blocks_total;
-    nb = blockIdx.x - mt * blocks_total;
+    // one wavefront per workgroup, walking blocks_per_wave consecutive column blocks of a
+    // row tile (FC2 only: the SituGLU epilogue takes one block per wavefront)
+    const int wpt = (blocks_total + blocks_per_wave - 1) / blocks_per_wave;
+    mt = blockIdx.x / wpt;
+    nb = (blockIdx.x - mt * wpt) * blocks_per_wave;
   }
+  const int nblk_w = WALK ? min(blocks_per_wave, blocks_total - nb) : 1;   // column blocks walked
   const int row0 = mt * 16 * R;   // R row groups of 16 share every weight fragment
   if (row0 >= g.M) return;
   const Seg sg = g.seg[0];
@@ -111,8 +122,13 @@ __global__ __launch_bounds__(256) void stream_gemm_mx_kernel(const StreamGemm g,
     as_off[r] = (uint32_t)arow * (uint32_t)(Kd / 32) + g4;
   }
 
+  // step t of the walk: K stage s of column block t / nsteps (nsteps is even: K is a
+  // multiple of 512)
   auto issue = [&](int t, MxStep<NT, R>& st) {
-    const int s = t >> 1, h = t & 1;
+    const int bi = t / nsteps;
+    const int tl = t - bi * nsteps;
+    const int s = tl >> 1, h = tl & 1;
+    const uint32_t nbase = (uint32_t)(bi * NT);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int q = 2 * h + u;
@@ -127,11 +143,11 @@ __global__ __launch_bounds__(256) void stream_gemm_mx_kernel(const StreamGemm g,
 #pragma unroll
       for (int j = 0; j < NT; ++j)
         st.b[j][u] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(wc_rs, lane * 16, (n16[j] * nst + s) * 4096u + q * 1024u, 0));
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(wc_rs, lane * 16, ((n16[j] + nbase) * nst + s) * 4096u + q * 1024u, 0));
     }
 #pragma unroll
     for (int j = 0; j < NT; ++j)
-      st.sb[j] = __builtin_amdgcn_raw_buffer_load_b32(ws_rs, lane * 4, (n16[j] * nst + s) * 256u, 0);
+      st.sb[j] = __builtin_amdgcn_raw_buffer_load_b32(ws_rs, lane * 4, ((n16[j] + nbase) * nst + s) * 256u, 0);
   };
 
   floatx4 acc[R][NT];
@@ -160,7 +176,58 @@ __global__ __launch_bounds__(256) void stream_gemm_mx_kernel(const StreamGemm g,
     }
   };
 
-  {
+  // ---- epilogue of column block nbc: row group r, lane holds rows row0 + 16 r + 4*g4 + i,
+  // column (tile j) ... + m
+  auto epilogue = [&](int nbc) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (!WALK && situ) {
+        const float inv_b = 1.0f / g.beta;
+        const float inv_lb = g.lbeta > 0.0f ? 1.0f / g.lbeta : 0.0f;
+        const int nblk = sg.n_out / 32;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int orow = row0 + 16 * r + 4 * g4 + i;
+          float v[half];
+          float amax = 0.0f;
+#pragma unroll
+          for (int j = 0; j < half; ++j) {
+            v[j] = situ_f(acc[r][j][i], acc[r][j + half][i], g.beta, inv_b, g.lbeta, inv_lb);
+            amax = fmaxf(amax, fabsf(v[j]));
+          }
+          // one MX block = the 32 columns of this wave (NT/2 == 2 gate tiles x 16 lanes)
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, WAVE));
+          const int X = mx_e4m3_exponent(amax);
+          if (pair_o[r][i] < 0) continue;
+          uint8_t* act = reinterpret_cast<uint8_t*>(sg.out) + (size_t)orow * sg.ldo;
+#pragma unroll
+          for (int j = 0; j < half; ++j)
+            act[nbc * half * 16 + j * 16 + m] = (uint8_t)e4m3_encode(__builtin_ldexpf(v[j], -X));
+          if (m == 0) g.out_scale[(size_t)orow * nblk + nbc] = (uint8_t)(X + 127);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int pair = pair_o[r][i];
+          if (pair < 0) continue;
+          const float wgt = pw[r][i];
+#pragma unroll
+          for (int j = 0; j < NT; ++j) {
+            const int col = nbc * NT * 16 + j * 16 + m;
+            if (sg.epi == Epi::PAIR)
+              reinterpret_cast<float*>(sg.out)[(size_t)pair * sg.ldo + col] = wgt * acc[r][j][i];
+            else if (sg.out_elt == Elt::F32)   // TOKEN (K == 1)
+              reinterpret_cast<float*>(sg.out)[(size_t)(pair / g.topk) * sg.ldo + col] = wgt * acc[r][j][i];
+            else
+              reinterpret_cast<uint16_t*>(sg.out)[(size_t)(pair / g.topk) * sg.ldo + col] = f32_to_bf16(wgt * acc[r][j][i]);
+          }
+        }
+      }
+    }
+  };
+
+  if constexpr (!WALK) {
     MxStep<NT, R> s0, s1;
     issue(0, s0);
     int t = 0;
@@ -176,55 +243,50 @@ __global__ __launch_bounds__(256) void stream_gemm_mx_kernel(const StreamGemm g,
       __builtin_amdgcn_sched_barrier(0);
       if (++t >= nsteps) break;
     }
-  }
-
-  // ---- epilogue: row group r, lane holds rows row0 + 16 r + 4*g4 + i, column (tile j) ... + m
+    epilogue(nb);
+  } else {
+    // two steps per trip (nsteps is even), so that a column block ends after the second;
+    // the next block's first step is already in flight during its epilogue
+    const int total = nblk_w * nsteps;
+    MxStep<NT, R> s0, s1;
+    issue(0, s0);
+    int t = 0, bi = 0;
+    while (true) {
+      issue(min(t + 1, total - 1), s1);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(t, s0);
+      __builtin_amdgcn_sched_barrier(0);
+      ++t;
+      issue(min(t + 1, total - 1), s0);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(t, s1);
+      __builtin_amdgcn_sched_barrier(0);
+      ++t;
+      if (t == (bi + 1) * nsteps) {
+        epilogue(nb + bi);
+        if (t >= total) break;
+        ++bi;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    if (situ) {
-      const float inv_b = 1.0f / g.beta;
-      const float inv_lb = g.lbeta > 0.0f ? 1.0f / g.lbeta : 0.0f;
-      const int nblk = sg.n_out / 32;
+        for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int orow = row0 + 16 * r + 4 * g4 + i;
-        float v[half];
-        float amax = 0.0f;
-#pragma unroll
-        for (int j = 0; j < half; ++j) {
-          v[j] = situ_f(acc[r][j][i], acc[r][j + half][i], g.beta, inv_b, g.lbeta, inv_lb);
-          amax = fmaxf(amax, fabsf(v[j]));
-        }
-        // one MX block = the 32 columns of this wave (NT/2 == 2 gate tiles x 16 lanes)
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, WAVE));
-        const int X = mx_e4m3_exponent(amax);
-        if (pair_o[r][i] < 0) continue;
-        uint8_t* act = reinterpret_cast<uint8_t*>(sg.out) + (size_t)orow * sg.ldo;
-#pragma unroll
-        for (int j = 0; j < half; ++j)
-          act[nb * half * 16 + j * 16 + m] = (uint8_t)e4m3_encode(__builtin_ldexpf(v[j], -X));
-        if (m == 0) g.out_scale[(size_t)orow * nblk + nb] = (uint8_t)(X + 127);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pair = pair_o[r][i];
-        if (pair < 0) continue;
-        const float wgt = pw[r][i];
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          const int col = nb * NT * 16 + j * 16 + m;
-          if (sg.epi == Epi::PAIR)
-            reinterpret_cast<float*>(sg.out)[(size_t)pair * sg.ldo + col] = wgt * acc[r][j][i];
-          else if (sg.out_elt == Elt::F32)   // TOKEN (K == 1)
-            reinterpret_cast<float*>(sg.out)[(size_t)(pair / g.topk) * sg.ldo + col] = wgt * acc[r][j][i];
-          else
-            reinterpret_cast<uint16_t*>(sg.out)[(size_t)(pair / g.topk) * sg.ldo + col] = f32_to_bf16(wgt * acc[r][j][i]);
-        }
+          for (int j = 0; j < NT; ++j) acc[r][j] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
     }
   }
+}
+
+template <int NT, int R>
+__global__ __launch_bounds__(256) void stream_gemm_mx_kernel(const StreamGemm g, int blocks_total, int nsteps,
+                                                             int grouped_waves) {
+  mx_gemm_body<NT, R, false>(g, blocks_total, nsteps, grouped_waves, 1);
+}
+
+// two wavefronts per SIMD asked for explicitly: left to itself the compiler gives the walk
+// more registers than that allows
+template <int NT, int R>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void stream_gemm_mx_walk_kernel(
+    const StreamGemm g, int blocks_total, int nsteps, int blocks_per_wave) {
+  mx_gemm_body<NT, R, true>(g, blocks_total, nsteps, 0, blocks_per_wave);
 }
 
 hipError_t launch_stream_gemm_mx(StreamGemm g, int live, hipStream_t stream) {
@@ -246,15 +308,26 @@ hipError_t launch_stream_gemm_mx(StreamGemm g, int live, hipStream_t stream) {
   // past the tiles returning at once. FC2 (K = d: 16 KB per tile) measured faster with one
   // wavefront per workgroup.
   const bool grouped_waves = g.seg[0].epi == Epi::SITU_MX;
+  // FC2 wavefronts walk MX_FC2_BLOCKS_PER_WAVE column blocks each, loading the next block
+  // while they store the last one's products (fewer, longer-lived waves: each one's first
+  // load latency is paid once per walk)
+  const int bpw = grouped_waves ? 1 : MX_FC2_BLOCKS_PER_WAVE;
   const unsigned grid = grouped_waves ? (unsigned)(((m_tiles + 7) / 8) * 8 * ((blocks + 3) / 4))
-                                      : (unsigned)(m_tiles * blocks);
+                                      : (unsigned)(m_tiles * ((blocks + bpw - 1) / bpw));
   const unsigned threads = grouped_waves ? 256 : 64;
-  if (R == 2)
-    hipLaunchKernelGGL((stream_gemm_mx_kernel<NT, 2>), dim3(grid), dim3(threads), 0, stream, g, blocks, nsteps,
-                       (int)grouped_waves);
-  else
-    hipLaunchKernelGGL((stream_gemm_mx_kernel<NT, 1>), dim3(grid), dim3(threads), 0, stream, g, blocks, nsteps,
-                       (int)grouped_waves);
+  if (grouped_waves) {
+    if (R == 2)
+      hipLaunchKernelGGL((stream_gemm_mx_kernel<NT, 2>), dim3(grid), dim3(threads), 0, stream, g, blocks, nsteps, 1);
+    else
+      hipLaunchKernelGGL((stream_gemm_mx_kernel<NT, 1>), dim3(grid), dim3(threads), 0, stream, g, blocks, nsteps, 1);
+  } else {
+    if (R == 2)
+      hipLaunchKernelGGL((stream_gemm_mx_walk_kernel<NT, 2>), dim3(grid), dim3(threads), 0, stream, g, blocks, nsteps,
+                         bpw);
+    else
+      hipLaunchKernelGGL((stream_gemm_mx_walk_kernel<NT, 1>), dim3(grid), dim3(threads), 0, stream, g, blocks, nsteps,
+                         bpw);
+  }
   return hipGetLastError();
 }
 

@@ -653,6 +653,40 @@ def test_fc1_fc2_mx_match_oracle(B, T, E, K, L, d, tile_m):
     assert norm_err(f64(z), oracle.f32_round(ref_z)) <= 1e-4
 
 
+# output widths of 1, 7 and 9 blocks of 64 columns: a wavefront that walks several column
+# blocks also meets a row tile's last, shorter run of blocks
+@pytest.mark.parametrize("T,E,K,d,out_dim,tile_m", [(40, 16, 8, 512, 576, 32), (24, 8, 4, 512, 448, 16),
+                                                    (30, 8, 4, 1024, 64, 32)])
+def test_fc2_mx_column_block_runs(B, T, E, K, d, out_dim, tile_m):
+    rng = np.random.default_rng(T + out_dim)
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    wts = (rng.random((T, K)) + 0.1).astype(np.float32)
+    perm = oracle.permute(ids, E, tile_m)
+    rc = B.lmoe_permute_rows_cap(T, E, K, tile_m)
+    r2p = torch.from_numpy(np.concatenate([perm["row_to_pair"], np.full(rc - len(perm["row_to_pair"]), -1)])
+                           .astype(np.int32)).to(DEV)
+    te = torch.from_numpy(tile_expert_from_offsets(perm["tile_offsets"], tile_m, rc // tile_m).astype(np.int32)).to(DEV)
+    W2c, W2s = _mx_weights(rng, E, out_dim, d)
+    p2c, p2s = B.packed_mxfp4(torch.from_numpy(W2c).to(DEV), torch.from_numpy(W2s).to(DEV))
+    aq, as_ = oracle.mxfp8_quantize(oracle.bf16_round(rng.standard_normal((rc, d))))
+    z = torch.full((T, out_dim), float("nan"), device=DEV)
+    wsb = B.lmoe_fc2_workspace_bytes(T, K, out_dim)
+    ws = torch.empty(max(wsb // 4, 1), device=DEV)
+    B.lmoe_fc2_combine(T, E, K, d, out_dim, tile_m, B.LMOE_MXFP8_E4M3, torch.from_numpy(aq).to(DEV),
+                       torch.from_numpy(as_).to(DEV), r2p, te, B.LMOE_MXFP4_E2M1, p2c, p2s,
+                       torch.from_numpy(wts).to(DEV), B.LMOE_F32, z, rc, ws, wsb)
+    torch.cuda.synchronize()
+    a_hat = oracle.mxfp8_dequant(aq, as_)
+    p2r = perm["pair_to_row"]
+    ref_z = np.zeros((T, out_dim))
+    for t in range(T):
+        for k in range(K):
+            e = ids[t, k]
+            y = oracle.linear(a_hat[p2r[t * K + k]][None, :], oracle.mxfp4_dequant(W2c[e], W2s[e]))[0]
+            ref_z[t] += wts[t, k].astype(np.float64) * y
+    assert norm_err(f64(z), oracle.f32_round(ref_z)) <= 1e-4
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_dense_mode_shared_expert(B, dt):
     rng = np.random.default_rng(4)
