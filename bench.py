@@ -77,12 +77,13 @@ def fc1_roofline(cfg, n_touched, rows, pairs, fc1_ms):
 
 
 def fc1_traffic(cfg, seed):
-    """HBM bytes per FC1 launch from the committed counter profile (FETCH_SIZE + WRITE_SIZE,
-    scaled by a plain copy of known size), for the workload it was taken on; None when
-    the workload differs or the kernel sources changed since."""
+    """HBM bytes per FC1 launch from the workload's committed counter profile
+    (profiles/fc1_<workload>_pmc.md: FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of
+    known size); None when there is none, for another seed, or when the kernel sources
+    changed since it was taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "fc1_decode_bf16_pmc.md")
-    if cfg.name != "decode_bf16" or seed != 2 or not os.path.exists(path):
+    path = os.path.join(ROOT, "profiles", f"fc1_{cfg.name}_pmc.md")
+    if seed != 2 or not os.path.exists(path):
         return None
     kv = {}
     for line in open(path):

@@ -30,6 +30,10 @@ namespace lmoe {
 // column blocks an FC2 wavefront walks (measured at T = 1024, d = 512, L = 2048: FC2 +
 // combine 183 / 167 / 169 / 179 us for 1 / 2 / 4 / 8)
 constexpr int MX_FC2_BLOCKS_PER_WAVE = 2;
+// consecutive FC1 row tiles placed on one XCD, so that an expert's two 32-row tiles read its
+// weights into one L2 (measured at T = 1024: FC1 reads 1.14 / 1.04 / 0.97 GB and takes
+// 255 / 253 / 254 us for 1 / 2 / 4)
+constexpr int MX_FC1_TILES_PER_XCD = 2;
 
 template <int NT, int R>
 struct MxStep {
@@ -50,14 +54,15 @@ __device__ __forceinline__ void mx_gemm_body(const StreamGemm& g, int blocks_tot
   if (grouped_waves) {
     // A workgroup's 4 wavefronts take 4 neighbouring column blocks of one row tile, so they
     // request the same activation rows on one CU; the workgroups of a row tile run on one
-    // XCD (workgroup b runs on XCD b % 8), consecutive row tiles on the XCDs in turn, so
-    // that each tile's activation rows cross into one L2 only and the tiles holding rows
-    // (the first ones) spread over all XCDs.
+    // XCD (workgroup b runs on XCD b % 8), runs of MX_FC1_TILES_PER_XCD consecutive row tiles
+    // on the XCDs in turn, so that each tile's activation rows and most experts' weights
+    // cross into one L2 only and the tiles holding rows (the first ones) spread over all
+    // XCDs.
     const int nwb = (blocks_total + 3) / 4;
     const int j = (int)(blockIdx.x >> 3);
-    const int lid = ((j / nwb) * 8 + (int)(blockIdx.x & 7)) * nwb + j % nwb;
-    mt = lid / nwb;
-    nb = (lid - mt * nwb) * 4 + (int)(threadIdx.x >> 6);
+    const int jt = j / nwb;                 // this XCD's jt-th row tile
+    mt = ((jt / MX_FC1_TILES_PER_XCD) * 8 + (int)(blockIdx.x & 7)) * MX_FC1_TILES_PER_XCD + jt % MX_FC1_TILES_PER_XCD;
+    nb = (j - jt * nwb) * 4 + (int)(threadIdx.x >> 6);
     if (nb >= blocks_total) return;
   } else {
     // one wavefront per workgroup, walking blocks_per_wave consecutive column blocks of a
@@ -312,7 +317,8 @@ hipError_t launch_stream_gemm_mx(StreamGemm g, int live, hipStream_t stream) {
   // while they store the last one's products (fewer, longer-lived waves: each one's first
   // load latency is paid once per walk)
   const int bpw = grouped_waves ? 1 : MX_FC2_BLOCKS_PER_WAVE;
-  const unsigned grid = grouped_waves ? (unsigned)(((m_tiles + 7) / 8) * 8 * ((blocks + 3) / 4))
+  const unsigned grid = grouped_waves ? (unsigned)(((m_tiles + 8 * MX_FC1_TILES_PER_XCD - 1) / (8 * MX_FC1_TILES_PER_XCD)) *
+                                                   8 * MX_FC1_TILES_PER_XCD * ((blocks + 3) / 4))
                                       : (unsigned)(m_tiles * ((blocks + bpw - 1) / bpw));
   const unsigned threads = grouped_waves ? 256 : 64;
   if (grouped_waves) {
