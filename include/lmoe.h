@@ -238,6 +238,24 @@ lmoe_status lmoe_fc1_situ(int T, int E, int K, int in_dim, int d, int tile_m,
                           lmoe_dtype act_dtype, void* act, uint8_t* act_scale,
                           int rows_cap, hipStream_t stream);
 
+/* lmoe_fc1_situ with a bound on the launch's width, for a call that runs on a second
+ * stream beside latency-bound work on the first ([P2] "Commit 2": the shared experts on
+ * their own stream, overlapping the router and the routed experts). The weight-streaming
+ * launch (bf16 / fp32 below 256 tokens) then aims for about max_waves wavefronts instead
+ * of 2048 (rounded to its shape: column blocks x K splits), so it takes a smaller share of
+ * the HBM bandwidth and finishes later; max_waves == 0 keeps the default, and the tiled
+ * and MX launches ignore it. Arguments and checks are those of lmoe_fc1_situ; so are the
+ * results, except that with fewer wavefronts K is split over fewer partial sums, so the
+ * fp32 accumulation adds in another order (same error bound; bit for bit only when
+ * max_waves == 0). max_waves < 0 gives LMOE_ERR_INVALID_ARG. */
+lmoe_status lmoe_fc1_situ_capped(int T, int E, int K, int in_dim, int d, int tile_m,
+                                 lmoe_dtype a_dtype, const void* a, const uint8_t* a_scale,
+                                 const int32_t* row_to_pair, const int32_t* tile_expert,
+                                 lmoe_dtype w_dtype, const void* w1, const uint8_t* w1_scale,
+                                 float beta, float linear_beta,
+                                 lmoe_dtype act_dtype, void* act, uint8_t* act_scale,
+                                 int rows_cap, int max_waves, hipStream_t stream);
+
 /* Grouped FC2 with the weighted combine ([P2] "Commit 1": finalize reads the
  * routing workspace; [P3] enable_quantized_routed_input: router weights are applied
  * after the experts, not on their input).

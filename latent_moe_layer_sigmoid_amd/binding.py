@@ -48,6 +48,8 @@ SIGNATURES = [
     ("lmoe_quant_mxfp8", _i, [_i, _i, _i, _p, _p, _p, _p]),
     ("lmoe_fc1_situ", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _i, _p, _p, _f, _f, _i, _p, _p, _i,
                            _p]),
+    ("lmoe_fc1_situ_capped", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _i, _p, _p, _f, _f, _i, _p, _p,
+                                  _i, _i, _p]),
     ("lmoe_fc2_workspace_bytes", _z, [_i, _i, _i]),
     ("lmoe_fc2_combine", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _i, _p, _p, _p, _i, _p, _i, _p,
                               _z, _p]),
@@ -232,6 +234,15 @@ def lmoe_fc1_situ(T, E, K, in_dim, d, tile_m, a_dtype, a, a_scale, row_to_pair, 
                                                 _ptr(row_to_pair), _ptr(tile_expert), w_dtype, _ptr(w1),
                                                 _ptr(w1_scale), float(beta), float(linear_beta), act_dtype,
                                                 _ptr(act), _ptr(act_scale), rows_cap, _stream(stream)))
+
+
+def lmoe_fc1_situ_capped(T, E, K, in_dim, d, tile_m, a_dtype, a, a_scale, row_to_pair, tile_expert, w_dtype, w1,
+                         w1_scale, beta, linear_beta, act_dtype, act, act_scale, rows_cap, max_waves, stream=None):
+    _check("lmoe_fc1_situ_capped",
+           lib().lmoe_fc1_situ_capped(T, E, K, in_dim, d, tile_m, a_dtype, _ptr(a), _ptr(a_scale), _ptr(row_to_pair),
+                                      _ptr(tile_expert), w_dtype, _ptr(w1), _ptr(w1_scale), float(beta),
+                                      float(linear_beta), act_dtype, _ptr(act), _ptr(act_scale), rows_cap,
+                                      max_waves, _stream(stream)))
 
 
 def lmoe_fc2_workspace_bytes(T, K, out_dim):

@@ -455,7 +455,8 @@ static void launch_nt(bool dual, int nbw, dim3 grid, dim3 block, size_t lds, hip
 constexpr long kTargetWaves = 2048;
 
 template <Elt ELT>
-static hipError_t launch_elt(StreamGemm g, int live, hipStream_t stream) {
+static hipError_t launch_elt(StreamGemm g, int live, hipStream_t stream, long target_waves) {
+  const long tw = target_waves > 0 ? target_waves : kTargetWaves;
   using TR = EltTraits<ELT>;
   if (!g.row_to_pair) g.weights_once = g.M <= 16;   // dense: one row tile reads every weight
   const bool dual = g.nseg == 1 && g.seg[0].epi == Epi::ADD2;
@@ -465,9 +466,10 @@ static hipError_t launch_elt(StreamGemm g, int live, hipStream_t stream) {
   if (live < 1) live = 1;
   // Columns per wave: NT tiles of 16 (a SituGLU segment pairs NT/2 gate tiles with their
   // up tiles; a segment's last block may be partial). Take the largest NT that still gives
-  // kTargetWaves live waves, else the smallest allowed; then split K over up to 8 waves of
-  // a workgroup to reach that count. With more live waves than the target (one segment, one
-  // phase), a wave takes several consecutive column blocks instead.
+  // tw live waves (kTargetWaves unless the caller asks for another count), else the
+  // smallest allowed; then split K over up to 8 waves of a workgroup to reach that count.
+  // With more live waves than the target (one segment, one phase), a wave takes several
+  // consecutive column blocks instead.
   bool any_situ = false;
   for (int i = 0; i < g.nseg; ++i) any_situ |= g.seg[i].epi == Epi::SITU;
   auto blocks_of = [&](int i, int NT) {
@@ -482,19 +484,19 @@ static hipError_t launch_elt(StreamGemm g, int live, hipStream_t stream) {
     for (int i = 0; i < g.nseg; ++i) t += blocks_of(i, cand);
     NT = cand;
     blocks_total = t;
-    if ((long)live * t >= kTargetWaves) break;
+    if ((long)live * t >= tw) break;
   }
   for (int i = 0, b0 = 0; i < g.nseg; ++i) {
     g.seg[i].blocks = blocks_of(i, NT);
     g.seg[i].block0 = b0;
     b0 += g.seg[i].blocks;
   }
-  int splits = (int)((kTargetWaves + (long)live * blocks_total - 1) / ((long)live * blocks_total));
+  int splits = (int)((tw + (long)live * blocks_total - 1) / ((long)live * blocks_total));
   splits = splits < 1 ? 1 : (splits > 8 ? 8 : splits);
   if (splits > nch0 + nch1) splits = nch0 + nch1;
   int nbw = 1;
   if (splits == 1 && !dual && g.nseg == 1) {
-    nbw = (int)((long)live * blocks_total / kTargetWaves);
+    nbw = (int)((long)live * blocks_total / tw);
     nbw = nbw < 1 ? 1 : (nbw > blocks_total ? blocks_total : nbw);
   }
   const int groups_total = (blocks_total + nbw - 1) / nbw;
@@ -508,9 +510,9 @@ static hipError_t launch_elt(StreamGemm g, int live, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_stream_gemm(StreamGemm g, Elt elt, int live_tiles, hipStream_t stream) {
-  return elt == Elt::BF16 ? launch_elt<Elt::BF16>(g, live_tiles, stream)
-                          : launch_elt<Elt::F32>(g, live_tiles, stream);
+hipError_t launch_stream_gemm(StreamGemm g, Elt elt, int live_tiles, hipStream_t stream, long target_waves) {
+  return elt == Elt::BF16 ? launch_elt<Elt::BF16>(g, live_tiles, stream, target_waves)
+                          : launch_elt<Elt::F32>(g, live_tiles, stream, target_waves);
 }
 
 }  // namespace lmoe

@@ -8,8 +8,9 @@
 
 namespace lmoe {
 
-// live_tiles: expected number of 16-row tiles that hold rows (sizes the split-K factor).
-hipError_t launch_stream_gemm(StreamGemm g, Elt elt, int live_tiles, hipStream_t stream);
+// live_tiles: expected number of 16-row tiles that hold rows (sizes the split-K factor);
+// target_waves: wavefronts the launch aims for (0: the default of 2048).
+hipError_t launch_stream_gemm(StreamGemm g, Elt elt, int live_tiles, hipStream_t stream, long target_waves = 0);
 // LDS-tiled bf16 GEMM: 128-row tiles (dense rows, or grouped tiles with tile_m == 128); Kd % 128 == 0.
 hipError_t launch_tiled_gemm(StreamGemm g, hipStream_t stream);
 bool tiled_dual_ok(const StreamGemm& g);

@@ -28,8 +28,9 @@ long rows_bound(long pairs, int E, int tile_m) {
 // weights over 16-row tiles.
 bool use_tiled_dense(long M, lmoe_dtype t) { return t == LMOE_BF16 && M >= 256; }
 bool use_tiled_grouped(int tile_m, lmoe_dtype t) { return t == LMOE_BF16 && tile_m == 128; }
-hipError_t run_gemm(const StreamGemm& g, lmoe_dtype t, bool tiled, int live, hipStream_t stream) {
-  return tiled ? launch_tiled_gemm(g, stream) : launch_stream_gemm(g, elt_of(t), live, stream);
+hipError_t run_gemm(const StreamGemm& g, lmoe_dtype t, bool tiled, int live, hipStream_t stream,
+                    long target_waves = 0) {
+  return tiled ? launch_tiled_gemm(g, stream) : launch_stream_gemm(g, elt_of(t), live, stream, target_waves);
 }
 // expected 16-row tiles holding rows: pairs / 16 plus one partial tile per touched expert
 int live_tiles(long pairs, int E) {
@@ -284,10 +285,12 @@ static lmoe_status check_grouped(int T, int E, int K, int tile_m, const int32_t*
   return LMOE_OK;
 }
 
-lmoe_status lmoe_fc1_situ(int T, int E, int K, int in_dim, int d, int tile_m, lmoe_dtype a_dtype, const void* a,
-                          const uint8_t* a_scale, const int32_t* row_to_pair, const int32_t* tile_expert,
-                          lmoe_dtype w_dtype, const void* w1, const uint8_t* w1_scale, float beta, float linear_beta,
-                          lmoe_dtype act_dtype, void* act, uint8_t* act_scale, int rows_cap, hipStream_t stream) {
+static lmoe_status fc1_situ_impl(int T, int E, int K, int in_dim, int d, int tile_m, lmoe_dtype a_dtype,
+                                 const void* a, const uint8_t* a_scale, const int32_t* row_to_pair,
+                                 const int32_t* tile_expert, lmoe_dtype w_dtype, const void* w1,
+                                 const uint8_t* w1_scale, float beta, float linear_beta, lmoe_dtype act_dtype,
+                                 void* act, uint8_t* act_scale, int rows_cap, long target_waves,
+                                 hipStream_t stream) {
   bool dense = false;
   lmoe_status st = check_grouped(T, E, K, tile_m, row_to_pair, tile_expert, rows_cap, &dense);
   if (st != LMOE_OK) return st;
@@ -345,7 +348,25 @@ lmoe_status lmoe_fc1_situ(int T, int E, int K, int in_dim, int d, int tile_m, lm
   g.seg[0] = Seg{w1, 2 * d, d, Epi::SITU, elt_of(act_dtype), act, d, 0, 0};
   const int live = dense ? (T + 15) / 16 : live_tiles((long)T * K, E);
   const bool tiled = dense ? use_tiled_dense(T, a_dtype) : use_tiled_grouped(tile_m, a_dtype);
-  return hip_status(run_gemm(g, a_dtype, tiled, live, stream));
+  return hip_status(run_gemm(g, a_dtype, tiled, live, stream, target_waves));
+}
+
+lmoe_status lmoe_fc1_situ(int T, int E, int K, int in_dim, int d, int tile_m, lmoe_dtype a_dtype, const void* a,
+                          const uint8_t* a_scale, const int32_t* row_to_pair, const int32_t* tile_expert,
+                          lmoe_dtype w_dtype, const void* w1, const uint8_t* w1_scale, float beta, float linear_beta,
+                          lmoe_dtype act_dtype, void* act, uint8_t* act_scale, int rows_cap, hipStream_t stream) {
+  return fc1_situ_impl(T, E, K, in_dim, d, tile_m, a_dtype, a, a_scale, row_to_pair, tile_expert, w_dtype, w1,
+                       w1_scale, beta, linear_beta, act_dtype, act, act_scale, rows_cap, 0, stream);
+}
+
+lmoe_status lmoe_fc1_situ_capped(int T, int E, int K, int in_dim, int d, int tile_m, lmoe_dtype a_dtype,
+                                 const void* a, const uint8_t* a_scale, const int32_t* row_to_pair,
+                                 const int32_t* tile_expert, lmoe_dtype w_dtype, const void* w1,
+                                 const uint8_t* w1_scale, float beta, float linear_beta, lmoe_dtype act_dtype,
+                                 void* act, uint8_t* act_scale, int rows_cap, int max_waves, hipStream_t stream) {
+  if (max_waves < 0) return LMOE_ERR_INVALID_ARG;
+  return fc1_situ_impl(T, E, K, in_dim, d, tile_m, a_dtype, a, a_scale, row_to_pair, tile_expert, w_dtype, w1,
+                       w1_scale, beta, linear_beta, act_dtype, act, act_scale, rows_cap, max_waves, stream);
 }
 
 size_t lmoe_fc2_workspace_bytes(int T, int K, int out_dim) {

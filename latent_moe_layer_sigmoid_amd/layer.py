@@ -50,7 +50,7 @@ class LatentMoELayer:
     device (lmoe_pack_weights) when the layer is built."""
 
     def __init__(self, shape: LayerShape, weights: dict, device="cuda", fused=True, shared_stream=False,
-                 router_stream=False, fold_shared_fc2=None):
+                 router_stream=False, fold_shared_fc2=None, side_waves=512):
         B.lib()   # fail loudly now if the library is missing
         self.s = shape
         # fused: the hidden-input projections share one launch (lmoe_linear_multi) and the
@@ -60,7 +60,9 @@ class LatentMoELayer:
         # shared_stream: the shared expert runs on a second stream, concurrently with the
         # router GEMM, routing, permutation and the routed experts, and the tail waits for
         # it (TensorRT-LLM PR 20541, "Commit 2": shared experts on their own stream, joined
-        # by an event before the routed reduction). Same kernels, same results.
+        # by an event before the routed reduction). Same kernels; the side stream's narrower
+        # shared FC1 (side_waves) sums K in another order, so the shared output can differ
+        # from the one-stream schedule's in the last bf16 bit.
         self.shared_stream = shared_stream or router_stream
         # router_stream: additionally, the router GEMM, routing and permutation run on a
         # router stream while the main stream computes the latent down projection
@@ -70,6 +72,11 @@ class LatentMoELayer:
         # and the tail computes the shared FC2 and the up projection in one call
         # (lmoe_tail_shared); None: fold when the token count takes the tiled GEMMs
         self.fold_shared_fc2 = fold_shared_fc2
+        # side_waves: wavefronts the side stream's shared FC1 aims for when it streams its
+        # weights (lmoe_fc1_situ_capped; 0: the library default of 2048). A narrower launch
+        # leaves more of the HBM bandwidth to the main stream's router GEMM and experts,
+        # while the shared expert still finishes before the tail needs it.
+        self.side_waves = side_waves
         self.device = torch.device(device)
         # extra streams at the default priority
         self._side = torch.cuda.Stream(self.device) if self.shared_stream else None
@@ -288,8 +295,8 @@ class LatentMoELayer:
         if not torch.cuda.is_current_stream_capturing():
             X.record_stream(side)
         fold = self.folds_shared_fc2(T)
-        B.lmoe_fc1_situ(T, 1, 1, s.H, s.I, 16, dt, X, None, None, None, dt, w["W_s1"], None, s.beta,
-                        s.linear_beta, dt, b["act_s"], None, T, side)
+        B.lmoe_fc1_situ_capped(T, 1, 1, s.H, s.I, 16, dt, X, None, None, None, dt, w["W_s1"], None, s.beta,
+                               s.linear_beta, dt, b["act_s"], None, T, self.side_waves, side)
         if not fold:
             B.lmoe_fc2_combine(T, 1, 1, s.I, s.H, 16, dt, b["act_s"], None, None, None, dt, w["W_s2"], None, None,
                                dt, b["sh"], T, None, 0, side)

@@ -81,6 +81,13 @@ def test_invalid_calls_are_rejected_without_a_gpu(B):
                            B.LMOE_F32, P, None, cap, None) == B.LMOE_ERR_INVALID_ARG
     assert L.lmoe_fc1_situ(4, 16, 4, 100, 64, 16, B.LMOE_BF16, P, None, P, P, B.LMOE_BF16, P, None, 1.0, 0.0,
                            B.LMOE_BF16, P, None, cap, None) == B.LMOE_ERR_UNSUPPORTED
+    # fc1 with a wave bound: the same checks, and the bound must not be negative
+    assert L.lmoe_fc1_situ_capped(4, 16, 4, 128, 64, 16, B.LMOE_F32, P, None, P, P, B.LMOE_F32, P, None, 0.0, 0.0,
+                                  B.LMOE_F32, P, None, cap, 512, None) == B.LMOE_ERR_INVALID_ARG
+    assert L.lmoe_fc1_situ_capped(4, 1, 1, 128, 64, 16, B.LMOE_F32, P, None, None, None, B.LMOE_F32, P, None, 1.0,
+                                  0.0, B.LMOE_F32, P, None, 4, -1, None) == B.LMOE_ERR_INVALID_ARG
+    assert L.lmoe_fc1_situ_capped(0, 1, 1, 128, 64, 16, B.LMOE_F32, None, None, None, None, B.LMOE_F32, None, None,
+                                  1.0, 0.0, B.LMOE_F32, None, None, 0, 512, None) == B.LMOE_OK   # T == 0
     # fc1 dense mode needs E == K == 1
     assert L.lmoe_fc1_situ(4, 2, 1, 128, 64, 16, B.LMOE_F32, P, None, None, None, B.LMOE_F32, P, None, 1.0, 0.0,
                            B.LMOE_F32, P, None, 4, None) == B.LMOE_ERR_INVALID_ARG

@@ -687,6 +687,53 @@ def test_fc2_mx_column_block_runs(B, T, E, K, d, out_dim, tile_m):
     assert norm_err(f64(z), oracle.f32_round(ref_z)) <= 1e-4
 
 
+@pytest.mark.parametrize("max_waves", [0, 512, 100, 64])
+def test_fc1_situ_capped_matches_fc1_situ(B, max_waves):
+    """The width-bounded FC1 against the oracle and against lmoe_fc1_situ: the shared
+    expert's decode shape in dense mode, and a grouped decode-sized call. With fewer
+    wavefronts K is split over fewer partial sums (another fp32 summation order), so the
+    two calls agree bit for bit only at max_waves == 0."""
+    rng = np.random.default_rng(7 + max_waves)
+    T, H, I = 8, 7168, 4096
+    X = torch.from_numpy(rng.standard_normal((T, H))).to(torch.bfloat16).to(DEV)
+    Ws = torch.from_numpy(rng.standard_normal((2 * I, H)) / math.sqrt(H)).to(torch.bfloat16)
+    W = B.packed(Ws.to(DEV))
+    ref = torch.full((T, I), float("nan"), dtype=torch.bfloat16, device=DEV)
+    got = torch.full_like(ref, float("nan"))
+    B.lmoe_fc1_situ(T, 1, 1, H, I, 16, B.LMOE_BF16, X, None, None, None, B.LMOE_BF16, W, None, 1.0, 0.5,
+                    B.LMOE_BF16, ref, None, T)
+    B.lmoe_fc1_situ_capped(T, 1, 1, H, I, 16, B.LMOE_BF16, X, None, None, None, B.LMOE_BF16, W, None, 1.0, 0.5,
+                           B.LMOE_BF16, got, None, T, max_waves)
+    torch.cuda.synchronize()
+    assert not torch.isnan(got.float()).any()
+    ref64 = oracle.round_to(oracle.situ_glu_rows(oracle.linear(f64(X.cpu()), f64(Ws)), 1.0, 0.5),
+                            "bf16")
+    assert norm_err(f64(got), ref64) <= 1e-2
+    if max_waves == 0:
+        assert torch.equal(got, ref)
+    else:
+        assert norm_err(f64(got), f64(ref)) <= 1e-2      # one bf16 ulp is up to 2^-7 of the max
+    # grouped: 8 tokens, 64 experts, top-16, tile 16
+    c = _expert_case(B, 8, 64, 16, 2048, 512, 16, "bf16", seed=3)
+    W1 = B.packed(c["W1"].to(DEV))
+    acts = []
+    for capped in (False, True):
+        act = torch.full((c["rc"], 512), -12288.0, dtype=torch.bfloat16, device=DEV)
+        args = (8, 64, 16, 2048, 512, 16, B.LMOE_BF16, c["x"].to(DEV), None, c["r2p"], c["te"], B.LMOE_BF16, W1,
+                None, 1.0, 0.5, B.LMOE_BF16, act, None, c["rc"])
+        if capped:
+            B.lmoe_fc1_situ_capped(*args, max_waves)
+        else:
+            B.lmoe_fc1_situ(*args)
+        acts.append(act)
+    torch.cuda.synchronize()
+    valid = torch.from_numpy(c["perm"]["row_to_pair"] >= 0)
+    n = len(valid)
+    a0, a1 = f64(acts[0][:n][valid.to(DEV)]), f64(acts[1][:n][valid.to(DEV)])
+    assert norm_err(a1, a0) <= 1e-2
+    assert torch.equal(acts[0][:n][~valid.to(DEV)], acts[1][:n][~valid.to(DEV)])   # pad rows untouched
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_dense_mode_shared_expert(B, dt):
     rng = np.random.default_rng(4)
