@@ -687,7 +687,7 @@ def test_fc2_mx_column_block_runs(B, T, E, K, d, out_dim, tile_m):
     assert norm_err(f64(z), oracle.f32_round(ref_z)) <= 1e-4
 
 
-@pytest.mark.parametrize("max_waves", [0, 512, 100, 64])
+@pytest.mark.parametrize("max_waves", [0, 512, 256, 100, 64])
 def test_fc1_situ_capped_matches_fc1_situ(B, max_waves):
     """The width-bounded FC1 against the oracle and against lmoe_fc1_situ: the shared
     expert's decode shape in dense mode, and a grouped decode-sized call. With fewer
