@@ -1,0 +1,61 @@
+"""Host logic of bench.py (no GPU): the algorithmic bytes and flops behind its roofline
+object, and the lookup of the committed FC1 traffic counters (profiles/fc1_<workload>_pmc.md),
+which must be withdrawn as soon as a kernel source they were taken on changes."""
+import os
+import shutil
+
+import bench
+import lmoe_inputs as LI
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_fc1_bytes_decode_and_mx_shapes():
+    dec = LI.CONFIGS["decode_bf16"]
+    # 114 touched experts: W1 (2d x L, bf16) once each, the 8 latent rows, 114 tiles of 16
+    # activation rows written
+    assert bench.fc1_bytes(dec, 114, 114 * 16) == 114 * 1024 * 2048 * 2 + 8 * 2048 * 2 + 1824 * 512 * 2
+    assert bench.fc1_bytes(dec, 114, 114 * 16) == 480051200
+    mx = LI.CONFIGS["mx_experts"]
+    # MXFP4: half a byte per weight + one e8m0 byte per 32; MXFP8 rows: one byte per element
+    # + one per 32 (764 touched experts, 990 tiles of 32 rows)
+    want = 764 * 1024 * 2048 * 17 // 32 + 1024 * 2048 * 33 // 32 + 31680 * 512 * 33 // 32
+    assert bench.fc1_bytes(mx, 764, 31680) == want == 870071296
+
+
+def test_fc1_roofline_bound_by_workload():
+    pf = LI.CONFIGS["prefill_bf16"]
+    r = bench.fc1_roofline(pf, 692, 188288, 131072, 1.0)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s"
+    assert r["algorithmic_flops"] == 2 * 131072 * 1024 * 2048      # pairs, not padded rows
+    assert abs(r["achieved"] - 2 * 131072 * 1024 * 2048 / 1e-3 / 1e12) < 0.1
+    dec = LI.CONFIGS["decode_bf16"]
+    r = bench.fc1_roofline(dec, 114, 1824, 128, 0.08)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
+    assert abs(r["achieved"] - 480051200 / 0.08e-3 / 1e9) < 0.1
+    assert abs(r["frac"] - r["achieved"] / 8000.0) < 1e-4
+
+
+def test_fc1_traffic_reads_each_committed_profile():
+    for name in ("decode_bf16", "prefill_bf16", "mx_experts"):
+        cfg = LI.CONFIGS[name]
+        v = bench.fc1_traffic(cfg, 2)
+        assert isinstance(v, int) and v > 0, name
+        with open(os.path.join(ROOT, "profiles", f"fc1_{name}_pmc.md")) as f:
+            assert f"traffic_bytes_per_launch: {v}\n" in f.read()
+        assert bench.fc1_traffic(cfg, 3) is None      # counters were taken at seed 2 only
+
+
+def test_fc1_traffic_is_withdrawn_when_a_kernel_source_changes(tmp_path, monkeypatch):
+    prof = os.path.join("profiles", "fc1_decode_bf16_pmc.md")
+    with open(os.path.join(ROOT, prof)) as f:
+        srcs = next(l for l in f if l.startswith("kernel_sources:")).split(":", 1)[1].split()
+    for rel in [prof] + srcs:
+        os.makedirs(tmp_path / os.path.dirname(rel), exist_ok=True)
+        shutil.copy(os.path.join(ROOT, rel), tmp_path / rel)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    cfg = LI.CONFIGS["decode_bf16"]
+    assert bench.fc1_traffic(cfg, 2) is not None
+    with open(tmp_path / srcs[0], "a") as f:
+        f.write("\n// edited\n")
+    assert bench.fc1_traffic(cfg, 2) is None
