@@ -456,7 +456,12 @@ constexpr long kTargetWaves = 2048;
 
 template <Elt ELT>
 static hipError_t launch_elt(StreamGemm g, int live, hipStream_t stream, long target_waves) {
-  const long tw = target_waves > 0 ? target_waves : kTargetWaves;
+  // Decode-sized grouped FC2 (per-pair products, every weight row met by one row tile):
+  // K = d is short, so half as many waves, each walking twice as many column blocks, pay
+  // the start-up of a wave over more bytes (T = 8, d = 512, L = 2048: FC2 + combine 59.4 ->
+  // 57.8 us; 3072 or 4096 waves slower).
+  const bool short_k_pairs = g.row_to_pair && g.weights_once && g.nseg == 1 && g.seg[0].epi == Epi::PAIR;
+  const long tw = target_waves > 0 ? target_waves : (short_k_pairs ? kTargetWaves / 2 : kTargetWaves);
   using TR = EltTraits<ELT>;
   if (!g.row_to_pair) g.weights_once = g.M <= 16;   // dense: one row tile reads every weight
   const bool dual = g.nseg == 1 && g.seg[0].epi == Epi::ADD2;
