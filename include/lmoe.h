@@ -168,8 +168,8 @@ lmoe_status lmoe_route_renormalize(int T, int E, int K, const float* logits, int
                                    float* topk_weights, hipStream_t stream);
 
 /* Stable expert-sorted permutation of the T*K (token, slot) pairs, pair p = t*K + k
- * ([P2] "Commit 1": the routing workspace that FC1 / FC2 / finalize read, computed for
- * the tile the runner reports). Outputs (all int32, caller-allocated):
+ * (the per-expert row map that the expert GEMMs and the
+ * weighted combine consume, padded to the expert GEMM's row tile; [P2] "Commit 1"). Outputs (all int32, caller-allocated):
  *   expert_counts[E]       pairs routed to each expert;
  *   expert_offsets[E+1]    exclusive prefix sum of the counts;
  *   tile_offsets[E+1]      exclusive prefix sum of counts rounded up to tile_m;
@@ -189,8 +189,8 @@ lmoe_status lmoe_permute(int T, int E, int K, int tile_m, const int32_t* topk_id
 
 /* Routing followed by the permutation, in one launch for decode-sized batches
  * (T <= 16 and T*K <= 1024: one workgroup routes each token with one wavefront, keeps the
- * ids on chip and builds the permutation from them; [P2] "Commit 1": routing writes the
- * workspace that FC1 / FC2 / finalize read). Larger batches run lmoe_route then
+ * ids on chip and builds the permutation from them; [P2] "Commit 1": the routing op
+ * produces the row map the expert GEMMs use). Larger batches run lmoe_route then
  * lmoe_permute. Arguments, outputs, checks and error codes are exactly those of the two
  * calls (topk_ids and topk_weights are written as by lmoe_route; workspace as for
  * lmoe_permute); results are identical to the two calls made in sequence. */
@@ -256,8 +256,8 @@ lmoe_status lmoe_fc1_situ_capped(int T, int E, int K, int in_dim, int d, int til
                                  lmoe_dtype act_dtype, void* act, uint8_t* act_scale,
                                  int rows_cap, int max_waves, hipStream_t stream);
 
-/* Grouped FC2 with the weighted combine ([P2] "Commit 1": finalize reads the
- * routing workspace; [P3] enable_quantized_routed_input: router weights are applied
+/* Grouped FC2 with the weighted combine ([P2] "Commit 1": the combine uses the
+ * routing row map; [P3] enable_quantized_routed_input: router weights are applied
  * after the experts, not on their input).
  *   y_r = act[r, :] @ w2[e]^T (w2 [E, out_dim, d]) for every valid row r, then
  *   out[t, :] = sum_{k=0..K-1} topk_weights[t, k] * y_{pair_to_row(t*K+k)}   (k ascending),

@@ -1,6 +1,6 @@
-// Stable expert-sorted permutation of the (token, slot) pairs for gfx950 (TensorRT-LLM
-// PR 20541, "Commit 1: routing as its own op": the routing workspace that FC1 / FC2 /
-// finalize read, computed for the runner's tile).
+// Stable expert-sorted permutation of the (token, slot) pairs for gfx950: the per-expert
+// row map that the expert GEMMs and the weighted combine consume, padded to the GEMM's row
+// tile (TensorRT-LLM PR 20541, "Commit 1: routing as its own op").
 //
 // Pairs p = t*K + k are cut into blocks of 1024. Counts are order-free (LDS atomics);
 // ranks inside an expert must follow pair order, so each block ranks its pairs with
@@ -8,14 +8,15 @@
 // (one ballot per bit), the rank inside the wave is the popcount of matching lower
 // lanes, and the per-wave counts in LDS give the offset of each earlier wave.
 //   1 block  : one fused kernel (count, scan, rank, scatter).
-//   >1 blocks: count per block (and -1 into every row of row_to_pair) -> one-block scan of
-//              the expert totals -> per block: its base in each expert (the counts of the
-//              blocks before it), rank + scatter.
+//   >1 blocks: count per block (and -1 into every row of row_to_pair) -> one-block scan:
+//              per expert, each block's exclusive prefix over the blocks (in place) and the
+//              totals, then the expert scan -> per block: its base in each expert, rank +
+//              scatter.
 // Threads of a workgroup share data through LDS only, so its barriers order LDS alone (the
 // global outputs are read by later launches).
 // Decode-sized batches (T <= 16 tokens, T*K <= 1024 pairs) can also run routing and the
 // permutation as one workgroup: wavefront t routes token t (TensorRT-LLM PR 20541,
-// "Commit 1": the routing kernel writes the workspace FC1 / FC2 read), the ids stay in LDS
+// "Commit 1": routing produces the expert GEMMs' row map), the ids stay in LDS
 // and the single-block permutation follows after a barrier.
 #include "common.h"
 #include "kernels.h"
@@ -43,29 +44,35 @@ LMOE_DEV int lanes_below(uint64_t m, int lane) {
 
 // Inclusive sum of x over the lanes of the wavefront (lane i gets lanes 0..i): row shifts
 // 1, 2, 4, 8 scan each row of 16 lanes (lanes shifted in from outside the row read 0), then
-// row broadcasts of lanes 15 and 31 add the earlier rows' totals.
-LMOE_DEV int wave_inclusive_sum(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);    // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);    // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);    // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);    // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15 -> rows 1, 3
-  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31 -> rows 2, 3
+// row broadcasts of lanes 15 and 31 add the earlier rows' totals. The sums wrap modulo 2^32
+// (unsigned), so a packed pair of 16-bit sums may carry into bit 31.
+template <int CTRL, int ROW_MASK, bool BOUND_CTRL>
+LMOE_DEV uint32_t dpp_add(uint32_t x) {
+  return x + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xF, BOUND_CTRL);
+}
+LMOE_DEV uint32_t wave_inclusive_sum(uint32_t x) {
+  x = dpp_add<0x111, 0xF, true>(x);    // row_shr:1
+  x = dpp_add<0x112, 0xF, true>(x);    // row_shr:2
+  x = dpp_add<0x114, 0xF, true>(x);    // row_shr:4
+  x = dpp_add<0x118, 0xF, true>(x);    // row_shr:8
+  x = dpp_add<0x142, 0xA, false>(x);   // row_bcast:15 -> rows 1, 3
+  x = dpp_add<0x143, 0xC, false>(x);   // row_bcast:31 -> rows 2, 3
   return x;
 }
 
-// Block-wide exclusive scan of v over PB threads; returns the prefix and sets *total.
-LMOE_DEV int block_exclusive_scan(int v, int* s_wave, int* total) {
+// Block-wide exclusive scan of v over PB threads (modulo 2^32); returns the prefix and sets
+// *total.
+LMOE_DEV uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int x = wave_inclusive_sum(v);
+  const uint32_t x = wave_inclusive_sum(v);
   if (lane == 63) s_wave[w] = x;
   lds_sync();
   if (w == 0) {
-    const int s = wave_inclusive_sum(lane < PW ? s_wave[lane] : 0);
+    const uint32_t s = wave_inclusive_sum(lane < PW ? s_wave[lane] : 0u);
     if (lane < PW) s_wave[PW + lane] = s;   // inclusive per-wave totals
   }
   lds_sync();
-  const int before = (w ? s_wave[PW + w - 1] : 0) + x - v;
+  const uint32_t before = (w ? s_wave[PW + w - 1] : 0u) + x - v;
   *total = s_wave[2 * PW - 1];
   lds_sync();
   return before;
@@ -89,16 +96,22 @@ LMOE_DEV void scan_experts(const int* s_cnt, int E, int tile_m, int max_tiles, i
     p_sum += (c + tmask) & ~tmask;
   }
   int c_tot, p_tot, c_pre, p_pre;
+  uint32_t* s_u = reinterpret_cast<uint32_t*>(s_scratch);
   if ((long)max_tiles * tile_m < 65536) {
-    int tot;
-    const int pre = block_exclusive_scan((p_sum << 16) | c_sum, s_scratch, &tot);
-    c_pre = pre & 0xFFFF;
-    p_pre = pre >> 16;
-    c_tot = tot & 0xFFFF;
-    p_tot = tot >> 16;
+    // both sums stay below 2^16: the padded-row sum in the high half (it may reach bit 31,
+    // so the word is decoded unsigned), the pair sum in the low half
+    uint32_t tot;
+    const uint32_t pre = block_exclusive_scan(((uint32_t)p_sum << 16) | (uint32_t)c_sum, s_u, &tot);
+    c_pre = (int)(pre & 0xFFFFu);
+    p_pre = (int)(pre >> 16);
+    c_tot = (int)(tot & 0xFFFFu);
+    p_tot = (int)(tot >> 16);
   } else {
-    c_pre = block_exclusive_scan(c_sum, s_scratch, &c_tot);
-    p_pre = block_exclusive_scan(p_sum, s_scratch, &p_tot);
+    uint32_t ct, pt;
+    c_pre = (int)block_exclusive_scan((uint32_t)c_sum, s_u, &ct);
+    p_pre = (int)block_exclusive_scan((uint32_t)p_sum, s_u, &pt);
+    c_tot = (int)ct;
+    p_tot = (int)pt;
   }
   for (int e = e0; e < e1; ++e) {
     const int c = s_cnt[e];
@@ -253,44 +266,46 @@ __global__ __launch_bounds__(PB) void permute_count_kernel(int npairs, int E, co
   for (int e = threadIdx.x; e < E; e += PB) block_counts[(size_t)blockIdx.x * E + e] = s_cnt[e];
 }
 
-// Sum over blocks [0, nb) of expert e's block counts; 32 counts requested together.
-LMOE_DEV int sum_block_counts(const int32_t* __restrict__ block_counts, int E, int e, int nb) {
-  int run = 0;
-  for (int b0 = 0; b0 < nb; b0 += 32) {
-    int c[32];
-#pragma unroll
-    for (int j = 0; j < 32; ++j) c[j] = b0 + j < nb ? block_counts[(size_t)(b0 + j) * E + e] : 0;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) run += c[j];
-  }
-  return run;
-}
-
-// One block: the expert totals (sums over blocks), then the expert scan (the pad rows are
-// already -1).
+// One block: for each expert, the running sum over the blocks of its block counts,
+// written back in place as each block's exclusive prefix (the pairs of that expert in the
+// blocks before it; 32 counts requested together), the total kept in LDS; then the expert
+// scan (the pad rows are already -1).
 __global__ __launch_bounds__(PB) void permute_scan_kernel(int nblk, int E, int tile_m, int max_tiles,
-                                                          const int32_t* __restrict__ block_counts, int32_t* counts,
+                                                          int32_t* __restrict__ block_counts, int32_t* counts,
                                                           int32_t* offsets, int32_t* tile_offsets,
                                                           int32_t* row_to_pair, int32_t* tile_expert) {
   extern __shared__ int smem[];
   int* s_cnt = smem;          // [E]
   int* s_scr = s_cnt + E;     // [2 * PW]
-  for (int e = threadIdx.x; e < E; e += PB) s_cnt[e] = sum_block_counts(block_counts, E, e, nblk);
+  for (int e = threadIdx.x; e < E; e += PB) {
+    int run = 0;
+    for (int b0 = 0; b0 < nblk; b0 += 32) {
+      int c[32];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) c[j] = b0 + j < nblk ? block_counts[(size_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        if (b0 + j < nblk) block_counts[(size_t)(b0 + j) * E + e] = run;
+        run += c[j];
+      }
+    }
+    s_cnt[e] = run;
+  }
   lds_sync();
   scan_experts(s_cnt, E, tile_m, max_tiles, counts, offsets, tile_offsets, row_to_pair, tile_expert,
                s_scr, nullptr, false);
 }
 
+// block_counts holds, per block and expert, the pairs of that expert in earlier blocks.
 __global__ __launch_bounds__(PB) void permute_scatter_kernel(int npairs, int E, const int32_t* __restrict__ ids,
-                                                             const int32_t* __restrict__ block_counts,
+                                                             const int32_t* __restrict__ block_before,
                                                              const int32_t* __restrict__ tile_offsets,
                                                              int32_t* row_to_pair, int32_t* pair_to_row) {
   extern __shared__ int s_base[];                                           // [E]
   unsigned short* s_wcnt = reinterpret_cast<unsigned short*>(s_base + E);   // [PW * E]
-  // first row of this block's pairs in each expert: the expert's first row plus the pairs
-  // of the blocks before this one
+  // first row of this block's pairs in each expert
   for (int e = threadIdx.x; e < E; e += PB)
-    s_base[e] = tile_offsets[e] + sum_block_counts(block_counts, E, e, blockIdx.x);
+    s_base[e] = tile_offsets[e] + block_before[(size_t)blockIdx.x * E + e];
   lds_sync();
   rank_scatter(ids, npairs, E, id_bits(E), blockIdx.x * PB, s_wcnt, [&](int e) { return s_base[e]; },
                row_to_pair, pair_to_row);

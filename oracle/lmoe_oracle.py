@@ -285,8 +285,8 @@ def route_renormalize(logits, K):
 
 
 def permute(ids, E, tile_m):
-    """Expert-sorted permutation of the (token, slot) pairs ([P2] "Commit 1": the
-    routing workspace that FC1 / FC2 / finalize read, computed for the runner's tile).
+    """Expert-sorted permutation of the (token, slot) pairs (the per-expert row map
+    the expert GEMMs and the combine consume, padded to a row tile; [P2] "Commit 1").
 
     Pair p = t*K + k. Pairs are stably sorted by expert id (token order inside each
     expert). Each expert's segment is padded to a multiple of tile_m rows.

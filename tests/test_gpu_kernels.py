@@ -186,7 +186,12 @@ def _run_permute(B, ids, E, tile_m):
 @pytest.mark.parametrize("T,E,K,tile_m,skew", [(4, 16, 4, 16, 0), (8, 896, 16, 16, 0), (64, 896, 16, 16, 1.0),
                                                (65, 100, 16, 32, 0), (1024, 896, 16, 16, 0.7),
                                                (3000, 512, 8, 128, 1.5), (8192, 896, 16, 128, 1.0),
-                                               (777, 1024, 64, 256, 0.3), (1, 1, 1, 16, 0)])
+                                               (777, 1024, 64, 256, 0.3), (1, 1, 1, 16, 0),
+                                               # padded row totals past 32767 while the row capacity
+                                               # stays below 65536 (one packed 16 + 16-bit scan):
+                                               # several blocks, and the single-block kernel
+                                               (2048, 896, 16, 16, 0), (3000, 896, 16, 16, 0.3),
+                                               (64, 896, 16, 64, 0)])
 def test_permute_matches_oracle(B, T, E, K, tile_m, skew):
     rng = np.random.default_rng(T * 7 + E)
     ids = _random_ids(T, E, K, rng, skew)
@@ -204,7 +209,8 @@ def test_permute_matches_oracle(B, T, E, K, tile_m, skew):
 
 
 @pytest.mark.parametrize("T,E,K,tile_m", [(4, 16, 4, 16), (8, 896, 16, 16), (16, 896, 16, 16), (17, 896, 16, 16),
-                                           (1, 8, 8, 16), (8, 1024, 64, 32), (64, 256, 16, 128), (300, 896, 16, 128)])
+                                           (1, 8, 8, 16), (8, 1024, 64, 32), (64, 256, 16, 128), (300, 896, 16, 128),
+                                           (16, 896, 16, 128), (2048, 896, 16, 16)])
 def test_route_permute_matches_oracle(B, T, E, K, tile_m):
     """One call = routing then permutation: fused into one workgroup for T <= 16 and
     T*K <= 1024, two kernels otherwise; both bit-exact against the oracle."""
