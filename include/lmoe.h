@@ -187,6 +187,24 @@ lmoe_status lmoe_permute(int T, int E, int K, int tile_m, const int32_t* topk_id
                          int32_t* row_to_pair, int32_t* tile_expert, int32_t* pair_to_row,
                          int rows_cap, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* lmoe_permute for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same arguments,
+ * checks and results as lmoe_permute, minus the workspace. The per-block counts of
+ * batches above 1024 pairs go to a fixed scratch array inside the library, one copy per
+ * GPU, of lmoe_permute_noalloc_max_bytes() bytes (1 MiB), held until the process ends;
+ * a call needing more than that (ceil(T*K / 1024) * E * 4 bytes, i.e. above about 292k
+ * pairs at E = 896) returns LMOE_ERR_WORKSPACE and enqueues nothing. The call allocates
+ * nothing; its first call on a device looks up that device's scratch address once.
+ * `stream` must belong to the current device (else LMOE_ERR_INVALID_ARG). Every call on
+ * one GPU shares that GPU's scratch: calls that may overlap in time on one GPU (on
+ * different streams, or from several host threads) race and must be serialized by the
+ * caller. The scratch needs no clearing: each call writes every count it reads. */
+size_t lmoe_permute_noalloc_max_bytes(void);
+lmoe_status lmoe_permute_noalloc(int T, int E, int K, int tile_m, const int32_t* topk_ids,
+                                 int32_t* expert_counts, int32_t* expert_offsets, int32_t* tile_offsets,
+                                 int32_t* row_to_pair, int32_t* tile_expert, int32_t* pair_to_row,
+                                 int rows_cap, hipStream_t stream);
+
 /* Routing followed by the permutation, in one launch for decode-sized batches
  * (T <= 16 and T*K <= 1024: one workgroup routes each token with one wavefront, keeps the
  * ids on chip and builds the permutation from them; [P2] "Commit 1": the routing op

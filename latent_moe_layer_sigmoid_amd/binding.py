@@ -44,6 +44,8 @@ SIGNATURES = [
     ("lmoe_permute_workspace_bytes", _z, [_i, _i, _i]),
     ("lmoe_permute_rows_cap", _i, [_i, _i, _i, _i]),
     ("lmoe_permute", _i, [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _i, _p, _z, _p]),
+    ("lmoe_permute_noalloc_max_bytes", _z, []),
+    ("lmoe_permute_noalloc", _i, [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _i, _p]),
     ("lmoe_route_permute", _i, [_i, _i, _i, _p, _p, _f, _i, _p, _p, _i, _p, _p, _p, _p, _p, _p, _i, _p, _z, _p]),
     ("lmoe_quant_mxfp8", _i, [_i, _i, _i, _p, _p, _p, _p]),
     ("lmoe_fc1_situ", _i, [_i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _i, _p, _p, _f, _f, _i, _p, _p, _i,
@@ -212,6 +214,18 @@ def lmoe_permute(T, E, K, tile_m, topk_ids, expert_counts, expert_offsets, tile_
                                               _ptr(expert_offsets), _ptr(tile_offsets), _ptr(row_to_pair),
                                               _ptr(tile_expert), _ptr(pair_to_row), rows_cap, _ptr(workspace),
                                               int(workspace_bytes), _stream(stream)))
+
+
+def lmoe_permute_noalloc_max_bytes():
+    return int(lib().lmoe_permute_noalloc_max_bytes())
+
+
+def lmoe_permute_noalloc(T, E, K, tile_m, topk_ids, expert_counts, expert_offsets, tile_offsets, row_to_pair,
+                         tile_expert, pair_to_row, rows_cap, stream=None):
+    _check("lmoe_permute_noalloc", lib().lmoe_permute_noalloc(T, E, K, tile_m, _ptr(topk_ids), _ptr(expert_counts),
+                                                              _ptr(expert_offsets), _ptr(tile_offsets),
+                                                              _ptr(row_to_pair), _ptr(tile_expert), _ptr(pair_to_row),
+                                                              rows_cap, _stream(stream)))
 
 
 def lmoe_route_permute(T, E, K, logits, bias, routed_scaling_factor, renormalize, topk_ids, topk_weights, tile_m,

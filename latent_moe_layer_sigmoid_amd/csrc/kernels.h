@@ -25,6 +25,10 @@ hipError_t launch_route(int T, int E, int K, const float* logits, const float* b
                         int32_t* ids, float* weights, hipStream_t stream);
 
 size_t permute_workspace_bytes(int npairs, int E);
+// Device scratch of the permutation when the caller brings no workspace: this device's
+// copy of a fixed array of PERMUTE_SCRATCH_BYTES (looked up once per device).
+constexpr size_t PERMUTE_SCRATCH_BYTES = size_t(1) << 20;
+hipError_t permute_scratch(void** ptr);
 hipError_t launch_permute(int npairs, int E, int tile_m, int max_tiles, const int32_t* ids, int32_t* counts,
                           int32_t* offsets, int32_t* tile_offsets, int32_t* row_to_pair, int32_t* tile_expert,
                           int32_t* pair_to_row, void* workspace, hipStream_t stream);

@@ -239,6 +239,36 @@ lmoe_status lmoe_permute(int T, int E, int K, int tile_m, const int32_t* topk_id
                                    stream));
 }
 
+size_t lmoe_permute_noalloc_max_bytes(void) { return PERMUTE_SCRATCH_BYTES; }
+
+lmoe_status lmoe_permute_noalloc(int T, int E, int K, int tile_m, const int32_t* topk_ids, int32_t* expert_counts,
+                                 int32_t* expert_offsets, int32_t* tile_offsets, int32_t* row_to_pair,
+                                 int32_t* tile_expert, int32_t* pair_to_row, int rows_cap, hipStream_t stream) {
+  if (T < 0 || E < 1 || K < 1 || K > E || K > 64 || !tile_ok(tile_m)) return LMOE_ERR_INVALID_ARG;
+  if (E > 1024) return LMOE_ERR_UNSUPPORTED;
+  if ((long)T * K > 0x3FFFFFFFL) return LMOE_ERR_UNSUPPORTED;
+  if (T == 0) return LMOE_OK;
+  if (!topk_ids || !expert_counts || !expert_offsets || !tile_offsets || !row_to_pair || !tile_expert ||
+      !pair_to_row)
+    return LMOE_ERR_INVALID_ARG;
+  const long npairs = (long)T * K;
+  if (rows_cap < rows_bound(npairs, E, tile_m) || rows_cap % tile_m != 0) return LMOE_ERR_WORKSPACE;
+  if (permute_workspace_bytes((int)npairs, E) > PERMUTE_SCRATCH_BYTES) return LMOE_ERR_WORKSPACE;
+  // the scratch address is the current device's: the stream must belong to that device
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return LMOE_ERR_HIP;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return LMOE_ERR_HIP;
+    if ((int)sdev != cur) return LMOE_ERR_INVALID_ARG;
+  }
+  void* scratch_ptr = nullptr;
+  if (permute_scratch(&scratch_ptr) != hipSuccess) return LMOE_ERR_HIP;
+  return hip_status(launch_permute((int)npairs, E, tile_m, rows_cap / tile_m, topk_ids, expert_counts,
+                                   expert_offsets, tile_offsets, row_to_pair, tile_expert, pair_to_row, scratch_ptr,
+                                   stream));
+}
+
 lmoe_status lmoe_route_permute(int T, int E, int K, const float* logits, const float* bias, float rsf,
                                int renormalize, int32_t* topk_ids, float* topk_weights, int tile_m,
                                int32_t* expert_counts, int32_t* expert_offsets, int32_t* tile_offsets,

@@ -18,6 +18,8 @@
 // permutation as one workgroup: wavefront t routes token t (TensorRT-LLM PR 20541,
 // "Commit 1": routing produces the expert GEMMs' row map), the ids stay in LDS
 // and the single-block permutation follows after a barrier.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 #include "route_dev.h"
@@ -335,6 +337,36 @@ hipError_t launch_permute(int npairs, int E, int tile_m, int max_tiles, const in
                      (size_t)E * sizeof(int) + (size_t)PW * E * sizeof(unsigned short), stream, npairs, E, ids,
                      block_counts, tile_offsets, row_to_pair, pair_to_row);
   return hipGetLastError();
+}
+
+// ---- permutation without a caller workspace ------------------------------------------------
+// The per-block expert counts of the multi-block path live in a fixed device array of this
+// library (one copy per GPU, held until the process ends). Its name is only a host-side
+// stand-in for the device address, so the address each device gives it is looked up once
+// per device and kept.
+static __device__ __align__(256) int32_t scratch[PERMUTE_SCRATCH_BYTES / sizeof(int32_t)];
+
+namespace {
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t permute_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // with `dev` current
+    if (err != hipSuccess) return err;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace lmoe
