@@ -94,6 +94,18 @@ class LatentMoELayer:
                 self.w[k] = v
         torch.cuda.synchronize(self.device)
 
+    def reshaped(self, **changes):
+        """A layer over the same packed device weights with some LayerShape fields changed
+        (e.g. tile_m for another batch size regime), its own buffers and streams."""
+        import copy
+        import dataclasses
+        other = copy.copy(self)
+        other.s = dataclasses.replace(self.s, **changes)
+        other._bufs = {}
+        other._side = torch.cuda.Stream(self.device) if self.shared_stream else None
+        other._router = torch.cuda.Stream(self.device) if self.router_stream else None
+        return other
+
     def buffers(self, T):
         if T in self._bufs:
             return self._bufs[T]

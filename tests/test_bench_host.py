@@ -59,3 +59,35 @@ def test_fc1_traffic_is_withdrawn_when_a_kernel_source_changes(tmp_path, monkeyp
     with open(tmp_path / srcs[0], "a") as f:
         f.write("\n// edited\n")
     assert bench.fc1_traffic(cfg, 2) is None
+
+
+def test_expert_floor_and_layer_flops():
+    pf = LI.CONFIGS["prefill_bf16"]
+    # a heavy expert (4000 rows) is MFMA-bound, a light one (3 rows) HBM-bound; the floor
+    # takes the larger of the two times per expert and sums over the experts
+    c = 4000
+    flops = 2.0 * c * 1024 * 2048
+    nbytes = 1024 * 2048 * 2 + c * 2048 * 2 + c * 512 * 2
+    want = max(flops / 2.5e15, nbytes / 8e12) * 1e3
+    assert abs(bench.fc1_expert_floor_ms(pf, [c]) - want) < 1e-12
+    light = 3
+    want_light = max(2.0 * light * 1024 * 2048 / 2.5e15, (1024 * 2048 * 2 + light * 2560 * 2) / 8e12) * 1e3
+    assert abs(bench.fc1_expert_floor_ms(pf, [c, 0, light]) - (want + want_light)) < 1e-12
+    r = bench.fc1_roofline(pf, 2, 4224, c + light, 1.0, [c, 0, light])
+    assert abs(r["expert_floor_frac"] - (want + want_light)) < 1e-4
+    # dense projections over all tokens plus the routed FC1 + FC2 over the pairs
+    dense = 2 * 8192 * (896 * 7168 + 2048 * 7168 + 3 * 7168 * 4096 + 7168 * 2048)
+    assert bench.layer_flops(pf) == dense + 2 * 8192 * 16 * 3 * 2048 * 512
+
+
+def test_percentiles_nearest_rank():
+    p = bench.percentiles([5.0, 1.0, 4.0, 2.0, 3.0] * 2 + [100.0])
+    assert p["median"] == 3.0 and p["p10"] == 1.0 and p["p90"] == 5.0
+
+
+def test_bench_refuses_several_gpus():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=60)
+    assert r.returncode == 2 and "one GPU" in r.stderr
