@@ -341,13 +341,14 @@ def layer_record(torch, cfg, layer, Xs, steps, flush, seed):
     }
 
 
-def make_layer(torch, LI, cfg, seed, schedule):
+def make_layer(torch, LI, cfg, seed, schedule, fold="auto"):
     from latent_moe_layer_sigmoid_amd import LatentMoELayer, LayerShape
     w = LI.make_layer_weights(cfg, seed, device="cuda")
     shape = LayerShape(H=cfg.H, L=cfg.L, E=cfg.E, K=cfg.K, d=cfg.d, I=cfg.I, dtype=cfg.dtype, experts=cfg.experts,
                        beta=cfg.beta, linear_beta=cfg.linear_beta, rsf=cfg.rsf, eps=cfg.eps, tile_m=cfg.tile_m)
     layer = LatentMoELayer(shape, w, shared_stream=schedule == "shared_stream",
-                           router_stream=schedule == "router_stream")
+                           router_stream=schedule == "router_stream",
+                           fold_shared_fc2={"auto": None, "on": True, "off": False}[fold])
     del w
     torch.cuda.empty_cache()
     return layer
@@ -438,6 +439,9 @@ def main():
                          "layer, as the reference kernel for HBM byte counters")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph of the layer step instead of eager launches")
+    ap.add_argument("--fold-shared-fc2", choices=["auto", "on", "off"], default="auto",
+                    help="with a second stream: compute the shared FC2 inside the tail (on), on the side stream "
+                         "(off), or by token count (auto: folded from 256 tokens)")
     ap.add_argument("--schedule", choices=["one_stream", "shared_stream", "router_stream"], default="shared_stream",
                     help="shared_stream: the shared expert runs on a second stream; router_stream: also the "
                          "router GEMM and routing on a third")
@@ -457,7 +461,7 @@ def main():
     B.lib()
     cfg = LI.CONFIGS[args.workload]
     log(f"workload {cfg.name}: generating weights on the GPU")
-    layer = make_layer(torch, LI, cfg, args.seed, args.schedule)
+    layer = make_layer(torch, LI, cfg, args.seed, args.schedule, args.fold_shared_fc2)
     X_cpu = LI.make_x(cfg, args.seed)
     X = X_cpu.to("cuda")
 

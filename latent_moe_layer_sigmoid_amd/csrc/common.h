@@ -19,26 +19,64 @@ constexpr int WAVE = 64;
 
 LMOE_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// float -> bfloat16, round to nearest even (NaN stays NaN).
-LMOE_DEV uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// float -> bfloat16, round to nearest even (NaN stays NaN): the gfx950 conversion
+// instruction (v_cvt_pk_bf16_f32), which rounds in the default nearest-even mode.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+LMOE_DEV uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// two floats -> two bfloat16 in one 32-bit word (lo in the low half), one instruction
+LMOE_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){lo, hi}, bf16x2_t));
 }
 
 // Hardware transcendental building blocks (v_exp_f32 / v_rcp_f32).
 LMOE_DEV float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 LMOE_DEV float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 LMOE_DEV float fast_sigmoid(float x) { return fast_rcp(1.0f + fast_exp(-x)); }
-// tanh(x) = 1 - 2 / (exp(2x) + 1); saturates cleanly to +-1 when exp over/underflows.
-LMOE_DEV float fast_tanh(float x) { return 1.0f - 2.0f * fast_rcp(fast_exp(2.0f * x) + 1.0f); }
+// tanh(x). For |x| >= 0.3: 1 - 2 / (exp(2x) + 1), which saturates cleanly to +-1 when
+// exp overflows or underflows. Below 0.3 that form loses relative accuracy as |x| -> 0
+// (1 minus a quotient near 1), so the odd Taylor series is used there up to x^9: the
+// first omitted term, 1382 x^11 / 155925, is below 6e-8 of tanh(x) at |x| = 0.3.
+LMOE_DEV float fast_tanh(float x) {
+  const float big = 1.0f - 2.0f * fast_rcp(fast_exp(2.0f * x) + 1.0f);
+  const float x2 = x * x;
+  float p = 62.0f / 2835.0f;
+  p = __builtin_fmaf(p, x2, -17.0f / 315.0f);
+  p = __builtin_fmaf(p, x2, 2.0f / 15.0f);
+  p = __builtin_fmaf(p, x2, -1.0f / 3.0f);
+  const float small = __builtin_fmaf(p * x2, x, x);
+  return __builtin_fabsf(x) < 0.3f ? small : big;
+}
+
+// exp(x) - 1: the Taylor series to x^7 for |x| < 0.3 (first omitted term below 2e-9 of
+// the result), e^x - 1 otherwise.
+LMOE_DEV float fast_expm1(float x, float ex) {
+  float p = 1.0f + x * (1.0f / 7.0f);
+  p = 1.0f + x * (1.0f / 6.0f) * p;
+  p = 1.0f + x * (1.0f / 5.0f) * p;
+  p = 1.0f + x * (1.0f / 4.0f) * p;
+  p = 1.0f + x * (1.0f / 3.0f) * p;
+  p = 1.0f + x * 0.5f * p;
+  return __builtin_fabsf(x) < 0.3f ? x * p : ex - 1.0f;
+}
 
 // SituGLU of one (gate, up) pair in fp32: beta*tanh(g/beta)*sigmoid(g) times
 // (linear_beta > 0 ? linear_beta*tanh(u/linear_beta) : u).
+// With beta = 1 the gate needs one exponential: with E = e^g,
+// tanh(g) * sigmoid(g) = (E^2 - 1) / (E^2 + 1) * E / (E + 1) = E (E - 1) / (E^2 + 1),
+// where E - 1 comes from fast_expm1 (accurate near g = 0); g is clamped to [-87, 40]
+// (beyond it the product is 1 to fp32 precision above and e^g to fp32 range below).
 LMOE_DEV float situ_f(float g, float u, float beta, float inv_beta, float lbeta, float inv_lbeta) {
-  float gate = beta * fast_tanh(g * inv_beta) * fast_sigmoid(g);
-  float up = lbeta > 0.0f ? lbeta * fast_tanh(u * inv_lbeta) : u;
+  float gate;
+  if (beta == 1.0f) {
+    const float gc = __builtin_fminf(__builtin_fmaxf(g, -87.0f), 40.0f);
+    const float ex = fast_exp(gc);
+    const float em1 = fast_expm1(gc, ex);
+    gate = em1 * ex * fast_rcp(__builtin_fmaf(ex, ex, 1.0f));
+  } else {
+    gate = beta * fast_tanh(g * inv_beta) * fast_sigmoid(g);
+  }
+  const float up = lbeta > 0.0f ? lbeta * fast_tanh(u * inv_lbeta) : u;
   return gate * up;
 }
 

@@ -1,6 +1,8 @@
 // Bandwidth-bound kernels of the layer for gfx950: masked SituGLU, MXFP8 quantization,
 // the fixed-order combine of per-pair expert outputs and the latent RMSNorm.
 // All use 16-byte (or wider) coalesced accesses; no MFMA (nothing here is a contraction).
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -8,65 +10,187 @@ namespace lmoe {
 
 // ---- masked SituGLU over [E, T_max, 2d] (vLLM PR 50088, commit 2: masked_situ_and_mul
 // reads expert_num_tokens and leaves padded rows untouched; fp32 math).
-// Thread = 8 consecutive outputs of one row; grid.y = expert.
+// The valid rows of all experts (v_e = min(count_e, T_max) each) are one list of
+// R = sum v_e rows, dealt evenly to a fixed grid: every workgroup scans the E counts in
+// LDS, then wavefront g of the grid takes list rows g, g + G, g + 2G, ... (G wavefronts in
+// all), MASK_ROWS rows per trip: it finds each row's expert by a binary search of the
+// scanned counts, issues the loads of all of them, then computes and stores. A few
+// heavily loaded experts thus do not leave one workgroup with most of the work, and no
+// workgroup is launched for rows that do not exist.
+constexpr int MASK_ROWS = 4;
+constexpr int MASK_MAX_E = 4096;       // experts held in LDS (larger E: one workgroup per expert row chunk)
+
 template <Elt ELT>
-__global__ __launch_bounds__(256) void situ_masked_kernel(int T_max, int d, const void* __restrict__ in,
-                                                          const int32_t* __restrict__ counts, float beta,
-                                                          float lbeta, void* __restrict__ out) {
-  const int e = blockIdx.y;
-  int v = counts[e];
-  v = v < 0 ? 0 : (v > T_max ? T_max : v);
-  const int vpr = d >> 3;   // vectors per row
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= v * vpr) return;
-  const int r = idx / vpr, c = idx - r * vpr;
-  const size_t in_row = ((size_t)e * T_max + r) * (size_t)(2 * d);
-  const size_t out_row = ((size_t)e * T_max + r) * (size_t)d;
-  const float inv_b = 1.0f / beta, inv_lb = lbeta > 0.0f ? 1.0f / lbeta : 0.0f;
-  float g[8], u[8], o[8];
+struct MaskVec {   // one vector: 8 gate and 8 up values as loaded
+  uint4 g[ELT == Elt::BF16 ? 1 : 2], u[ELT == Elt::BF16 ? 1 : 2];
+};
+
+template <Elt ELT>
+LMOE_DEV void mask_load(const void* in, size_t idx, uint4* v) {
   if (ELT == Elt::BF16) {
-    const uint16_t* p = reinterpret_cast<const uint16_t*>(in);
-    const uint4 gv = *reinterpret_cast<const uint4*>(p + in_row + c * 8);
-    const uint4 uv = *reinterpret_cast<const uint4*>(p + in_row + d + c * 8);
-    const uint16_t* gs = reinterpret_cast<const uint16_t*>(&gv);
-    const uint16_t* us = reinterpret_cast<const uint16_t*>(&uv);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      g[i] = bf16_to_f32(gs[i]);
-      u[i] = bf16_to_f32(us[i]);
-    }
+    v[0] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(in) + idx);
   } else {
-    const float* p = reinterpret_cast<const float*>(in);
-    const float4* gp = reinterpret_cast<const float4*>(p + in_row + c * 8);
-    const float4* up = reinterpret_cast<const float4*>(p + in_row + d + c * 8);
-    const float4 g0 = gp[0], g1 = gp[1], u0 = up[0], u1 = up[1];
-    g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w; g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
-    u[0] = u0.x; u[1] = u0.y; u[2] = u0.z; u[3] = u0.w; u[4] = u1.x; u[5] = u1.y; u[6] = u1.z; u[7] = u1.w;
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(in) + idx);
+    v[0] = p[0];
+    v[1] = p[1];
   }
+}
+
+template <Elt ELT>
+LMOE_DEV void mask_compute_store(const MaskVec<ELT>& q, void* out, size_t oidx, float beta, float inv_b, float lbeta,
+                                 float inv_lb) {
+  float g[8], u[8];
+#pragma unroll
+  for (int h = 0; h < (ELT == Elt::BF16 ? 1 : 2); ++h) {
+    const uint32_t gw[4] = {q.g[h].x, q.g[h].y, q.g[h].z, q.g[h].w};
+    const uint32_t uw[4] = {q.u[h].x, q.u[h].y, q.u[h].z, q.u[h].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (ELT == Elt::BF16) {
+        g[2 * i] = __uint_as_float(gw[i] << 16);
+        g[2 * i + 1] = __uint_as_float(gw[i] & 0xFFFF0000u);
+        u[2 * i] = __uint_as_float(uw[i] << 16);
+        u[2 * i + 1] = __uint_as_float(uw[i] & 0xFFFF0000u);
+      } else {
+        g[4 * h + i] = __uint_as_float(gw[i]);
+        u[4 * h + i] = __uint_as_float(uw[i]);
+      }
+    }
+  }
+  float o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = situ_f(g[i], u[i], beta, inv_b, lbeta, inv_lb);
   if (ELT == Elt::BF16) {
     uint4 ov;
-    uint16_t* os = reinterpret_cast<uint16_t*>(&ov);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) os[i] = f32_to_bf16(o[i]);
-    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + out_row + c * 8) = ov;
+    ov.x = pack_bf16x2(o[0], o[1]);
+    ov.y = pack_bf16x2(o[2], o[3]);
+    ov.z = pack_bf16x2(o[4], o[5]);
+    ov.w = pack_bf16x2(o[6], o[7]);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + oidx) = ov;
   } else {
-    float4* op = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + out_row + c * 8);
+    float4* op = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + oidx);
     op[0] = make_float4(o[0], o[1], o[2], o[3]);
     op[1] = make_float4(o[4], o[5], o[6], o[7]);
   }
 }
 
+template <Elt ELT>
+__global__ __launch_bounds__(256) void situ_masked_kernel(int E, int T_max, int d, const void* __restrict__ in,
+                                                          const int32_t* __restrict__ counts, float beta,
+                                                          float lbeta, void* __restrict__ out) {
+  __shared__ int s_off[MASK_MAX_E + 1];   // exclusive prefix of the clamped counts
+  __shared__ int s_tot[4];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // clamped counts and their exclusive scan (chunks of 256 experts, running total)
+  int run = 0;
+  for (int e0 = 0; e0 < E; e0 += 256) {
+    const int e = e0 + (int)threadIdx.x;
+    int v = e < E ? counts[e] : 0;
+    v = v < 0 ? 0 : (v > T_max ? T_max : v);
+    int x = v;   // inclusive scan within the wave (shift by 1, 2, ... 32 lanes)
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off, WAVE);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) s_tot[w] = x;
+    lds_sync();
+    int before = run;
+    for (int i = 0; i < w; ++i) before += s_tot[i];
+    if (e < E) s_off[e] = before + x - v;
+    run += s_tot[0] + s_tot[1] + s_tot[2] + s_tot[3];
+    lds_sync();
+  }
+  if (threadIdx.x == 0) s_off[E] = run;
+  lds_sync();
+  const int R = s_off[E];
+  const float inv_b = 1.0f / beta, inv_lb = lbeta > 0.0f ? 1.0f / lbeta : 0.0f;
+  const int G = (int)gridDim.x * 4;                      // wavefronts in the grid
+  const int vpr = d >> 3;                                // vectors per row
+  // expert of list row r: the last e with s_off[e] <= r (wave-uniform search)
+  auto expert_of = [&](int r) {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[mid] <= r) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+  for (int r0 = (int)blockIdx.x * 4 + w; r0 < R; r0 += G * MASK_ROWS) {
+    size_t irow[MASK_ROWS], orow[MASK_ROWS];
+    bool live[MASK_ROWS];
+#pragma unroll
+    for (int k = 0; k < MASK_ROWS; ++k) {
+      const int r = r0 + k * G;
+      live[k] = r < R;
+      const int e = live[k] ? expert_of(r) : 0;
+      const size_t row = (size_t)e * T_max + (size_t)(r - s_off[e]);
+      irow[k] = row * (size_t)(2 * d);
+      orow[k] = row * (size_t)d;
+    }
+    for (int c0 = 0; c0 < vpr; c0 += 64) {
+      // every load is issued unconditionally (rows past the list and lanes past the row
+      // read the trip's first row and the row's last vector instead), so that no branch
+      // separates them and all are in flight together; only the stores are masked
+      const int c = c0 + lane;
+      const size_t cl = (size_t)min(c, vpr - 1) * 8;
+      MaskVec<ELT> q[MASK_ROWS];
+#pragma unroll
+      for (int k = 0; k < MASK_ROWS; ++k) {
+        const size_t ir = live[k] ? irow[k] : irow[0];
+        mask_load<ELT>(in, ir + cl, q[k].g);
+        mask_load<ELT>(in, ir + d + cl, q[k].u);
+      }
+#pragma unroll
+      for (int k = 0; k < MASK_ROWS; ++k)
+        if (live[k] && c < vpr) mask_compute_store<ELT>(q[k], out, orow[k] + (size_t)c * 8, beta, inv_b, lbeta, inv_lb);
+    }
+  }
+}
+
+// E above MASK_MAX_E: one workgroup per (expert, 16-row chunk), 8 outputs per thread.
+template <Elt ELT>
+__global__ __launch_bounds__(256) void situ_masked_chunk_kernel(int T_max, int d, const void* __restrict__ in,
+                                                                const int32_t* __restrict__ counts, float beta,
+                                                                float lbeta, void* __restrict__ out) {
+  const int e = blockIdx.y;
+  int v = counts[e];
+  v = v < 0 ? 0 : (v > T_max ? T_max : v);
+  const int vpr = d >> 3;
+  const float inv_b = 1.0f / beta, inv_lb = lbeta > 0.0f ? 1.0f / lbeta : 0.0f;
+  const int r_end = min(v, (int)(blockIdx.x + 1) * 16);
+  for (int idx = (int)blockIdx.x * 16 * vpr + (int)threadIdx.x; idx < r_end * vpr; idx += 256) {
+    const int r = idx / vpr, c = idx - r * vpr;
+    const size_t row = (size_t)e * T_max + r;
+    MaskVec<ELT> q;
+    mask_load<ELT>(in, row * (size_t)(2 * d) + (size_t)c * 8, q.g);
+    mask_load<ELT>(in, row * (size_t)(2 * d) + d + (size_t)c * 8, q.u);
+    mask_compute_store<ELT>(q, out, row * (size_t)d + (size_t)c * 8, beta, inv_b, lbeta, inv_lb);
+  }
+}
+
 hipError_t launch_situ_masked(int E, int T_max, int d, Elt elt, const void* in, const int32_t* counts,
                               float beta, float lbeta, void* out, hipStream_t stream) {
-  const long vecs = (long)T_max * (d / 8);
-  const dim3 grid((unsigned)((vecs + 255) / 256), (unsigned)E), block(256);
+  if (E > MASK_MAX_E) {
+    const dim3 grid((unsigned)((T_max + 15) / 16), (unsigned)E);
+    if (elt == Elt::BF16)
+      hipLaunchKernelGGL(situ_masked_chunk_kernel<Elt::BF16>, grid, dim3(256), 0, stream, T_max, d, in, counts, beta,
+                         lbeta, out);
+    else
+      hipLaunchKernelGGL(situ_masked_chunk_kernel<Elt::F32>, grid, dim3(256), 0, stream, T_max, d, in, counts, beta,
+                         lbeta, out);
+    return hipGetLastError();
+  }
+  // enough wavefronts for about MASK_ROWS rows each when every row is valid, at most 1024
+  // workgroups (four per CU)
+  const long rows = (long)E * T_max;
+  const unsigned grid = (unsigned)std::max(1L, std::min(1024L, (rows + 4 * MASK_ROWS - 1) / (4 * MASK_ROWS)));
   if (elt == Elt::BF16)
-    hipLaunchKernelGGL(situ_masked_kernel<Elt::BF16>, grid, block, 0, stream, T_max, d, in, counts, beta, lbeta,
-                       out);
+    hipLaunchKernelGGL(situ_masked_kernel<Elt::BF16>, dim3(grid), dim3(256), 0, stream, E, T_max, d, in, counts, beta,
+                       lbeta, out);
   else
-    hipLaunchKernelGGL(situ_masked_kernel<Elt::F32>, grid, block, 0, stream, T_max, d, in, counts, beta, lbeta, out);
+    hipLaunchKernelGGL(situ_masked_kernel<Elt::F32>, dim3(grid), dim3(256), 0, stream, E, T_max, d, in, counts, beta,
+                       lbeta, out);
   return hipGetLastError();
 }
 
@@ -142,8 +266,8 @@ __global__ __launch_bounds__(256) void combine_kernel(int K, int N, const float*
   }
   if (out_bf16) {
     uint2 o;
-    o.x = (uint32_t)f32_to_bf16(s.x) | ((uint32_t)f32_to_bf16(s.y) << 16);
-    o.y = (uint32_t)f32_to_bf16(s.z) | ((uint32_t)f32_to_bf16(s.w) << 16);
+    o.x = pack_bf16x2(s.x, s.y);
+    o.y = pack_bf16x2(s.z, s.w);
     reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + (size_t)t * N)[c4] = o;
   } else {
     reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + (size_t)t * N)[c4] = s;
@@ -225,11 +349,11 @@ LMOE_DEV void store_norm(void* out, int out_bf16, size_t idx, const typename Vec
   if (out_bf16) {
     uint16_t* p = reinterpret_cast<uint16_t*>(out) + idx;
     if (VW == 2) {
-      *reinterpret_cast<uint32_t*>(p) = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+      *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(o[0], o[1]);
     } else {
       uint2 w;
-      w.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
-      w.y = (uint32_t)f32_to_bf16(o[VW - 2]) | ((uint32_t)f32_to_bf16(o[VW - 1]) << 16);
+      w.x = pack_bf16x2(o[0], o[1]);
+      w.y = pack_bf16x2(o[VW - 2], o[VW - 1]);
       *reinterpret_cast<uint2*>(p) = w;
     }
   } else {

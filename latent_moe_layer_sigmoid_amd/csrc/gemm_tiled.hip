@@ -64,8 +64,8 @@ LMOE_DEV void store4(Elt elt, void* base, size_t idx, floatx4 v) {
   if (elt == Elt::F32) {
     *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(base) + idx) = v;
   } else {
-    const uint32_t lo = f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    const uint32_t hi = f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    const uint32_t lo = pack_bf16x2(v[0], v[1]);
+    const uint32_t hi = pack_bf16x2(v[2], v[3]);
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + idx) = make_uint2(lo, hi);
   }
 }
@@ -617,8 +617,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const StreamGemm g, 
   if (sg.out_elt == Elt::F32) {
     *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(sg.out) + idx) = v;
   } else {
-    const uint32_t lo = f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    const uint32_t hi = f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    const uint32_t lo = pack_bf16x2(v[0], v[1]);
+    const uint32_t hi = pack_bf16x2(v[2], v[3]);
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(sg.out) + idx) = make_uint2(lo, hi);
   }
 }

@@ -36,26 +36,50 @@ def test_fc1_roofline_bound_by_workload():
     assert abs(r["frac"] - r["achieved"] / 8000.0) < 1e-4
 
 
-def test_fc1_traffic_reads_each_committed_profile():
+def _profile_copy(tmp_path, name):
+    """A copy of the committed counter profile of `name` (with its kernel sources) under
+    tmp_path, its recorded hash set to the sources as they are now; returns the recorded
+    traffic line."""
+    import hashlib
+    prof = os.path.join("profiles", f"fc1_{name}_pmc.md")
+    with open(os.path.join(ROOT, prof)) as f:
+        text = f.read()
+    srcs = next(l for l in text.splitlines() if l.startswith("kernel_sources:")).split(":", 1)[1].split()
+    h = hashlib.sha256()
+    for rel in srcs:
+        os.makedirs(tmp_path / os.path.dirname(rel), exist_ok=True)
+        shutil.copy(os.path.join(ROOT, rel), tmp_path / rel)
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    lines = [l if not l.startswith("kernel_sources_sha256:") else f"kernel_sources_sha256: {h.hexdigest()}"
+             for l in text.splitlines()]
+    os.makedirs(tmp_path / "profiles", exist_ok=True)
+    with open(tmp_path / prof, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return next(l for l in lines if l.startswith("traffic_bytes_per_launch:"))
+
+
+def test_fc1_traffic_reads_each_committed_profile(tmp_path, monkeypatch):
+    """The lookup parses every committed profile (here with its hash matched to the
+    current sources; the real files are withdrawn by the next test's rule whenever a
+    kernel source has changed since they were taken)."""
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     for name in ("decode_bf16", "prefill_bf16", "mx_experts"):
+        line = _profile_copy(tmp_path, name)
         cfg = LI.CONFIGS[name]
         v = bench.fc1_traffic(cfg, 2)
         assert isinstance(v, int) and v > 0, name
-        with open(os.path.join(ROOT, "profiles", f"fc1_{name}_pmc.md")) as f:
-            assert f"traffic_bytes_per_launch: {v}\n" in f.read()
+        assert line == f"traffic_bytes_per_launch: {v}"
         assert bench.fc1_traffic(cfg, 3) is None      # counters were taken at seed 2 only
 
 
 def test_fc1_traffic_is_withdrawn_when_a_kernel_source_changes(tmp_path, monkeypatch):
-    prof = os.path.join("profiles", "fc1_decode_bf16_pmc.md")
-    with open(os.path.join(ROOT, prof)) as f:
-        srcs = next(l for l in f if l.startswith("kernel_sources:")).split(":", 1)[1].split()
-    for rel in [prof] + srcs:
-        os.makedirs(tmp_path / os.path.dirname(rel), exist_ok=True)
-        shutil.copy(os.path.join(ROOT, rel), tmp_path / rel)
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    _profile_copy(tmp_path, "decode_bf16")
     cfg = LI.CONFIGS["decode_bf16"]
     assert bench.fc1_traffic(cfg, 2) is not None
+    with open(os.path.join(ROOT, "profiles", "fc1_decode_bf16_pmc.md")) as f:
+        srcs = next(l for l in f if l.startswith("kernel_sources:")).split(":", 1)[1].split()
     with open(tmp_path / srcs[0], "a") as f:
         f.write("\n// edited\n")
     assert bench.fc1_traffic(cfg, 2) is None

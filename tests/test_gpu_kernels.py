@@ -309,6 +309,29 @@ def test_situ_masked_f32_and_clamps(B):
     np.testing.assert_allclose(got[ok], ref[ok], rtol=2e-5, atol=1e-6)
 
 
+@pytest.mark.parametrize("linear_beta", [0.5, 0.0])
+def test_situ_masked_f32_relative_small_arguments(B, linear_beta):
+    """fp32 SituGLU element by element, relative error only: gate and up values spread
+    log-uniformly over [1e-6, 4] in magnitude, so that tanh and sigmoid are evaluated near
+    zero, where 1 - 2 / (exp(2x) + 1) alone would lose most of its relative accuracy; counts
+    that end inside, at and past the 16-row chunks the kernel works in."""
+    E, Tm, d = 6, 40, 64
+    rng = np.random.default_rng(17)
+    mag = 10.0 ** rng.uniform(-6, np.log10(4.0), (E, Tm, 2 * d))
+    inp = torch.from_numpy((mag * rng.choice([-1.0, 1.0], mag.shape)).astype(np.float32))
+    counts = np.array([0, 1, 16, 17, 33, 40], dtype=np.int32)
+    out = torch.full((E, Tm, d), float("nan"), device=DEV)
+    B.lmoe_situ_masked(E, Tm, d, B.LMOE_F32, inp.to(DEV), torch.from_numpy(counts).to(DEV), 1.0, linear_beta, out)
+    torch.cuda.synchronize()
+    ref = oracle.situ_masked(inp.double().numpy(), counts, 1.0, linear_beta, np.full((E, Tm, d), np.nan), dtype="f32")
+    got = out.cpu().double().numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    rel = np.abs(got[ok] - ref[ok]) / np.abs(ref[ok])
+    print(f"[situ f32] max relative error {rel.max():.3e}", flush=True)
+    assert rel.max() <= 2e-6
+
+
 # -------------------------------------------------------------------------- MXFP8 quant
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
