@@ -117,6 +117,37 @@ LMOE_DEV rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// ---- buffer-to-LDS copies and the waits around them (tiled and MX GEMMs)
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt immediates (gfx9 encoding): vm = vector-memory count (6 bits), lgkm = LDS
+// count (4 bits); expcnt unconstrained.
+constexpr int waitcnt(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8); }
+
+// One wave-wide copy of 16 bytes per lane from a buffer into LDS at lds + 16 * lane.
+LMOE_DEV void to_lds(rsrc_t r, char* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
+}
+
+// A wave-uniform copy of a pointer / value (kept in scalar registers, so that buffer
+// descriptors built from it need no per-lane waterfall).
+LMOE_DEV const char* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
+// Workgroup barrier without the release/acquire fences of __syncthreads(): the fence would
+// make every wavefront wait for all of its buffer-to-LDS loads, including the ones meant
+// to stay in flight. A kernel using it orders LDS itself: s_waitcnt on its own loads, then
+// this.
+LMOE_DEV void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <typename T>
 LMOE_DEV T wave_max(T v) {
 #pragma unroll

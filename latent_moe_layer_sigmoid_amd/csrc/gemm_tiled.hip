@@ -41,8 +41,6 @@
 
 namespace lmoe {
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 constexpr int TILE_M = 128;
 constexpr int TILE_N = 512;           // weight rows per workgroup (SituGLU: 256 gate + 256 up)
 constexpr int NSLOT = 4;              // LDS ring of K steps
@@ -50,14 +48,6 @@ constexpr int SLOT = 40960;           // bytes per K step: A 8 x 1 KB + B 32 x 1
 constexpr int B_OFF = 8192;
 constexpr int LOADS_PER_STEP = 5;     // per wavefront: 1 A block + 4 B blocks
 constexpr int GROUP_M = 8;            // row tiles per swizzle group
-
-// s_waitcnt immediates (gfx9 encoding): vm = vector-memory count (6 bits), lgkm = LDS
-// count (4 bits); expcnt unconstrained.
-constexpr int waitcnt(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8); }
-
-LMOE_DEV void to_lds(rsrc_t r, char* lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
-}
 
 // four consecutive outputs as fp32 (16 bytes) or bf16 (8 bytes)
 LMOE_DEV void store4(Elt elt, void* base, size_t idx, floatx4 v) {
@@ -68,15 +58,6 @@ LMOE_DEV void store4(Elt elt, void* base, size_t idx, floatx4 v) {
     const uint32_t hi = pack_bf16x2(v[2], v[3]);
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + idx) = make_uint2(lo, hi);
   }
-}
-
-// A wave-uniform copy of a pointer / value (kept in scalar registers, so that buffer
-// descriptors built from it need no per-lane waterfall).
-LMOE_DEV const char* uniform_ptr(const void* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
 }
 
 // 16-byte LDS read at byte address addr + OFF. Issued as inline assembly: the compiler
@@ -90,15 +71,6 @@ LMOE_DEV bf16x8_t lds_read16(uint32_t addr) {
   u32x4_t r;
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
   return __builtin_bit_cast(bf16x8_t, r);
-}
-
-// Workgroup barrier without the release/acquire fences of __syncthreads(): the fence would
-// make every wavefront wait for all of its buffer-to-LDS loads, including the ones meant
-// to stay in flight. The kernel orders LDS itself: s_waitcnt on its own loads, then this.
-LMOE_DEV void lds_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
 }
 
 struct Frag {

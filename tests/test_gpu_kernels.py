@@ -682,10 +682,12 @@ def test_fc1_fc2_mx_match_oracle(B, T, E, K, L, d, tile_m):
     assert norm_err(f64(z), oracle.f32_round(ref_z)) <= 1e-4
 
 
-# output widths of 1, 7 and 9 blocks of 64 columns: a wavefront that walks several column
-# blocks also meets a row tile's last, shorter run of blocks
+# output widths of 1, 2, 7, 9 and 32 blocks of 64 columns: a wavefront that walks several
+# column blocks also meets a row tile's last, shorter run of blocks (or none); K = 1 stores
+# the token rows directly
 @pytest.mark.parametrize("T,E,K,d,out_dim,tile_m", [(40, 16, 8, 512, 576, 32), (24, 8, 4, 512, 448, 16),
-                                                    (30, 8, 4, 1024, 64, 32)])
+                                                    (30, 8, 4, 1024, 64, 32), (20, 4, 1, 512, 128, 32),
+                                                    (70, 4, 2, 512, 2048, 32)])
 def test_fc2_mx_column_block_runs(B, T, E, K, d, out_dim, tile_m):
     rng = np.random.default_rng(T + out_dim)
     ids = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
