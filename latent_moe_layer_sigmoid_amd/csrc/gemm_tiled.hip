@@ -27,7 +27,8 @@
 // A wavefront computes only those of its two 32-row tiles that hold a row to store: the
 // padding at the end of an expert's last tile (and, in the dense launches that need no
 // tail or add, rows past M) takes no MFMAs and no fragment reads, while the copies, waits
-// and barriers stay those of every other wavefront.
+// and barriers stay those of every other wavefront (the copy lanes of such rows read past
+// the end of the buffer, which costs no memory request).
 //
 // The epilogue goes through LDS 32 rows per wavefront at a time; the pair ids of the
 // tile's rows are requested before the K loop and the combine weights and in-place
@@ -132,16 +133,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   uint32_t a_off;
   {
     const int row = row0 + 16 * wave + m;
+    // Padding rows (and rows past M) copy from past the end of the buffer: the hardware
+    // range check turns those lanes' copies into zeros without a memory request (their
+    // products are never stored). Buffers within 1 MB of 4 GB copy row 0 instead.
     int arow;
     if (grouped) {
-      int p = g.row_to_pair[row];
-      const bool real = p >= 0;
-      if (!real) p = g.row_to_pair[row0];               // the tile's first row is always a real pair
-      arow = g.a_by_row ? (real ? row : row0) : p / g.topk;
+      const int p = g.row_to_pair[row];
+      arow = p >= 0 ? (g.a_by_row ? row : p / g.topk) : -1;
     } else {
-      arow = min(row, g.M - 1);
+      arow = row < g.M ? row : -1;
     }
-    a_off = (uint32_t)arow * (uint32_t)(g.lda * 2) + g4 * 16;
+    const uint32_t pad_off = g.a_bytes <= 0xFFF00000u ? g.a_bytes : 0u;
+    a_off = (arow >= 0 ? (uint32_t)arow * (uint32_t)(g.lda * 2) : pad_off) + g4 * 16;
   }
   // pair of the output row row0 + 64 rh + lane (-1: padding or past M), read by the
   // epilogue; requested here so that its latency hides behind the K loop

@@ -307,8 +307,20 @@ class LatentMoELayer:
         if not torch.cuda.is_current_stream_capturing():
             X.record_stream(side)
         fold = self.folds_shared_fc2(T)
+        # When the shared FC1's 128 x 512 tiles alone fill the CUs (one workgroup holds a
+        # whole CU), the main stream also waits until the side stream has taken the fork:
+        # the shared FC1 then starts first and shares the chip with the router + down
+        # projection, instead of with the routed FC1 by a race between the two queues.
+        # Same step time (prefill 3.43-3.44 ms either way), a stable split between the
+        # launches. With fewer tiles (T = 1024) the extra wait measured slower.
+        forked = None
+        if (T + 127) // 128 * ((2 * s.I + 511) // 512) >= 256:
+            forked = torch.cuda.Event()
+            forked.record(side)
         B.lmoe_fc1_situ_capped(T, 1, 1, s.H, s.I, 16, dt, X, None, None, None, dt, w["W_s1"], None, s.beta,
                                s.linear_beta, dt, b["act_s"], None, T, self.side_waves, side)
+        if forked is not None:
+            main.wait_event(forked)
         if not fold:
             B.lmoe_fc2_combine(T, 1, 1, s.I, s.H, 16, dt, b["act_s"], None, None, None, dt, w["W_s2"], None, None,
                                dt, b["sh"], T, None, 0, side)
