@@ -194,6 +194,29 @@ def test_layer_decode_graph_replays_match_eager(shared_stream, router_stream):
         torch.cuda.synchronize()
 
 
+def test_layer_token_heavy_graph_replays_match_eager():
+    """Token-heavy two-stream step whose shared FC1 tiles fill the CUs (16 row tiles x 16
+    column blocks), so the main stream also waits for the side stream's fork: a captured
+    graph replays it bit for bit like the eager launches, with eager work in between."""
+    cfg = LI.scaled(LI.PREFILL, name="prefill_heavy_reduced", T=2048, H=1024, L=512, E=64, K=8, d=128, I=4096)
+    layer, _ = build_layer(cfg, 6, shared_stream=True)
+    X = LI.make_x(cfg, 6)
+    X2 = LI.make_x(cfg, 66)
+    Xs = X.to(DEV).clone()
+    eager = layer.forward(Xs).clone()
+    eager2 = layer.forward(X2.to(DEV)).clone()
+    torch.cuda.synchronize()
+    graph = layer.capture(Xs)
+    for r in range(4):
+        Xs.copy_(X.to(DEV) if r % 2 == 0 else X2.to(DEV))
+        graph.replay()
+        torch.cuda.synchronize()
+        want = eager if r % 2 == 0 else eager2
+        assert torch.equal(layer.buffers(cfg.T)["out"].view(torch.int16), want.view(torch.int16)), f"replay {r}"
+        layer.forward(X2.to(DEV))
+        torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("routing,n_group,topk_group", [("renormalize", 1, 1), ("sigmoid", 4, 2)])
 def test_layer_tiny_other_routing_methods(routing, n_group, topk_group):
     cfg = LI.scaled(LI.TINY, routing=routing, n_group=n_group, topk_group=topk_group)
