@@ -13,7 +13,9 @@ weight-streaming kernels of decode and MX experts. `cpu_baseline` is the CPU ora
 bounded sample of the same workload. `workloads` carries the other measurements in the
 same run: the decode layer (warm: back-to-back steps on one input; cold: a 1 GiB scratch
 write before every step and four inputs in rotation, the flush outside the timed events),
-the MX-expert layer (warm and cold), routing us/call at T=1024 (three methods), the masked
+the decode step's time per launch mode (the Python call sequence, the library's own step
+lmoe_layer_forward, its HIP graph, torch's HIP graph), the MX-expert layer (warm and cold),
+routing us/call at T=1024 (three methods), the masked
 SituGLU over the [896, 64, 1024] buffer, the permutation, step-time percentiles, the GPU
 clock and a measured device-copy bandwidth.
 
@@ -300,6 +302,36 @@ def time_layer(torch, layer, Xs, steps, flush=None):
     return [a.elapsed_time(b) for a, b in evs]
 
 
+def launch_modes(torch, layer, X, steps=200):
+    """Microseconds per step, back to back, of the same layer step launched four ways: the
+    Python sequence of library calls (the default), the library's own step
+    (lmoe_layer_forward), the library's HIP graph of it (lmoe_layer_capture / _replay) and
+    torch's HIP graph of the Python sequence."""
+    import time
+
+    def per_step(fn):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return round((time.perf_counter() - t0) / steps * 1e6, 2)
+
+    T = X.shape[0]
+    nat = layer.native(T)
+    cap = torch.cuda.Stream()              # stream capture needs a stream other than the default
+    nat.capture(X, cap)
+    g = layer.capture(X)
+    res = {"python_eager": per_step(lambda: layer.forward(X)), "library_eager": per_step(lambda: nat.forward(X)),
+           "library_graph": per_step(nat.replay), "torch_graph": per_step(g.replay)}
+    torch.cuda.synchronize()
+    nat.close()
+    del g
+    return res
+
+
 def kernel_durations(torch, layer, Xs, steps, flush=None):
     """Mean durations (ms) of each library call of the step (StepTimer events on the launch
     stream) over `steps` steps; with `flush`, a cache-clearing write precedes each step."""
@@ -558,7 +590,8 @@ def main():
             wl["decode_bf16"] = {"config": f"T={dec.T} H={dec.H} L={dec.L} E={dec.E} top-{dec.K} d={dec.d} "
                                            f"shared I={dec.I} bf16 tile_m={dec.tile_m}",
                                  "warm": layer_record(torch, dec, dl, Xd[:1], 100, None, args.seed),
-                                 "cold": layer_record(torch, dec, dl, Xd, 40, flush, args.seed)}
+                                 "cold": layer_record(torch, dec, dl, Xd, 40, flush, args.seed),
+                                 "launch_us_per_step": launch_modes(torch, dl, Xd[0])}
             del dl
         # prefill as a sub-record when the headline is another workload
         if cfg.name != "prefill_bf16" and cfg.experts == "dense" and cfg.dtype == "bf16":

@@ -368,6 +368,134 @@ lmoe_status lmoe_situ_masked(int E, int T_max, int d, lmoe_dtype dtype, const vo
                              const int32_t* expert_num_tokens, float beta, float linear_beta,
                              void* out, hipStream_t stream);
 
+/* ---- One layer step, and its HIP graph ----------------------------------------------
+ * The calls above strung into one forward step of the layer, in the benchmark's schedule
+ * ([P2] "Commit 2": the shared experts on their own stream, overlapping the router and
+ * the routed experts, joined by an event before the routed reduction):
+ *   main stream:   lmoe_linear_multi_ws (router GEMM -> fp32 logits, latent down
+ *                  projection) -> routing + permutation (lmoe_route_permute; or
+ *                  lmoe_route_grouped / lmoe_route_renormalize then lmoe_permute)
+ *                  -> [MX: lmoe_quant_mxfp8] -> lmoe_fc1_situ -> lmoe_fc2_combine_norm
+ *                  -> wait for the second stream -> lmoe_tail (shared FC2 on the second
+ *                  stream) or lmoe_tail_shared_ws (shared FC2 folded into the tail);
+ *   second stream: lmoe_fc1_situ_capped (the shared FC1, dense mode)
+ *                  [-> lmoe_fc2_combine (the shared FC2) when it is not folded].
+ * When the shared FC1's 128 x 512 tiles alone fill the CUs (ceil(T/128) * ceil(2I/512)
+ * >= 256), the main stream also waits until the second stream has taken the fork, so the
+ * shared FC1 starts first. With shared_stream == 0 everything runs on the caller's stream:
+ * one lmoe_linear_multi_ws launch with the shared FC1 as its third projection, then the
+ * routed path, then lmoe_tail_shared_ws. Results are those of the same calls made one by
+ * one (bit for bit: the same launches in the same order).
+ * [P2] measures its decode steps under CUDA graphs and checks graph runs bitwise against
+ * eager ones ("Test Coverage"): lmoe_layer_capture records one step into a HIP graph held
+ * by the layer object, and lmoe_layer_replay launches it.
+ *
+ * lmoe_layer_desc: shapes (T tokens, H hidden, L latent, E experts, K top-k, d expert
+ * intermediate, I shared intermediate), the expert row tile tile_m, dtype (F32 or BF16:
+ * activations, dense weights, gamma and outputs), mx_experts (0: W1 / W2 in dtype; 1:
+ * MXFP4 expert weights with scales, the latent quantized to MXFP8), the routing method
+ * (n_group / topk_group for LMOE_ROUTE_GROUPED; topk weights renormalized and scaled by
+ * routed_scaling_factor as in lmoe_route), beta / linear_beta (SituGLU), eps (RMSNorm),
+ * the packed weights (bias and gamma may be NULL), and the caller-owned device buffers
+ * every call writes, with the sizes those calls require: logits [T,E] fp32, topk_ids /
+ * topk_weights [T,K], the permutation outputs (rows_cap >= lmoe_permute_rows_cap and its
+ * workspace), latent [T,L] (MX: latent_q [T,L] and latent_scales [T,L/32] too), act
+ * [rows_cap,d] (MX: act_scales [rows_cap,d/32]), z [T,L] fp32 and fc2_ws
+ * (lmoe_fc2_workspace_bytes), shared_act [T,I], shared_out [T,H] (needed only when the
+ * shared FC2 is not folded), norm [T,L], out [T,H], and the optional split-K workspaces
+ * of the front and tail launches (NULL: no split). shared_stream selects the schedule,
+ * fold_shared_fc2 (-1: fold from 256 tokens in BF16, 0 / 1) the tail, side_waves the
+ * bound passed to lmoe_fc1_situ_capped (0: its default), side_stream the second stream
+ * (NULL: the layer creates its own; passing the stream the caller's other work already
+ * uses keeps the process's streams from sharing hardware queues with the main stream,
+ * which would serialize the two).
+ *
+ * lmoe_layer_create checks the description (pointers and buffer / workspace sizes, then
+ * every call's shape and dtype rules by calling it with no tokens, which enqueues nothing)
+ * and returns LMOE_ERR_INVALID_ARG / LMOE_ERR_UNSUPPORTED / LMOE_ERR_WORKSPACE as those
+ * calls would. It copies the description and creates, on the current device, three events
+ * and (shared_stream set, side_stream NULL) a second stream of default priority; the layer owns what it
+ * creates and allocates no device buffer. lmoe_layer_forward enqueues one step reading x [T,H] on `stream` (which must
+ * belong to the layer's device; the second stream joins and leaves it through events, so
+ * the step is complete once `stream` reaches its end). Its calls were checked at
+ * creation, so it fails only with LMOE_ERR_HIP (a launch error; the step may then be
+ * partly enqueued) or LMOE_ERR_INVALID_ARG (another current device, x NULL).
+ * lmoe_layer_capture records one step reading x into a HIP graph (stream capture of
+ * `stream`, which must not be the legacy default stream; the graph replaces any earlier
+ * one, and the HIP runtime allocates what it needs to instantiate it); nothing runs. The
+ * graph reads x and writes the description's buffers at the addresses given, so a replay
+ * uses x's contents at that time. lmoe_layer_replay launches the graph on `stream`
+ * (LMOE_ERR_INVALID_ARG before a capture). A layer object is used by one host thread at a
+ * time, and steps of one layer (eager or replayed) must not overlap in time: they share
+ * the buffers and the second stream. lmoe_layer_destroy releases the graph, events and
+ * stream (after the caller has waited for the layer's work); NULL is ignored. */
+typedef enum { LMOE_ROUTE_SIGMOID = 0, LMOE_ROUTE_GROUPED = 1, LMOE_ROUTE_RENORMALIZE = 2 } lmoe_routing;
+
+typedef struct lmoe_layer_desc {
+  int T, H, L, E, K, d, I, tile_m;
+  lmoe_dtype dtype;
+  int mx_experts;
+  lmoe_routing routing;
+  int n_group, topk_group;
+  float beta, linear_beta, routed_scaling_factor, eps;
+  /* packed weights */
+  const void* w_router;      /* [E, H] */
+  const float* bias;         /* [E] fp32 selection bias, NULL = 0 */
+  const void* w_down;        /* [L, H] */
+  const void* w1;            /* [E, 2d, L] (MX: codes [E, 2d, L/2]) */
+  const uint8_t* w1_scales;  /* MX: [E, 2d, L/32] */
+  const void* w2;            /* [E, L, d] (MX: codes [E, L, d/2]) */
+  const uint8_t* w2_scales;  /* MX: [E, L, d/32] */
+  const void* w_s1;          /* [2I, H], gate rows first */
+  const void* w_s2;          /* [H, I] */
+  const void* gamma;         /* [L], NULL = ones */
+  const void* w_up;          /* [H, L] */
+  /* buffers */
+  float* logits;
+  int32_t* topk_ids;
+  float* topk_weights;
+  int32_t* expert_counts;
+  int32_t* expert_offsets;
+  int32_t* tile_offsets;
+  int32_t* row_to_pair;
+  int32_t* tile_expert;
+  int32_t* pair_to_row;
+  int rows_cap;
+  void* perm_ws;
+  size_t perm_ws_bytes;
+  void* latent;
+  uint8_t* latent_q;
+  uint8_t* latent_scales;
+  void* act;
+  uint8_t* act_scales;
+  float* z;
+  void* fc2_ws;
+  size_t fc2_ws_bytes;
+  void* shared_act;
+  void* shared_out;
+  void* norm;
+  void* out;
+  void* front_ws;
+  size_t front_ws_bytes;
+  void* tail_ws;
+  size_t tail_ws_bytes;
+  /* schedule */
+  int shared_stream;
+  int fold_shared_fc2;
+  int side_waves;
+  hipStream_t side_stream;   /* the second stream (caller-owned, default priority); NULL: the layer creates one */
+} lmoe_layer_desc;
+
+typedef struct lmoe_layer lmoe_layer;
+
+/* sizeof(lmoe_layer_desc) as this library was built (a binding checks its own layout). */
+size_t lmoe_layer_desc_bytes(void);
+lmoe_status lmoe_layer_create(const lmoe_layer_desc* desc, lmoe_layer** layer);
+lmoe_status lmoe_layer_forward(lmoe_layer* layer, const void* x, hipStream_t stream);
+lmoe_status lmoe_layer_capture(lmoe_layer* layer, const void* x, hipStream_t stream);
+lmoe_status lmoe_layer_replay(lmoe_layer* layer, hipStream_t stream);
+void lmoe_layer_destroy(lmoe_layer* layer);
+
 #ifdef __cplusplus
 }
 #endif

@@ -5,6 +5,6 @@ include/lmoe.h); `binding` exposes that ABI to Python and `layer` sequences it.
 """
 from . import binding
 from .binding import LmoeError
-from .layer import LatentMoELayer, LayerShape, StepTimer
+from .layer import LatentMoELayer, LayerShape, NativeLayer, StepTimer
 
-__all__ = ["binding", "LmoeError", "LatentMoELayer", "LayerShape", "StepTimer"]
+__all__ = ["binding", "LmoeError", "LatentMoELayer", "LayerShape", "NativeLayer", "StepTimer"]

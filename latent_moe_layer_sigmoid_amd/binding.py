@@ -62,7 +62,34 @@ SIGNATURES = [
     ("lmoe_tail_shared_workspace_bytes", _z, [_i, _i, _i, _i, _i]),
     ("lmoe_tail_shared_ws", _i, [_i, _i, _i, _i, _p, _p, _f, _p, _p, _p, _i, _p, _p, _p, _z, _p]),
     ("lmoe_situ_masked", _i, [_i, _i, _i, _i, _p, _p, _f, _f, _p, _p]),
+    ("lmoe_layer_desc_bytes", _z, []),
+    ("lmoe_layer_create", _i, [_p, _p]),
+    ("lmoe_layer_forward", _i, [_p, _p, _p]),
+    ("lmoe_layer_capture", _i, [_p, _p, _p]),
+    ("lmoe_layer_replay", _i, [_p, _p]),
+    ("lmoe_layer_destroy", None, [_p]),
 ]
+
+LMOE_ROUTE_SIGMOID, LMOE_ROUTE_GROUPED, LMOE_ROUTE_RENORMALIZE = range(3)
+
+
+class LayerDesc(ctypes.Structure):
+    """lmoe_layer_desc of include/lmoe.h, field for field."""
+    _fields_ = (
+        [(n, _i) for n in ("T", "H", "L", "E", "K", "d", "I", "tile_m", "dtype", "mx_experts", "routing", "n_group",
+                           "topk_group")]
+        + [(n, _f) for n in ("beta", "linear_beta", "routed_scaling_factor", "eps")]
+        + [(n, _p) for n in ("w_router", "bias", "w_down", "w1", "w1_scales", "w2", "w2_scales", "w_s1", "w_s2",
+                             "gamma", "w_up", "logits", "topk_ids", "topk_weights", "expert_counts",
+                             "expert_offsets", "tile_offsets", "row_to_pair", "tile_expert", "pair_to_row")]
+        + [("rows_cap", _i), ("perm_ws", _p), ("perm_ws_bytes", _z)]
+        + [(n, _p) for n in ("latent", "latent_q", "latent_scales", "act", "act_scales", "z", "fc2_ws")]
+        + [("fc2_ws_bytes", _z)]
+        + [(n, _p) for n in ("shared_act", "shared_out", "norm", "out", "front_ws")]
+        + [("front_ws_bytes", _z), ("tail_ws", _p), ("tail_ws_bytes", _z)]
+        + [(n, _i) for n in ("shared_stream", "fold_shared_fc2", "side_waves")]
+        + [("side_stream", _p)]
+    )
 
 _lib = None
 
@@ -307,3 +334,32 @@ def lmoe_tail_shared_ws(T, L, H, I, latent, gamma, eps, w_up, shared_act, w_s2, 
 def lmoe_situ_masked(E, T_max, d, dtype, inp, expert_num_tokens, beta, linear_beta, out, stream=None):
     _check("lmoe_situ_masked", lib().lmoe_situ_masked(E, T_max, d, dtype, _ptr(inp), _ptr(expert_num_tokens),
                                                       float(beta), float(linear_beta), _ptr(out), _stream(stream)))
+
+
+def lmoe_layer_desc_bytes():
+    return lib().lmoe_layer_desc_bytes()
+
+
+def lmoe_layer_create(desc):
+    """A layer object for `desc` (a LayerDesc); returns its handle (an int)."""
+    if ctypes.sizeof(LayerDesc) != lib().lmoe_layer_desc_bytes():
+        raise RuntimeError("LayerDesc does not match the library's lmoe_layer_desc")
+    h = ctypes.c_void_p()
+    _check("lmoe_layer_create", lib().lmoe_layer_create(ctypes.byref(desc), ctypes.byref(h)))
+    return h.value
+
+
+def lmoe_layer_forward(layer, x, stream=None):
+    _check("lmoe_layer_forward", lib().lmoe_layer_forward(layer, _ptr(x), _stream(stream)))
+
+
+def lmoe_layer_capture(layer, x, stream=None):
+    _check("lmoe_layer_capture", lib().lmoe_layer_capture(layer, _ptr(x), _stream(stream)))
+
+
+def lmoe_layer_replay(layer, stream=None):
+    _check("lmoe_layer_replay", lib().lmoe_layer_replay(layer, _stream(stream)))
+
+
+def lmoe_layer_destroy(layer):
+    lib().lmoe_layer_destroy(layer)

@@ -6,6 +6,7 @@ commit 7 and the vLLM latent_moe_runner API page for the latent tail).
 This module only sequences library calls and owns device buffers (allocated with torch
 once per token count); every step runs in liblmoe's HIP kernels.
 """
+import weakref
 from dataclasses import dataclass
 
 import torch
@@ -31,6 +32,22 @@ class LayerShape:
     routing: str = "sigmoid"   # "sigmoid" (bias-corrected, DeepSeekV3) or "renormalize"
     n_group: int = 1          # grouped top-k for sigmoid routing
     topk_group: int = 1
+
+
+# The extra streams of the layer, one of each kind per device, shared by every layer of the
+# process: HIP gives a process a few hardware queues (four by default) and spreads its
+# streams over them, so every new stream risks landing on the main stream's queue, where
+# its work would run after the main stream's instead of beside it (measured: an MX step
+# 0.59 -> 0.73 ms with a freshly created side stream in a process holding several). Layers
+# run one after another, so sharing costs no overlap.
+_AUX_STREAMS = {}
+
+
+def _aux_stream(device, kind):
+    key = (str(device), kind)
+    if key not in _AUX_STREAMS:
+        _AUX_STREAMS[key] = torch.cuda.Stream(device)   # default priority
+    return _AUX_STREAMS[key]
 
 
 def _lmoe_dtype(dtype):
@@ -79,8 +96,8 @@ class LatentMoELayer:
         self.side_waves = side_waves
         self.device = torch.device(device)
         # extra streams at the default priority
-        self._side = torch.cuda.Stream(self.device) if self.shared_stream else None
-        self._router = torch.cuda.Stream(self.device) if router_stream else None
+        self._side = _aux_stream(self.device, "side") if self.shared_stream else None
+        self._router = _aux_stream(self.device, "router") if router_stream else None
         self._bufs = {}
         # weights go to HBM in the packed MFMA-operand layout once, at construction
         self.w = {}
@@ -102,8 +119,8 @@ class LatentMoELayer:
         other = copy.copy(self)
         other.s = dataclasses.replace(self.s, **changes)
         other._bufs = {}
-        other._side = torch.cuda.Stream(self.device) if self.shared_stream else None
-        other._router = torch.cuda.Stream(self.device) if self.router_stream else None
+        other._side = self._side
+        other._router = self._router
         return other
 
     def buffers(self, T):
@@ -214,6 +231,14 @@ class LatentMoELayer:
         if self.fold_shared_fc2 is not None:
             return self.fold_shared_fc2
         return T >= 256 and self.s.dtype == "bf16"
+
+    def native(self, T):
+        """This layer's step over T tokens as one library object (lmoe_layer_create): the
+        same launches as forward() with its schedule, run by lmoe_layer_forward, and
+        recordable as a HIP graph inside the library (lmoe_layer_capture / _replay). It
+        uses this layer's packed weights and buffers(T). The fused schedules only (one
+        stream, or the shared-expert stream without the router stream)."""
+        return NativeLayer(self, T)
 
     def capture(self, X):
         """A HIP graph of one forward pass on the static input X (same buffers as
@@ -354,6 +379,76 @@ class LatentMoELayer:
             B.lmoe_tail(T, s.L, s.H, None, w["gamma"], s.eps, w["W_up"], b["sh"], dt, b["out"], b["n"], main)
         mark(None)
         return b["out"]
+
+
+class NativeLayer:
+    """A lmoe_layer object over a LatentMoELayer's weights and buffers for T tokens.
+    forward(X) enqueues one step (output in buffers(T)["out"]); capture(X) records one
+    step reading X into a HIP graph inside the library and replay() launches it."""
+
+    def __init__(self, layer, T):
+        if not layer.fused or layer.router_stream:
+            raise ValueError("the library's layer step runs the fused schedules without the router stream")
+        s, w = layer.s, layer.w
+        b = layer.buffers(T)
+        mx = s.experts == "mx"
+        d = B.LayerDesc()
+        d.T, d.H, d.L, d.E, d.K, d.d, d.I, d.tile_m = T, s.H, s.L, s.E, s.K, s.d, s.I, s.tile_m
+        d.dtype = _lmoe_dtype(s.dtype)
+        d.mx_experts = int(mx)
+        if s.routing == "renormalize":
+            d.routing = B.LMOE_ROUTE_RENORMALIZE
+        else:
+            d.routing = B.LMOE_ROUTE_GROUPED if s.n_group > 1 else B.LMOE_ROUTE_SIGMOID
+        d.n_group, d.topk_group = s.n_group, s.topk_group
+        d.beta, d.linear_beta, d.routed_scaling_factor, d.eps = s.beta, s.linear_beta, s.rsf, s.eps
+        P = B._ptr
+        d.w_router, d.bias, d.w_down = P(w["W_r"]), P(w.get("bias")), P(w["W_down"])
+        if mx:
+            d.w1, d.w1_scales = P(w["W1_codes"]), P(w["W1_scales"])
+            d.w2, d.w2_scales = P(w["W2_codes"]), P(w["W2_scales"])
+        else:
+            d.w1, d.w2 = P(w["W1"]), P(w["W2"])
+        d.w_s1, d.w_s2, d.gamma, d.w_up = P(w["W_s1"]), P(w["W_s2"]), P(w.get("gamma")), P(w["W_up"])
+        d.logits, d.topk_ids, d.topk_weights = P(b["logits"]), P(b["ids"]), P(b["weights"])
+        d.expert_counts, d.expert_offsets, d.tile_offsets = P(b["counts"]), P(b["offsets"]), P(b["tile_offsets"])
+        d.row_to_pair, d.tile_expert, d.pair_to_row = P(b["row_to_pair"]), P(b["tile_expert"]), P(b["pair_to_row"])
+        d.rows_cap, d.perm_ws, d.perm_ws_bytes = b["rows_cap"], P(b["perm_ws"]), b["perm_ws_bytes"]
+        d.latent = P(b["x"])
+        if mx:
+            d.latent_q, d.latent_scales, d.act_scales = P(b["xq"]), P(b["xs"]), P(b["act_scale"])
+        d.act, d.z, d.fc2_ws, d.fc2_ws_bytes = P(b["act"]), P(b["z"]), P(b["fc2_ws"]), b["fc2_ws_bytes"]
+        d.shared_act, d.shared_out, d.norm, d.out = P(b["act_s"]), P(b["sh"]), P(b["n"]), P(b["out"])
+        d.front_ws, d.front_ws_bytes = P(b["front_ws"]), b["front_ws_bytes"]
+        d.tail_ws, d.tail_ws_bytes = P(b["tail_ws"]), b["tail_ws_bytes"]
+        d.shared_stream = int(layer.shared_stream)
+        d.fold_shared_fc2 = -1 if layer.fold_shared_fc2 is None else int(bool(layer.fold_shared_fc2))
+        d.side_waves = layer.side_waves
+        # the Python layer's own second stream: one more stream of the library's would
+        # share a hardware queue with the main stream in a process that holds many
+        d.side_stream = layer._side.cuda_stream if layer._side is not None else None
+        self.T = T
+        self.out = b["out"]
+        self._keep = (layer, b, w)      # the tensors behind every pointer stay alive
+        self.handle = B.lmoe_layer_create(d)
+        # released when the object goes away, or at interpreter exit (before the HIP
+        # runtime's own teardown)
+        self._finalizer = weakref.finalize(self, B.lmoe_layer_destroy, self.handle)
+
+    def forward(self, X, stream=None):
+        B.lmoe_layer_forward(self.handle, X, stream)
+        return self.out
+
+    def capture(self, X, stream=None):
+        B.lmoe_layer_capture(self.handle, X, stream)
+
+    def replay(self, stream=None):
+        B.lmoe_layer_replay(self.handle, stream)
+
+    def close(self):
+        """Destroy the library object (the caller has waited for its work)."""
+        self._finalizer()
+        self.handle = None
 
 
 class StepTimer:

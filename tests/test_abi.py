@@ -15,7 +15,7 @@ def header_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     funcs = {}
-    for m in re.finditer(r"(?:lmoe_status|size_t|int|const char\s*\*)\s+(lmoe_\w+)\s*\(([^)]*)\)\s*;", src):
+    for m in re.finditer(r"(?:lmoe_status|size_t|int|void|const char\s*\*)\s+(lmoe_\w+)\s*\(([^)]*)\)\s*;", src):
         args = m.group(2).strip()
         funcs[m.group(1)] = 0 if args in ("", "void") else len(args.split(","))
     return funcs
@@ -106,6 +106,56 @@ def test_invalid_calls_are_rejected_without_a_gpu(B):
     # linear: N % 16, dtype mismatch
     assert L.lmoe_linear(4, 20, 128, B.LMOE_BF16, P, B.LMOE_BF16, P, B.LMOE_F32, P, None) == B.LMOE_ERR_UNSUPPORTED
     assert L.lmoe_linear(4, 32, 128, B.LMOE_BF16, P, B.LMOE_F32, P, B.LMOE_F32, P, None) == B.LMOE_ERR_INVALID_ARG
+
+
+def test_layer_descriptions_are_checked_without_a_gpu(B):
+    """lmoe_layer_create rejects a bad description before any HIP call: its own pointer
+    and size checks, then the zero-token calls of every step (which touch no HIP API)."""
+    import ctypes
+    assert ctypes.sizeof(B.LayerDesc) == B.lmoe_layer_desc_bytes()
+    L = B.lib()
+    P = 0x1000   # never dereferenced
+
+    def desc(**over):
+        d = B.LayerDesc()
+        d.T, d.H, d.L, d.E, d.K, d.d, d.I, d.tile_m = 8, 7168, 2048, 896, 16, 512, 4096, 16
+        d.dtype, d.routing, d.n_group, d.topk_group = B.LMOE_BF16, B.LMOE_ROUTE_SIGMOID, 1, 1
+        d.beta, d.linear_beta, d.routed_scaling_factor, d.eps = 1.0, 0.5, 2.5, 1e-6
+        for n in ("w_router", "w_down", "w1", "w2", "w_s1", "w_s2", "w_up", "logits", "topk_ids", "topk_weights",
+                  "expert_counts", "expert_offsets", "tile_offsets", "row_to_pair", "tile_expert", "pair_to_row",
+                  "perm_ws", "latent", "act", "z", "fc2_ws", "shared_act", "shared_out", "norm", "out"):
+            setattr(d, n, P)
+        d.rows_cap = B.lmoe_permute_rows_cap(8, 896, 16, 16)
+        d.perm_ws_bytes = 1 << 20
+        d.fc2_ws_bytes = B.lmoe_fc2_workspace_bytes(8, 16, 2048)
+        d.shared_stream, d.fold_shared_fc2 = 1, -1
+        for k, v in over.items():
+            setattr(d, k, v)
+        return d
+
+    def create(d):
+        h = ctypes.c_void_p()
+        st = L.lmoe_layer_create(ctypes.byref(d), ctypes.byref(h))
+        assert h.value is None
+        return st
+
+    assert L.lmoe_layer_create(None, None) == B.LMOE_ERR_INVALID_ARG
+    assert create(desc(H=0)) == B.LMOE_ERR_INVALID_ARG
+    assert create(desc(dtype=B.LMOE_MXFP8_E4M3)) == B.LMOE_ERR_INVALID_ARG
+    assert create(desc(routing=7)) == B.LMOE_ERR_INVALID_ARG
+    assert create(desc(w1=None)) == B.LMOE_ERR_INVALID_ARG
+    assert create(desc(out=None)) == B.LMOE_ERR_INVALID_ARG
+    assert create(desc(mx_experts=1)) == B.LMOE_ERR_INVALID_ARG            # no scales
+    assert create(desc(shared_out=None)) == B.LMOE_ERR_INVALID_ARG         # T = 8: the shared FC2 is not folded
+    assert create(desc(side_waves=-1)) == B.LMOE_ERR_INVALID_ARG
+    assert create(desc(rows_cap=16)) == B.LMOE_ERR_WORKSPACE
+    assert create(desc(fc2_ws_bytes=16)) == B.LMOE_ERR_WORKSPACE
+    assert create(desc(E=2048, rows_cap=B.lmoe_permute_rows_cap(8, 2048, 16, 16))) == B.LMOE_ERR_UNSUPPORTED
+    assert create(desc(K=65, rows_cap=B.lmoe_permute_rows_cap(8, 896, 65, 16),
+                       fc2_ws_bytes=B.lmoe_fc2_workspace_bytes(8, 65, 2048))) == B.LMOE_ERR_INVALID_ARG  # K <= 64
+    assert create(desc(H=7160)) == B.LMOE_ERR_UNSUPPORTED                   # projections: H % 128
+    assert create(desc(routing=B.LMOE_ROUTE_GROUPED, n_group=3)) == B.LMOE_ERR_INVALID_ARG   # E % n_group
+    assert create(desc(beta=0.0)) == B.LMOE_ERR_INVALID_ARG
 
 
 def test_product_path_refuses_to_run_without_the_library(monkeypatch):

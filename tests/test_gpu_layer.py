@@ -217,6 +217,70 @@ def test_layer_token_heavy_graph_replays_match_eager():
         torch.cuda.synchronize()
 
 
+HEAVY = LI.scaled(LI.PREFILL, name="prefill_heavy_reduced", T=2048, H=1024, L=512, E=64, K=8, d=128, I=4096)
+NATIVE_CASES = {"decode": LI.DECODE, "mx": LI.MX, "heavy": HEAVY,
+                "grouped": LI.scaled(LI.TINY, n_group=4, topk_group=2),
+                "renormalize": LI.scaled(LI.TINY, routing="renormalize")}
+
+
+@pytest.mark.parametrize("name,shared_stream", [("decode", True), ("decode", False), ("mx", True), ("heavy", True),
+                                                 ("heavy", False), ("grouped", True), ("renormalize", False)])
+def test_native_layer_step_matches_python_forward(name, shared_stream):
+    """lmoe_layer_forward (the step strung together inside the library, its second stream
+    its own) leaves the same bits as the Python layer's forward in every buffer the step
+    writes: the same launches in the same order."""
+    cfg = NATIVE_CASES[name]
+    print(f"[native step] {name} T={cfg.T} shared_stream={shared_stream}", flush=True)
+    layer, _ = build_layer(cfg, 3, shared_stream=shared_stream)
+    X = LI.make_x(cfg, 3).to(DEV)
+    b = layer.buffers(cfg.T)
+    keys = ["out", "n", "z", "ids", "weights", "counts", "row_to_pair", "logits", "x", "act_s"]
+    layer.forward(X)
+    torch.cuda.synchronize()
+    want = {k: b[k].clone() for k in keys}
+    for k in keys:
+        b[k].fill_(0) if b[k].dtype != torch.int32 else b[k].fill_(-7)
+    nat = layer.native(cfg.T)
+    nat.forward(X)
+    torch.cuda.synchronize()
+    used = int(b["tile_offsets"][-1].item())   # rows past the last tile are never written
+    for k in keys:
+        got, exp = b[k], want[k]
+        if k == "row_to_pair":
+            got, exp = got[:used], exp[:used]
+        assert torch.equal(got.view(torch.uint8), exp.view(torch.uint8)), k
+    assert used > 0
+    nat.close()
+
+
+@pytest.mark.parametrize("name,shared_stream", [("decode", True), ("heavy", True), ("decode", False)])
+def test_native_layer_graph_replays_match_eager(name, shared_stream):
+    """lmoe_layer_capture records one step into a HIP graph inside the library; replays,
+    with eager steps and synchronizations between them, reproduce the eager output bit for
+    bit for the input's contents at each replay."""
+    cfg = NATIVE_CASES[name]
+    print(f"[native graph] {name} T={cfg.T} shared_stream={shared_stream}", flush=True)
+    layer, _ = build_layer(cfg, 4, shared_stream=shared_stream)
+    nat = layer.native(cfg.T)
+    X1, X2 = LI.make_x(cfg, 4).to(DEV), LI.make_x(cfg, 44).to(DEV)
+    s = torch.cuda.Stream(DEV)
+    with torch.cuda.stream(s):
+        e1 = nat.forward(X1).clone()
+        e2 = nat.forward(X2).clone()
+        Xs = X1.clone()
+        torch.cuda.synchronize()
+        nat.capture(Xs)
+        for r in range(4):
+            Xs.copy_(X1 if r % 2 == 0 else X2)
+            nat.replay()
+            torch.cuda.synchronize()
+            want = e1 if r % 2 == 0 else e2
+            assert torch.equal(nat.out.view(torch.int16), want.view(torch.int16)), f"replay {r}"
+            nat.forward(X2)
+            torch.cuda.synchronize()
+    nat.close()
+
+
 @pytest.mark.parametrize("routing,n_group,topk_group", [("renormalize", 1, 1), ("sigmoid", 4, 2)])
 def test_layer_tiny_other_routing_methods(routing, n_group, topk_group):
     cfg = LI.scaled(LI.TINY, routing=routing, n_group=n_group, topk_group=topk_group)
