@@ -6,6 +6,8 @@ import numpy as np
 import pytest
 import torch
 
+from latent_moe_layer_sigmoid_amd import binding as B
+
 import lmoe_inputs as LI
 import oracle
 from gpu_helpers import (f64, guarded_x, norm_err, oracle_route, oracle_weights, run_oracle_layer,
@@ -278,6 +280,26 @@ def test_native_layer_graph_replays_match_eager(name, shared_stream):
             assert torch.equal(nat.out.view(torch.int16), want.view(torch.int16)), f"replay {r}"
             nat.forward(X2)
             torch.cuda.synchronize()
+    nat.close()
+
+
+def test_native_layer_edge_cases():
+    """A replay before any capture is rejected; capture on the legacy default stream is
+    rejected (stream capture needs another stream); closing twice is harmless."""
+    cfg = LI.TINY
+    layer, _ = build_layer(cfg, 8, shared_stream=True)
+    nat = layer.native(cfg.T)
+    X = LI.make_x(cfg, 8).to(DEV)
+    with pytest.raises(B.LmoeError) as e:
+        nat.replay()
+    assert e.value.status == B.LMOE_ERR_INVALID_ARG
+    with pytest.raises(B.LmoeError) as e:
+        B.lmoe_layer_capture(nat.handle, X, 0)
+    assert e.value.status == B.LMOE_ERR_INVALID_ARG
+    out = nat.forward(X).clone()            # still usable after the rejected calls
+    torch.cuda.synchronize()
+    assert torch.equal(out, layer.forward(X))
+    nat.close()
     nat.close()
 
 
