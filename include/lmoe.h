@@ -130,7 +130,7 @@ lmoe_status lmoe_linear_multi_ws(int M, int Kd, lmoe_dtype x_dtype, const void* 
                                  hipStream_t stream);
 
 /* Single-group DeepSeekV3 top-k routing ([P1] commit 1: with one group the
- * grouped top-k is a plain top-k over all experts, result k held in lane k; [P1]
+ * grouped rule reduces to choosing the K best of every expert, result k held in lane k; [P1]
  * commit 4: sigmoid scores, selection bias, routed scaling factor, FP32 logits).
  *   s = sigmoid(logits[t, :]);  selection key = s + bias (bias may be NULL = 0);
  *   topk_ids[t, k]  = expert with the k-th largest key (ties -> lower expert index);
@@ -220,8 +220,8 @@ lmoe_status lmoe_route_permute(int T, int E, int K, const float* logits, const f
                                int rows_cap, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* MXFP8 (E4M3) quantization along rows ([OCP-MX]; [P2] "Description": input
- * quantization before the MXE4M3 x MXE2M1 experts; [P1] commit 3: the general gated
- * activations apply the activation, then requantize). Per 32 consecutive elements:
+ * quantization before the MXE4M3 x MXE2M1 experts; [P1] commit 3: outside the fused
+ * SiLU path, the activation output is quantized again afterwards). Per 32 consecutive elements:
  * exponent X = floor(log2 max|v|) - 8 clamped to [-127,127] (0 for an all-zero block);
  * code = E4M3(v / 2^X), nearest-even, saturating at 448, sign bit set for v < 0.
  * in [rows, cols] (F32 or BF16), codes u8 [rows, cols], scales u8 [rows, cols/32] = X+127.
@@ -359,7 +359,7 @@ lmoe_status lmoe_tail_shared_ws(int T, int L, int H, int I, const float* latent,
                                 hipStream_t stream);
 
 /* Masked SituGLU over the batched [E, T_max, 2d] expert layout ([P1] commit 2:
- * masked_situ_and_mul reads expert_num_tokens and leaves padded rows untouched).
+ * the masked kernel takes each expert's valid row count and never touches rows past it).
  *   For e < E and r < clamp(expert_num_tokens[e], 0, T_max):
  *     out[e, r, j] = SituGLU(in[e, r, j], in[e, r, d + j]), fp32 math;
  *   every other element of `out` is left exactly as it was.

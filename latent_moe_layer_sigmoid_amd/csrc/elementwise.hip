@@ -8,8 +8,8 @@
 
 namespace lmoe {
 
-// ---- masked SituGLU over [E, T_max, 2d] (vLLM PR 50088, commit 2: masked_situ_and_mul
-// reads expert_num_tokens and leaves padded rows untouched; fp32 math).
+// ---- masked SituGLU over [E, T_max, 2d] (vLLM PR 50088, commit 2: the masked kernel takes
+// each expert's valid row count and never touches rows past it; fp32 math).
 // The valid rows of all experts (v_e = min(count_e, T_max) each) are one list of
 // R = sum v_e rows, dealt evenly to a fixed grid: every workgroup scans the E counts in
 // LDS, then wavefront g of the grid takes list rows g, g + G, g + 2G, ... (G wavefronts in

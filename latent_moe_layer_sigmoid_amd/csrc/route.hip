@@ -1,6 +1,6 @@
 // Single-group sigmoid top-k routing for gfx950 (vLLM PR 50088, "What's in it",
-// commit 1: with n_group == topk_group == 1 the grouped top-k is a plain top-k over all
-// experts, result k in lane k; commit 4: sigmoid scores, selection bias, routed scaling
+// commit 1: with n_group == topk_group == 1 the grouped rule reduces to the K best of
+// every expert, result k in lane k; commit 4: sigmoid scores, selection bias, routed scaling
 // factor, FP32 logits).
 //
 // One wavefront (64 lanes) per token. Lane l owns experts l, l+64, l+128, ... and keeps

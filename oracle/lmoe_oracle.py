@@ -201,7 +201,7 @@ def router_logits(X, W_r):
 def route(logits, bias, K, rsf, renormalize=True):
     """Single-group DeepSeekV3 top-k routing ([P1] commits 1 and 4).
 
-    With one group, the grouped top-k is a plain top-k over all experts (commit 1).
+    With one group, the grouped rule reduces to the K best of every expert (commit 1).
     Scores are s = sigmoid(logits); experts are selected on the bias-corrected score
     kappa = s + bias, slot k holding the k-th largest (commit 1: result k sits in
     lane k), ties to the lower expert index. The selection key is formed in fp32,
