@@ -109,8 +109,12 @@ def fc1_roofline(cfg, n_touched, rows, pairs, fc1_ms, counts=None):
         return r
     fb = fc1_bytes(cfg, n_touched, rows)
     achieved = fb / (fc1_ms * 1e-3) / 1e9
-    kern = ("stream_gemm_mx_kernel, MXFP8 x MXFP4 scaled MFMA" if cfg.experts == "mx"
-            else "stream_gemm_kernel, SituGLU epilogue")
+    if cfg.experts == "mx":
+        # 32-row expert tiles: activation rows staged in LDS once per 4-wavefront workgroup
+        kern = ("mx_fc1_lds_kernel" if cfg.tile_m % 32 == 0 else "stream_gemm_mx_kernel") + \
+            ", MXFP8 x MXFP4 scaled MFMA, SituGLU + MXFP8 requantization epilogue"
+    else:
+        kern = "stream_gemm_kernel, SituGLU epilogue"
     return {"kernel": f"grouped FC1 + SituGLU ({kern})", "bound": "hbm", "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "algorithmic_bytes": fb, "avg_ms": round(fc1_ms, 5), "n_touched_experts": n_touched}

@@ -34,6 +34,11 @@ def test_fc1_roofline_bound_by_workload():
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
     assert abs(r["achieved"] - 480051200 / 0.08e-3 / 1e9) < 0.1
     assert abs(r["frac"] - r["achieved"] / 8000.0) < 1e-4
+    # the kernel named is the one each workload's FC1 launches (the profiles name the same)
+    assert "tiled_gemm_kernel" in bench.fc1_roofline(pf, 692, 188288, 131072, 1.0)["kernel"]
+    assert "stream_gemm_kernel" in r["kernel"]
+    mx = LI.CONFIGS["mx_experts"]
+    assert mx.tile_m == 32 and "mx_fc1_lds_kernel" in bench.fc1_roofline(mx, 764, 31680, 16384, 0.2)["kernel"]
 
 
 def _profile_copy(tmp_path, name):
