@@ -24,18 +24,31 @@ LMOE_DEV uint32_t wave_max_u32(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
-LMOE_DEV void cas_desc(uint64_t& a, uint64_t& b) {
-  const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+// Sort keys are positive normal doubles: the bits 2^52 + s 2^10 + (1023 - e) for the
+// order-preserving 32 bits s of an expert's fp32 key and its index e < 1024, so that the
+// fp64 order is that of s, then of the lower index; padding is 2^52 itself (s = 0, which
+// no real key has), below every real key. A compare-exchange is then one fp64 max and one
+// fp64 min (each returns one of its operands unchanged), with no condition register
+// between the comparators, which a 64-bit integer compare and four selects would need.
+LMOE_DEV double sort_key(uint32_t s, int e) {
+  return __builtin_bit_cast(double, (1ull << 52) | ((uint64_t)s << 10) | (uint64_t)(1023 - e));
+}
+constexpr double kSortPad = 2.2250738585072014e-308;   // the double with bits 2^52
+LMOE_DEV uint32_t sort_key_s(double k) { return (uint32_t)((__builtin_bit_cast(uint64_t, k) >> 10) & 0xFFFFFFFFull); }
+LMOE_DEV int sort_key_e(double k) { return 1023 - (int)(__builtin_bit_cast(uint64_t, k) & 1023ull); }
+
+LMOE_DEV void cas_desc(double& a, double& b) {
+  const double hi = __builtin_fmax(a, b), lo = __builtin_fmin(a, b);
   a = hi;
   b = lo;
 }
 
 // Batcher's odd-even merge sort of N (a power of two) keys, descending; fully unrolled.
-// Keys from index LIVE on are padding holding 0, below every real key: a descending
+// Keys from index LIVE on are padding, below every real key: a descending
 // compare-exchange leaves the smaller key at the higher index, so such a slot only ever
-// meets real keys as the higher index and keeps its 0; those comparators are left out.
+// meets real keys as the higher index and keeps its padding; those comparators are left out.
 template <int N, int LIVE = N>
-LMOE_DEV void sort_desc(uint64_t* k) {
+LMOE_DEV void sort_desc(double* k) {
 #pragma unroll
   for (int p = 1; p < N; p <<= 1)
 #pragma unroll
@@ -86,24 +99,23 @@ LMOE_DEV void route_token(int t, int E, int K, const float* __restrict__ logits,
     lg[j] = row[e];
     bs[j] = (METHOD == 0 && bias) ? bias[e] : 0.0f;
   }
-  uint64_t key[NP];
+  double key[NP];
 #pragma unroll
   for (int j = 0; j < NP; ++j) {
     const int e = lane + 64 * j;
-    key[j] = 0;   // below every real key; never selected since K <= the competing experts
+    key[j] = kSortPad;   // below every real key; never selected since K <= the competing experts
     const bool competes = e < E && (group_size <= 0 || ((keep_groups >> (e / max(group_size, 1))) & 1ull));
-    if (j < KPL && competes) {
-      const float kap = route_key<METHOD>(lg[j], bs[j]);
-      key[j] = ((uint64_t)orderable(kap) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
-    }
+    if (j < KPL && competes) key[j] = sort_key(orderable(route_key<METHOD>(lg[j], bs[j])), e);
   }
   sort_desc<NP, KPL>(key);
+  // the selection rounds work on two 32-bit words per key: the score bits (0 for padding)
+  // and ~expert
   u32v vh, vl;
   f32v vlg;
 #pragma unroll
   for (int j = 0; j < NP; ++j) {
-    vh[j] = (uint32_t)(key[j] >> 32);
-    vl[j] = (uint32_t)key[j];
+    vh[j] = sort_key_s(key[j]);
+    vl[j] = 0xFFFFFFFFu - (uint32_t)sort_key_e(key[j]);
     vlg[j] = j < KPL ? lg[j] : 0.0f;
   }
 
