@@ -123,12 +123,12 @@ LMOE_DEV void route_token(int t, int E, int K, const float* __restrict__ logits,
   int head = 0;
   uint32_t my_lo = 0;
   float my_lg = 0.0f;
-  for (int k = 0; k < K; ++k) {
+  auto round = [&](int k) __attribute__((always_inline)) {
     const uint32_t mh = wave_max_u32(hh);
     const uint64_t tied = __ballot(hh == mh);
     int wl;
     uint32_t ml;
-    if (__popcll(tied) == 1) {
+    if (__builtin_expect(__popcll(tied) == 1, 1)) {   // ties are rare: the other path out of line
       wl = __ffsll((unsigned long long)tied) - 1;
       ml = (uint32_t)__builtin_amdgcn_readlane((int)ll, wl);
     } else {   // equal scores: the larger ~expert (lower expert index) wins
@@ -155,6 +155,16 @@ LMOE_DEV void route_token(int t, int E, int K, const float* __restrict__ logits,
       ll = nl;
       head = nxt;
     }
+  };
+  // top-16 and top-8, the common cases, as straight code: no loop branch between rounds,
+  // and one round's tail overlaps the next one's maximum (measured at top-16: 5.9 -> 5.2 us
+  // per call of 1024 tokens)
+  if (K == 16) {
+    static_for<16>([&](auto k) __attribute__((always_inline)) { round(decltype(k)::value); });
+  } else if (K == 8) {
+    static_for<8>([&](auto k) __attribute__((always_inline)) { round(decltype(k)::value); });
+  } else {
+    for (int k = 0; k < K; ++k) round(k);
   }
   int e = -1;
   float s = 0.0f;
