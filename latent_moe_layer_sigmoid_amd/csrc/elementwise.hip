@@ -81,11 +81,23 @@ __global__ __launch_bounds__(256) void situ_masked_kernel(int E, int T_max, int 
   __shared__ int s_off[MASK_MAX_E + 1];   // exclusive prefix of the clamped counts
   __shared__ int s_tot[4];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  // clamped counts and their exclusive scan (chunks of 256 experts, running total)
+  // clamped counts and their exclusive scan (chunks of 256 experts, running total); every
+  // chunk's counts are requested before the first scan step, so that the loads do not wait
+  // on each other across the scan's barriers
+  constexpr int NCH = MASK_MAX_E / 256;
+  int cv[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int e = 256 * i + (int)threadIdx.x;
+    cv[i] = e < E ? counts[e] : 0;
+  }
   int run = 0;
-  for (int e0 = 0; e0 < E; e0 += 256) {
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int e0 = 256 * i;
+    if (e0 >= E) break;
     const int e = e0 + (int)threadIdx.x;
-    int v = e < E ? counts[e] : 0;
+    int v = cv[i];
     v = v < 0 ? 0 : (v > T_max ? T_max : v);
     int x = v;   // inclusive scan within the wave (shift by 1, 2, ... 32 lanes)
 #pragma unroll
@@ -96,7 +108,7 @@ __global__ __launch_bounds__(256) void situ_masked_kernel(int E, int T_max, int 
     if (lane == 63) s_tot[w] = x;
     lds_sync();
     int before = run;
-    for (int i = 0; i < w; ++i) before += s_tot[i];
+    for (int j = 0; j < w; ++j) before += s_tot[j];
     if (e < E) s_off[e] = before + x - v;
     run += s_tot[0] + s_tot[1] + s_tot[2] + s_tot[3];
     lds_sync();
