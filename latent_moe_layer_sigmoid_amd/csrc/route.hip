@@ -69,7 +69,20 @@ __global__ __launch_bounds__(256) void route_grouped_kernel(int T, int E, int K,
   float* kap = s_kap + wv * (E + 64);
   float* gsc = kap + E;
   const float* row = logits + (size_t)t * E;
-  for (int e = lane; e < E; e += 64) kap[e] = score_of(row[e]) + (bias ? bias[e] : 0.0f);
+  {   // every logit and bias requested before the first score is stored
+    float lg[KPL], bs[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int e = min(lane + 64 * j, E - 1);
+      lg[j] = row[e];
+      bs[j] = bias ? bias[e] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E) kap[e] = score_of(lg[j]) + bs[j];
+    }
+  }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -82,6 +95,7 @@ __global__ __launch_bounds__(256) void route_grouped_kernel(int T, int E, int K,
   const int g = lane / lpg, sub = lane % lpg;
   float t1 = -INFINITY, t2 = -INFINITY;
   if (g < n_group) {
+#pragma unroll 8
     for (int i = sub; i < gs; i += lpg) {
       const float v = kap[g * gs + i];
       if (v > t1) {
