@@ -5,7 +5,8 @@
 //
 // One wavefront (64 lanes) per token. Lane l owns experts l, l+64, l+128, ... and keeps
 // their keys as a list sorted in descending order (a Batcher odd-even merge network in
-// registers). A key is (order-preserving bits of sigmoid(logit) + bias, ~expert): the
+// registers, on keys encoded as positive doubles so that each compare-exchange is an fp64
+// max and min). A key is (order-preserving bits of sigmoid(logit) + bias, ~expert): the
 // larger key wins and equal scores resolve to the lower expert index. Each of the K
 // rounds takes the wave maximum of the lanes' list heads in two 32-bit passes (score
 // bits, then ~expert among the lanes holding the top score) with DPP row shifts and row
