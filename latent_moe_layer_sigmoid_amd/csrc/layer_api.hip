@@ -246,9 +246,9 @@ lmoe_status lmoe_layer_capture(lmoe_layer* layer, const void* x, hipStream_t str
   if (st == LMOE_OK && end != hipSuccess) st = LMOE_ERR_HIP;
   hipGraphExec_t exec = nullptr;
   if (st == LMOE_OK && hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) != hipSuccess) st = LMOE_ERR_HIP;
-  if (graph) hipGraphDestroy(graph);
+  if (graph) (void)hipGraphDestroy(graph);   // releases: nothing to report to the caller
   if (st != LMOE_OK) return st;
-  if (layer->exec) hipGraphExecDestroy(layer->exec);
+  if (layer->exec) (void)hipGraphExecDestroy(layer->exec);
   layer->exec = exec;
   return LMOE_OK;
 }
@@ -263,11 +263,12 @@ lmoe_status lmoe_layer_replay(lmoe_layer* layer, hipStream_t stream) {
 
 void lmoe_layer_destroy(lmoe_layer* layer) {
   if (!layer) return;
-  if (layer->exec) hipGraphExecDestroy(layer->exec);
-  if (layer->ev_start) hipEventDestroy(layer->ev_start);
-  if (layer->ev_fork) hipEventDestroy(layer->ev_fork);
-  if (layer->ev_shared) hipEventDestroy(layer->ev_shared);
-  if (layer->own_side && layer->side) hipStreamDestroy(layer->side);
+  // releases only: a failure here leaves nothing the caller could act on
+  if (layer->exec) (void)hipGraphExecDestroy(layer->exec);
+  if (layer->ev_start) (void)hipEventDestroy(layer->ev_start);
+  if (layer->ev_fork) (void)hipEventDestroy(layer->ev_fork);
+  if (layer->ev_shared) (void)hipEventDestroy(layer->ev_shared);
+  if (layer->own_side && layer->side) (void)hipStreamDestroy(layer->side);
   delete layer;
 }
 
