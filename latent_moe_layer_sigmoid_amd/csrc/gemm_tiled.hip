@@ -553,6 +553,19 @@ int tiled_splitk(const StreamGemm& g0) {
   return k < 2 ? 1 : k;
 }
 
+// Dense launches of whole rounds: with one workgroup per CU, M x n_out outputs in tiles
+// that make a whole number of rounds of the 256 CUs plus part of one leave CUs idle in
+// that last round. Returns the output columns (a multiple of TILE_N) whose tiles make
+// whole rounds, when the tiles of the remaining columns are at most half a round, so that
+// a second launch runs them with split K over every CU; n_out when no such split exists.
+int tiled_round_cols(int M, int n_out) {
+  const long mt = (M + TILE_M - 1) / TILE_M, nb = (n_out + TILE_N - 1) / TILE_N, G = mt * nb;
+  if (G <= 256 || G % 256 == 0) return n_out;
+  for (long nb1 = nb - 1; nb1 > 0; --nb1)
+    if ((mt * nb1) % 256 == 0) return mt * (nb - nb1) <= 128 ? (int)(nb1 * TILE_N) : n_out;
+  return n_out;
+}
+
 size_t tiled_splitk_bytes(const StreamGemm& g, int ksplit) {
   if (ksplit <= 1) return 0;
   size_t cols = 0;

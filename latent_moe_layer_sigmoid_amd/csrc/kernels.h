@@ -18,6 +18,9 @@ bool tiled_dual_ok(const StreamGemm& g);
 // bytes it then needs.
 int tiled_splitk(const StreamGemm& g);
 size_t tiled_splitk_bytes(const StreamGemm& g, int ksplit);
+// Output columns of a dense M-row launch that fill whole rounds of the CUs, when the rest
+// is small enough to run with split K (n_out: no split).
+int tiled_round_cols(int M, int n_out);
 // MXFP8 x packed MXFP4 (grouped mode, one segment: SITU_MX or PAIR / TOKEN); Kd % 512 == 0.
 hipError_t launch_stream_gemm_mx(StreamGemm g, int live_tiles, hipStream_t stream);
 

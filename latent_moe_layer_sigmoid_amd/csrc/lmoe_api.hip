@@ -564,6 +564,19 @@ static StreamGemm tail_shared_gemm(int T, int L, int H, int I, const void* w_up,
   return g;
 }
 
+// Output columns [c0, c0 + nc) of the tail GEMM: the weight rows of both phases (packed
+// in 16-row groups, so a row offset is a byte offset) and the output columns, row pitch H.
+static StreamGemm tail_columns(StreamGemm g, int c0, int nc, int L, int I, int H, lmoe_dtype io_dtype) {
+  const size_t es = (size_t)esize_of(io_dtype);
+  if (g.seg[0].w) g.seg[0].w = static_cast<const char*>(g.seg[0].w) + (size_t)c0 * I * es;
+  if (g.w1) g.w1 = static_cast<const char*>(g.w1) + (size_t)c0 * L * es;
+  if (g.seg[0].out) g.seg[0].out = static_cast<char*>(g.seg[0].out) + (size_t)c0 * es;
+  g.seg[0].n_total = nc;
+  g.seg[0].n_out = nc;
+  g.seg[0].ldo = H;
+  return g;
+}
+
 static lmoe_status tail_shared_impl(int T, int L, int H, int I, const float* latent, const void* gamma, float eps,
                                     const void* w_up, const void* shared_act, const void* w_s2,
                                     lmoe_dtype io_dtype, void* out, void* norm_out, void* workspace,
@@ -585,10 +598,26 @@ static lmoe_status tail_shared_impl(int T, int L, int H, int I, const float* lat
     // token-heavy: one tiled GEMM with two K phases, out = round(shared_act w_s2^T +
     // norm_out w_up^T): the shared-expert FC2 and the up projection accumulate into the
     // same fp32 tiles (the shared output is not rounded on its own here); with a
-    // workspace, split-K when the tiles alone would leave CUs idle
+    // workspace, split-K when the tiles alone would leave CUs idle: for the whole GEMM
+    // when it has less than a round of tiles, else for the columns past the last whole
+    // round of tiles, in a second launch (T = 8192, H = 7168: 768 tiles at full K, then
+    // 128 tiles in two K slices, rather than 896 tiles of which the last 128 run alone)
     StreamGemm g = tail_shared_gemm(T, L, H, I, w_up, shared_act, w_s2, io_dtype, out, norm_out);
     if (!tiled_dual_ok(g)) return LMOE_ERR_UNSUPPORTED;
     if (workspace) {
+      const int c1 = tiled_round_cols(T, H);
+      if (c1 < H) {
+        StreamGemm g2 = tail_columns(g, c1, H - c1, L, I, H, io_dtype);
+        const int k = tiled_splitk(g2);
+        if (k > 1) {
+          if (workspace_bytes < tiled_splitk_bytes(g2, k)) return LMOE_ERR_WORKSPACE;
+          g2.part = static_cast<float*>(workspace);
+          g2.ksplit = k;
+        }
+        const hipError_t e1 = launch_tiled_gemm(tail_columns(g, 0, c1, L, I, H, io_dtype), stream);
+        if (e1 != hipSuccess) return hip_status(e1);
+        return hip_status(launch_tiled_gemm(g2, stream));
+      }
       const int k = tiled_splitk(g);
       if (k > 1) {
         if (workspace_bytes < tiled_splitk_bytes(g, k)) return LMOE_ERR_WORKSPACE;
@@ -627,6 +656,11 @@ size_t lmoe_tail_shared_workspace_bytes(int T, int L, int H, int I, lmoe_dtype i
   if (T <= 0 || L <= 0 || H <= 0 || I <= 0 || !dense_elt(io_dtype) || !use_tiled_dense(T, io_dtype)) return 0;
   if (L % kchunk_of(io_dtype) != 0 || I % kchunk_of(io_dtype) != 0 || H % 16 != 0) return 0;
   const StreamGemm g = tail_shared_gemm(T, L, H, I, nullptr, nullptr, nullptr, io_dtype, nullptr, nullptr);
+  const int c1 = tiled_round_cols(T, H);
+  if (c1 < H) {
+    const StreamGemm g2 = tail_columns(g, c1, H - c1, L, I, H, io_dtype);
+    return tiled_splitk_bytes(g2, tiled_splitk(g2));
+  }
   return tiled_splitk_bytes(g, tiled_splitk(g));
 }
 

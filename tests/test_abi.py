@@ -70,6 +70,14 @@ def test_invalid_calls_are_rejected_without_a_gpu(B):
     assert L.lmoe_permute(8, 64, 4, 16, P, P, P, P, P, P, P, cap - 16, None, 0, None) == B.LMOE_ERR_WORKSPACE
     assert B.lmoe_permute_workspace_bytes(8, 64, 4) == 0
     assert B.lmoe_permute_workspace_bytes(8192, 896, 16) == 128 * 896 * 4
+    # fused tail workspace (fp32 split-K slices, 128 x 512 tiles, 256 CUs): 8 x 14 tiles, two
+    # slices of every column; 32 x 14 = 1.75 rounds, no split; 64 x 14 = 3.5 rounds, the last
+    # 1024 columns (128 tiles) in two slices; 16 x 17 tiles, the last 512 columns in four
+    assert B.lmoe_tail_shared_workspace_bytes(1024, 2048, 7168, 4096, B.LMOE_BF16) == 2 * 1024 * 7168 * 4
+    assert B.lmoe_tail_shared_workspace_bytes(4096, 2048, 7168, 4096, B.LMOE_BF16) == 0
+    assert B.lmoe_tail_shared_workspace_bytes(8192, 2048, 7168, 4096, B.LMOE_BF16) == 2 * 8192 * 1024 * 4
+    assert B.lmoe_tail_shared_workspace_bytes(2048, 512, 8704, 1536, B.LMOE_BF16) == 4 * 2048 * 512 * 4
+    assert B.lmoe_tail_shared_workspace_bytes(8, 2048, 7168, 4096, B.LMOE_BF16) == 0   # few tokens: no tiled path
     big_cap = B.lmoe_permute_rows_cap(8192, 896, 16, 128)
     assert L.lmoe_permute(8192, 896, 16, 128, P, P, P, P, P, P, P, big_cap, None, 0, None) == B.LMOE_ERR_WORKSPACE
     # fc1: beta required and positive; mismatched dtypes; unsupported K dim

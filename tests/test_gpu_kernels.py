@@ -864,12 +864,17 @@ def test_tail_shared_matches_oracle(B, T, L, H, I, dt):
     assert norm_err(f64(out), rout) <= 1e-2
 
 
-@pytest.mark.parametrize("T,L,H,I", [(1024, 2048, 7168, 4096), (300, 512, 400, 1280), (300, 512, 400, 1536)])
-def test_tail_shared_split_k_matches_oracle(B, T, L, H, I):
+@pytest.mark.parametrize("T,L,H,I,c1", [(1024, 2048, 7168, 4096, 0), (300, 512, 400, 1280, 0),
+                                         (300, 512, 400, 1536, 0), (8192, 2048, 7168, 4096, 6144),
+                                         (2048, 512, 8704, 1536, 8192)])
+def test_tail_shared_split_k_matches_oracle(B, T, L, H, I, c1):
     # the token-heavy fused tail with too few output tiles for the CUs: split-K slices over
     # both K phases, against the oracle and against the unsplit call. Slices of 32-wide
     # steps: 192 in 2 (the phase boundary at step 128 inside the second slice), 56 in 3
-    # (boundary 40 inside the third), 64 in 4 (boundary 48 at the start of the fourth)
+    # (boundary 40 inside the third), 64 in 4 (boundary 48 at the start of the fourth).
+    # c1 > 0: tiles past whole rounds of the CUs (64 x 14 = 3.5 rounds; 16 x 17 = 272 tiles)
+    # -- columns [0, c1) in one full-K launch, bit-identical to the unsplit call, the rest
+    # split into 2 (of 192 steps) or 4 (of 64 steps) slices in a second launch
     rng = np.random.default_rng(T + 7 * L + I)
     td = torch.bfloat16
     z = torch.from_numpy(rng.standard_normal((T, L)) * 0.3).float()
@@ -891,12 +896,15 @@ def test_tail_shared_split_k_matches_oracle(B, T, L, H, I):
             B.lmoe_tail_shared_ws(*args, out1, n1, ws, wsb - 4)
         assert ei.value.status == B.LMOE_ERR_WORKSPACE
     torch.cuda.synchronize()
-    sel = np.arange(T) if T <= 300 else np.array([0, 1, 511, 1022, 1023])
+    sel = np.arange(T) if T <= 300 else np.array([0, 1, T // 2 - 1, T - 2, T - 1])
     sh = oracle.round_to(oracle.linear(f64(a_s)[sel], f64(Ws2)), "bf16")
     rn, rout = oracle.tail(f64(z)[sel], f64(gamma), 1e-6, f64(Wup), sh, "bf16")
     assert norm_err(f64(n)[sel], rn) <= 1e-2
     assert norm_err(f64(out)[sel], rout) <= 1e-2
     assert norm_err(f64(out), f64(out1)) <= 1e-2
+    if c1:
+        assert torch.equal(out[:, :c1], out1[:, :c1])
+        assert norm_err(f64(out)[:, c1:], f64(out1)[:, c1:]) <= 1e-2
 
 
 # ------------------------------------------------------------------------------- tail
