@@ -249,7 +249,12 @@ def copy_bandwidth(torch, nbytes=FLUSH_BYTES):
 
 def gpu_clock():
     """The GPU's shader (gfx) clock in MHz as amd-smi reports it right after the timed
-    region (current, min and max of the first gfx clock domain), or the tool's error."""
+    region (current, min and max of the first gfx clock domain), or the tool's error. Not
+    under rocprofv3: the tool is a Python script started through `env`, and a child that
+    inherits the profiler's preloaded library would replace itself after that library has
+    opened the GPU."""
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
+        return {"skipped": "running under rocprofv3"}
     try:
         r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True, text=True,
                            timeout=20)
