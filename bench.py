@@ -341,14 +341,38 @@ def launch_modes(torch, layer, X, steps=200):
     return res
 
 
+_SPIN = {}
+
+
+def spin_cycles_per_us(torch):
+    """Clock cycles of torch.cuda._sleep (a one-wave kernel that spins on the clock and
+    touches no memory) per microsecond, measured once with events."""
+    if "c" not in _SPIN:
+        n = 1 << 20
+        torch.cuda._sleep(n)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.cuda._sleep(n)
+        b.record()
+        torch.cuda.synchronize()
+        _SPIN["c"] = n / max(a.elapsed_time(b) * 1e3, 1.0)
+    return _SPIN["c"]
+
+
 def kernel_durations(torch, layer, Xs, steps, flush=None):
     """Mean durations (ms) of each library call of the step (StepTimer events on the launch
-    stream) over `steps` steps; with `flush`, a cache-clearing write precedes each step."""
+    stream) over `steps` steps; with `flush`, a cache-clearing write precedes each step,
+    without it a 500 µs spin that touches no memory. Either keeps the GPU behind the host,
+    whose event bookkeeping takes longer than a decode step: otherwise the GPU would wait
+    for the host inside the first timed call of every step."""
     from latent_moe_layer_sigmoid_amd import StepTimer
     timer = StepTimer(torch.cuda.current_stream())
+    spin = int(spin_cycles_per_us(torch) * 500) if flush is None else 0
     for i in range(steps):
         if flush is not None:
             flush.fill_(i & 0xFF)
+        else:
+            torch.cuda._sleep(spin)
         layer.forward(Xs[i % len(Xs)], timer=timer)
     torch.cuda.synchronize()
     return timer.durations()
