@@ -77,6 +77,7 @@ def test_invalid_calls_are_rejected_without_a_gpu(B):
     assert B.lmoe_tail_shared_workspace_bytes(4096, 2048, 7168, 4096, B.LMOE_BF16) == 0
     assert B.lmoe_tail_shared_workspace_bytes(8192, 2048, 7168, 4096, B.LMOE_BF16) == 2 * 8192 * 1024 * 4
     assert B.lmoe_tail_shared_workspace_bytes(2048, 512, 8704, 1536, B.LMOE_BF16) == 4 * 2048 * 512 * 4
+    assert B.lmoe_tail_shared_workspace_bytes(8192, 512, 7040, 512, B.LMOE_BF16) == 2 * 8192 * 896 * 4
     assert B.lmoe_tail_shared_workspace_bytes(8, 2048, 7168, 4096, B.LMOE_BF16) == 0   # few tokens: no tiled path
     big_cap = B.lmoe_permute_rows_cap(8192, 896, 16, 128)
     assert L.lmoe_permute(8192, 896, 16, 128, P, P, P, P, P, P, P, big_cap, None, 0, None) == B.LMOE_ERR_WORKSPACE

@@ -866,7 +866,7 @@ def test_tail_shared_matches_oracle(B, T, L, H, I, dt):
 
 @pytest.mark.parametrize("T,L,H,I,c1", [(1024, 2048, 7168, 4096, 0), (300, 512, 400, 1280, 0),
                                          (300, 512, 400, 1536, 0), (8192, 2048, 7168, 4096, 6144),
-                                         (2048, 512, 8704, 1536, 8192)])
+                                         (2048, 512, 8704, 1536, 8192), (8192, 512, 7040, 512, 6144)])
 def test_tail_shared_split_k_matches_oracle(B, T, L, H, I, c1):
     # the token-heavy fused tail with too few output tiles for the CUs: split-K slices over
     # both K phases, against the oracle and against the unsplit call. Slices of 32-wide
@@ -874,7 +874,8 @@ def test_tail_shared_split_k_matches_oracle(B, T, L, H, I, c1):
     # (boundary 40 inside the third), 64 in 4 (boundary 48 at the start of the fourth).
     # c1 > 0: tiles past whole rounds of the CUs (64 x 14 = 3.5 rounds; 16 x 17 = 272 tiles)
     # -- columns [0, c1) in one full-K launch, bit-identical to the unsplit call, the rest
-    # split into 2 (of 192 steps) or 4 (of 64 steps) slices in a second launch
+    # split into 2 (of 192 or 32 steps) or 4 (of 64 steps) slices in a second launch; H =
+    # 7040 leaves a last block of 384 columns in the split launch
     rng = np.random.default_rng(T + 7 * L + I)
     td = torch.bfloat16
     z = torch.from_numpy(rng.standard_normal((T, L)) * 0.3).float()
