@@ -359,19 +359,20 @@ def spin_cycles_per_us(torch):
     return _SPIN["c"]
 
 
-def kernel_durations(torch, layer, Xs, steps, flush=None):
+def kernel_durations(torch, layer, Xs, steps, flush=None, spin_us=0):
     """Mean durations (ms) of each library call of the step (StepTimer events on the launch
     stream) over `steps` steps; with `flush`, a cache-clearing write precedes each step,
-    without it a 500 µs spin that touches no memory. Either keeps the GPU behind the host,
-    whose event bookkeeping takes longer than a decode step: otherwise the GPU would wait
-    for the host inside the first timed call of every step."""
+    with `spin_us` (and no flush) a spin of that many microseconds that touches no memory.
+    Either keeps the GPU behind the host when the host's event bookkeeping takes longer
+    than a step (decode): otherwise the GPU would wait for the host inside the first timed
+    call of every step."""
     from latent_moe_layer_sigmoid_amd import StepTimer
     timer = StepTimer(torch.cuda.current_stream())
-    spin = int(spin_cycles_per_us(torch) * 500) if flush is None else 0
+    spin = int(spin_cycles_per_us(torch) * spin_us) if flush is None and spin_us > 0 else 0
     for i in range(steps):
         if flush is not None:
             flush.fill_(i & 0xFF)
-        else:
+        elif spin:
             torch.cuda._sleep(spin)
         layer.forward(Xs[i % len(Xs)], timer=timer)
     torch.cuda.synchronize()
@@ -386,7 +387,8 @@ def layer_record(torch, cfg, layer, Xs, steps, flush, seed):
     torch.cuda.synchronize()
     st = time_layer(torch, layer, Xs, steps, flush)
     pc = percentiles(st)
-    dur = kernel_durations(torch, layer, Xs, steps, flush)
+    # steps under 1 ms (decode) are shorter than the host's bookkeeping of the timed pass
+    dur = kernel_durations(torch, layer, Xs, steps, flush, spin_us=500 if pc["median"] < 1.0 else 0)
     b = layer.buffers(cfg.T)
     counts = b["counts"].cpu()
     n_touched = int((counts > 0).sum())
