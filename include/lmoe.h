@@ -348,7 +348,10 @@ lmoe_status lmoe_tail_shared(int T, int L, int H, int I, const float* latent, co
  * and too few 128 x 512 output tiles to fill the CUs (for example T = 1024, H = 7168), the
  * K range of both phases together is cut into slices computed by separate workgroups into
  * `workspace`, and a second kernel adds the slices in fixed order and rounds (results are
- * reproducible; they may differ in the last bits from the unsplit call).
+ * reproducible; they may differ in the last bits from the unsplit call). When the tiles
+ * make whole rounds of the 256 CUs plus at most half a round (for example T = 8192, H =
+ * 7168: 896 tiles), the columns of the whole rounds are computed at full K, bit-identical
+ * to the unsplit call, and only the remaining columns are split into slices.
  * lmoe_tail_shared_workspace_bytes returns the bytes needed for the same shapes (0: no
  * split, workspace unused). workspace NULL: no split; non-NULL but smaller than needed:
  * LMOE_ERR_WORKSPACE. Everything else as lmoe_tail_shared. */
